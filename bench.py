@@ -1,0 +1,228 @@
+"""Benchmark: one decode step of the paged-KV attention hot path on one GPU.
+
+A step is the KV write of every sequence's new token followed by batched GQA
+decode attention over the paged pool, on the Qwen3-0.6B-shaped workload
+(16 q / 8 kv heads, head_dim 128, bf16, block size 16, 256 sequences with
+context = U[100,1024] + U[0,1024] capped at 2048, pool 1.2x the blocks in use,
+permuted block ids).  Inputs are synthetic and resident in HBM before timing.
+
+Two copies of the pools alternate between steps, so no step finds the previous
+step's K/V in the 256 MB last-level cache: every step streams its context from
+HBM, as a real decode step over a large batch does.
+
+Prints ONE JSON line (see the fields below).  --gpus N > 1 exits: this path runs
+on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "pa_decode HBM GB/s (% of peak) + seq-steps/s, Qwen3-0.6B shape, batch 256"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_qwen3_06b_b256_traffic.json")
+KERNEL_SOURCES = ["attn_rows.hip", "pa_device.hpp", "pa_internal.hpp", "pa_api.cpp"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_attention_22_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(partition: int):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, when
+    they were taken on the kernel sources and partition in use now."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("partition_tokens") != partition:
+        return None
+    return t.get("hbm_bytes_per_decode")
+
+
+def decode_bytes(b) -> int:
+    """Algorithmic bytes of one decode call: each context token's K and V row
+    once, q and out, the block-table entries in use and the lengths."""
+    es = b.elem_bytes
+    kv = int(b.context_lens.sum()) * 2 * b.num_kv_heads * b.head_dim * es
+    qo = 2 * b.num_seqs * b.num_q_heads * b.head_dim * es
+    tables = 4 * int(sum(-(-int(L) // 16) for L in b.context_lens))
+    return kv + qo + tables + 4 * b.num_seqs
+
+
+def kv_write_bytes(b) -> int:
+    T = int((b.slot_mapping >= 0).sum())
+    return 2 * 2 * T * b.num_kv_heads * b.head_dim * b.elem_bytes + 4 * b.slot_mapping.size
+
+
+def cpu_baseline(b, min_seconds: float = 10.0) -> dict:
+    """The fp64 oracle on the same step (KV write + decode), one thread,
+    repeated over the whole batch until at least min_seconds have passed."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    passes, t0 = 0, time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            kp, vp = oracle.kv_write(b.k_pool, b.v_pool, b.new_k, b.new_v, b.slot_mapping)
+            oracle.decode(b.q, kp, vp, b.block_tables, b.context_lens, b.scale, b.dtype)
+            passes += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+    dt = (time.perf_counter() - t0) / passes
+    gbs = (decode_bytes(b) + kv_write_bytes(b)) / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seq_steps_per_s": round(b.num_seqs / dt, 2),
+            "sample": f"whole batch ({b.num_seqs} seqs), KV write + decode, {passes} pass(es), "
+                      f"{dt:.2f} s per pass, numpy fp64, BLAS limited to 1 thread"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--partition", type=int, default=0,
+                    help="partition_tokens for pa_decode (0 = library choice, -1 = one pass)")
+    ap.add_argument("--workload", default="qwen3_06b_decode",
+                    help="generator preset (default: the Qwen3-0.6B batch-256 decode step)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(no multi-GPU path is built)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_attention_22_amd as pa
+    from workloads import PRESETS
+
+    if not os.path.exists(pa.LIB_PATH):
+        from paged_kv_attention_22_amd import build as pa_build
+        pa_build.build()
+
+    log(f"[bench] generating {args.workload}")
+    b = PRESETS[args.workload]()
+    if b.num_prefill_seqs:
+        print("bench.py measures decode steps; pick a decode workload", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"[bench] device {props.name}, {props.multi_processor_count} CUs, "
+        f"{props.total_memory / 2**30:.0f} GiB")
+
+    def up(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    pools = [(up(b.k_pool), up(b.v_pool)) for _ in range(2)]
+    q, new_k, new_v = up(b.q), up(b.new_k), up(b.new_v)
+    slots, tables, lens = up(b.slot_mapping), up(b.block_tables), up(b.context_lens)
+    out = torch.empty_like(q)
+    part = pa.decode_partition_tokens(b.num_seqs, b.num_kv_heads, b.max_context_len, args.partition)
+    ws_bytes = pa.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                         b.max_context_len, args.partition)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        kp, vp = pools[i & 1]
+        pa.kv_write(new_k, new_v, slots, kp, vp)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.decode(q, kp, vp, tables, lens, b.max_context_len, scale=b.scale, out=out,
+                  partition_tokens=args.partition, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    log(f"[bench] warmup {args.warmup} steps (partition_tokens={part})")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = [e0.elapsed_time(e1) for e0, e1 in events]
+    log(f"[bench] done: {wall * 1e3 / args.steps:.3f} ms/step, decode median "
+        f"{float(np.median(dec_ms)) * 1e3:.1f} us")
+
+    ms_per_step = wall * 1e3 / args.steps
+    dbytes, wbytes = decode_bytes(b), kv_write_bytes(b)
+    value = (dbytes + wbytes) / (ms_per_step * 1e-3) / 1e9
+    dec_mean_s = float(np.mean(dec_ms)) * 1e-3
+    achieved = dbytes / dec_mean_s / 1e9
+    traffic = measured_traffic(part)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": b.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": b.name, "recipe": b.recipe, "seed": b.seed, "num_seqs": b.num_seqs,
+            "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads,
+            "head_dim": b.head_dim, "block_size": 16, "num_blocks": b.num_blocks,
+            "mean_context": round(float(b.context_lens.mean()), 2),
+            "max_context": b.max_context_len, "partition_tokens": part,
+            "step": "pa_kv_write (one new token per sequence) + pa_decode",
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seq_steps_per_s": round(b.num_seqs / (ms_per_step * 1e-3), 1),
+        "decode_us": {"mean": round(dec_mean_s * 1e6, 2),
+                      "median": round(float(np.median(dec_ms)) * 1e3, 2),
+                      "p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+                      "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2)},
+        "roofline": {
+            "kernel": "pa_decode (split partials + merge)" if part > 0 else "pa_decode (one pass)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": dbytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(b)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,183 @@
+/*
+ * pa.h -- C ABI of the paged-KV attention library for MI355X (gfx950).
+ *
+ * The library has three operations, taken from how the pages frame the
+ * problem:
+ *
+ *   pa_kv_write       append each step's new K/V rows into a shared block pool
+ *                     at flat slots ("mini_engine", Next: fused kernels -- the
+ *                     fused KV-cache write; "mini-vllm", Milestones item 7 --
+ *                     GPU-side slot derivation).
+ *   pa_decode         batched grouped-query decode attention over a ragged set
+ *                     of sequences, reading K/V in place through per-sequence
+ *                     block tables ("09 -- Mini Inference Engine (The
+ *                     Capstone)", Week 4 -- Paged KV cache; "mini-vllm",
+ *                     Milestones item 6; "mini_engine", What it does -- GQA).
+ *   pa_prefill_chunk  causal attention for a mixed batch of prefill chunks and
+ *                     decode rows under a token budget ("mini_engine", What it
+ *                     does -- chunked prefill; Capstone page, Week 3 option B
+ *                     and the design-decision table's chunked-prefill entry).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every tensor pointer is DEVICE memory owned by the caller.  The library
+ *   allocates nothing, keeps no handle between calls, and is reentrant.  Scratch
+ *   memory is passed in as `workspace`, sized by the matching *_workspace_bytes.
+ * - Every call validates its host arguments first.  On failure it returns a
+ *   non-zero pa_status, enqueues nothing and leaves every output untouched.
+ * - On success the work is enqueued on `stream` (a hipStream_t; NULL means the
+ *   default stream) and the call returns without synchronising.  The library
+ *   never reads device memory from the host, so all sizes the launch needs come
+ *   in as host integers.
+ * - Layouts are row-major and contiguous unless a stride says otherwise:
+ *     pools          [num_blocks, 16, num_kv_heads, head_dim]
+ *     q, out         [rows, num_q_heads, head_dim]
+ *     block_tables   int32 [num_seqs, max_blocks_per_seq]; entry i is the
+ *                    physical block holding logical tokens 16i .. 16i+15
+ *     context_lens   int32 [num_seqs]; tokens attended, including the ones
+ *                    written in this step (write first, then attend)
+ * - Query head h attends with kv head h / (num_q_heads / num_kv_heads).
+ * - q, out and the pools share one element type: bf16 (accumulation in fp32,
+ *   output rounded to nearest even) or fp32.
+ * - Device-side data is trusted for results but not for memory safety: slots
+ *   outside [0, num_blocks*16) are skipped, block ids are clamped into
+ *   [0, num_blocks), context lengths are clamped into [0, max_context_len] and
+ *   to max_blocks_per_seq*16.  Such inputs give unspecified values, never an
+ *   out-of-bounds access.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_NULL = 1,        /* a required pointer is NULL */
+    PA_ERR_SHAPE = 2,       /* a size or count is out of range or inconsistent */
+    PA_ERR_DTYPE = 3,       /* unknown element type */
+    PA_ERR_UNSUPPORTED = 4, /* valid but not built: block size, head_dim, group */
+    PA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+    PA_ERR_LAUNCH = 6,      /* the HIP runtime rejected a launch */
+    PA_ERR_ALIGN = 7        /* a pointer or stride breaks 16-byte alignment */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Shape of one layer's K pool (the V pool has the same shape).
+ * block_size must be 16; head_dim 64 or 128; dtype a pa_dtype. */
+typedef struct {
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t dtype;
+} pa_pool_desc;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* pa_status_str(int32_t status);
+
+/*
+ * pa_kv_write -- scatter new tokens' K and V rows into the pools.
+ *
+ * k, v            [num_tokens, num_kv_heads, head_dim] rows; consecutive
+ *                 tokens are k_token_stride / v_token_stride ELEMENTS apart
+ *                 (so views into a packed QKV projection work); within a token
+ *                 the [num_kv_heads, head_dim] row is contiguous.
+ * slot_mapping    int32 [num_tokens]; token t goes to block slot/16, offset
+ *                 slot%16, i.e. row `slot` of the pool seen as
+ *                 [num_blocks*16, num_kv_heads*head_dim].  slot < 0 marks a
+ *                 padding token: nothing is written for it.  Slots must be
+ *                 distinct within one call (otherwise which row wins is
+ *                 unspecified).
+ * k_pool, v_pool  written in place; nothing else in them changes.
+ * The copy is bit-exact.  Pointers and strides must be 16-byte aligned.
+ * num_tokens == 0 returns PA_OK without enqueuing anything.
+ */
+int32_t pa_kv_write(const void* k, const void* v,
+                    int64_t k_token_stride, int64_t v_token_stride,
+                    const int32_t* slot_mapping, int32_t num_tokens,
+                    void* k_pool, void* v_pool, pa_pool_desc pool,
+                    void* stream);
+
+/*
+ * Split-context choice shared by pa_decode and pa_prefill_chunk:
+ *   partition_tokens < 0   one pass per (sequence, kv head); no workspace;
+ *   partition_tokens == 0  the library picks (see pa_decode_partition_tokens);
+ *   partition_tokens > 0   a multiple of 16: each (sequence, kv head) is split
+ *                          into chunks of that many context tokens whose
+ *                          partial softmax states are merged by a second
+ *                          kernel (log-sum-exp), which needs the workspace.
+ *
+ * pa_decode_partition_tokens returns the partition size the library uses for
+ * these arguments (-1 = one pass).  pa_decode_workspace_bytes returns the
+ * workspace pa_decode needs for the same arguments (0 when one pass).
+ */
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                   int32_t max_context_len, int32_t partition_tokens);
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_tokens);
+
+/*
+ * pa_decode -- one query row per sequence.
+ *
+ * q, out          [num_seqs, num_q_heads, head_dim]
+ * k_pool, v_pool  [num_blocks, 16, num_kv_heads, head_dim] (read only)
+ * block_tables    int32 [num_seqs, max_blocks_per_seq]; entries past
+ *                 ceil(context_len/16) are never read
+ * context_lens    int32 [num_seqs]; 0 gives an all-zero output row
+ * max_context_len host-side upper bound of context_lens
+ * scale           multiplies q.k before the softmax (normally 1/sqrt(head_dim))
+ * Supported: num_q_heads % num_kv_heads == 0 with a group size of 1..8.
+ * num_seqs == 0 returns PA_OK without enqueuing anything.
+ */
+int32_t pa_decode(const void* q, const void* k_pool, const void* v_pool,
+                  pa_pool_desc pool,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, int32_t num_seqs,
+                  int32_t max_context_len, int32_t num_q_heads, float scale,
+                  void* out, int32_t partition_tokens,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_prefill_chunk -- causal attention for a packed mixed batch.
+ *
+ * q, out            [total_query_tokens, num_q_heads, head_dim]; the rows of
+ *                   sequence s are query_start_loc[s] .. query_start_loc[s+1]-1
+ * query_start_loc   int32 [num_seqs + 1], non-decreasing, [0] == 0,
+ *                   [num_seqs] == total_query_tokens
+ * num_prefill_seqs  sequences 0 .. num_prefill_seqs-1 may have any number of
+ *                   rows n <= context_len (prefill chunks); the others must
+ *                   have exactly one row (decode)
+ * max_query_len     host-side upper bound of the rows of any sequence
+ * Row i of a sequence with n rows and context length L sits at position
+ * L-n+i and attends to keys 0 .. L-n+i (causal, aligned to the context end).
+ * Chunks giving at least 16 (row, head) pairs per kv head run on the matrix
+ * cores; the rest, and the decode rows, run on the vector path.
+ * The workspace covers the vector path's split-context partials.
+ */
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_prefill_seqs,
+                                  int32_t total_query_tokens, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_tokens);
+
+int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc,
+                         int32_t total_query_tokens, int32_t num_seqs,
+                         int32_t num_prefill_seqs, int32_t max_query_len,
+                         const void* k_pool, const void* v_pool, pa_pool_desc pool,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t max_context_len,
+                         int32_t num_q_heads, float scale, void* out,
+                         int32_t partition_tokens,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,201 @@
+"""Paged-KV attention for MI355X (gfx950): Python binding of libpa.so.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in include/pa.h.  PyTorch supplies device memory and the current
+stream.  If libpa.so is missing the calls raise; there is no fallback.
+
+    import paged_kv_attention_22_amd as pa
+    pa.kv_write(k, v, slot_mapping, k_pool, v_pool)
+    out = pa.decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len)
+    out = pa.prefill_chunk(q, query_start_loc, num_prefill_seqs, max_query_len,
+                           k_pool, v_pool, block_tables, context_lens, max_context_len)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+BLOCK_SIZE = 16
+
+PA_OK, PA_F32, PA_BF16 = 0, 0, 1
+
+c_i32, c_i64, c_size, c_vp, c_f = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                  ctypes.c_void_p, ctypes.c_float)
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", c_i32), ("block_size", c_i32), ("num_kv_heads", c_i32),
+                ("head_dim", c_i32), ("dtype", c_i32)]
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+_SIGNATURES = {
+    "pa_status_str": (ctypes.c_char_p, [c_i32]),
+    "pa_kv_write": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_vp, PoolDesc, c_vp]),
+    "pa_decode_partition_tokens": (c_i32, [c_i32, c_i32, c_i32, c_i32]),
+    "pa_decode_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "pa_decode": (c_i32, [c_vp, c_vp, c_vp, PoolDesc, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
+                          c_f, c_vp, c_i32, c_vp, c_size, c_vp]),
+    "pa_prefill_workspace_bytes": (c_size, [c_i32] * 8),
+    "pa_prefill_chunk": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, PoolDesc,
+                                 c_vp, c_i32, c_vp, c_i32, c_i32, c_f, c_vp, c_i32, c_vp,
+                                 c_size, c_vp]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m paged_kv_attention_22_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().pa_status_str(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != PA_OK:
+        raise PAError(status, what)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype == torch.float32:
+        return PA_F32
+    raise TypeError(f"unsupported element type {t.dtype} (bf16 or fp32)")
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.data_ptr()
+
+
+def _contig(t: torch.Tensor, name: str) -> int:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return _dev(t, name)
+
+
+def _i32(t: torch.Tensor, name: str) -> int:
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return _contig(t, name)
+
+
+def pool_desc(k_pool: torch.Tensor) -> PoolDesc:
+    nb, bs, hkv, d = k_pool.shape
+    return PoolDesc(nb, bs, hkv, d, _dtype_code(k_pool))
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def kv_write(k, v, slot_mapping, k_pool, v_pool, stream=None) -> None:
+    """Scatter rows k[t], v[t] ([T, Hkv, D], token stride free) to pool row
+    slot_mapping[t]; negative slots are skipped."""
+    for name, t in (("k", k), ("v", v)):
+        if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError(f"{name} must be [T, Hkv, D] with contiguous token rows")
+    if k.dtype != k_pool.dtype or v.dtype != v_pool.dtype:
+        raise TypeError("k/v and pools must share an element type")
+    st = lib().pa_kv_write(_dev(k, "k"), _dev(v, "v"), k.stride(0), v.stride(0),
+                           _i32(slot_mapping, "slot_mapping"), slot_mapping.numel(),
+                           _contig(k_pool, "k_pool"), _contig(v_pool, "v_pool"),
+                           pool_desc(k_pool), _stream(stream))
+    _check(st, "pa_kv_write")
+
+
+def decode_partition_tokens(num_seqs, num_kv_heads, max_context_len, partition_tokens=0) -> int:
+    return lib().pa_decode_partition_tokens(num_seqs, num_kv_heads, max_context_len,
+                                            partition_tokens)
+
+
+def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                           partition_tokens=0) -> int:
+    return lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           max_context_len, partition_tokens)
+
+
+def prefill_workspace_bytes(num_seqs, num_prefill_seqs, total_query_tokens, num_q_heads,
+                            num_kv_heads, head_dim, max_context_len, partition_tokens=0) -> int:
+    return lib().pa_prefill_workspace_bytes(num_seqs, num_prefill_seqs, total_query_tokens,
+                                            num_q_heads, num_kv_heads, head_dim,
+                                            max_context_len, partition_tokens)
+
+
+def _workspace(nbytes: int, workspace, device) -> tuple[int, int]:
+    if nbytes == 0:
+        return 0, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
+def decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale=None,
+           out=None, partition_tokens=0, workspace=None, stream=None):
+    """Batched decode attention, q [S, Hq, D] -> out [S, Hq, D]."""
+    S, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    hkv = k_pool.shape[2]
+    need = decode_workspace_bytes(S, Hq, hkv, D, max_context_len, partition_tokens)
+    wp, wb = _workspace(need, workspace, q.device)
+    st = lib().pa_decode(_contig(q, "q"), _contig(k_pool, "k_pool"), _contig(v_pool, "v_pool"),
+                         pool_desc(k_pool), _i32(block_tables, "block_tables"),
+                         block_tables.shape[1], _i32(context_lens, "context_lens"), S,
+                         int(max_context_len), Hq, float(scale), _contig(out, "out"),
+                         int(partition_tokens), wp, wb, _stream(stream))
+    _check(st, "pa_decode")
+    return out
+
+
+def prefill_chunk(q, query_start_loc, num_prefill_seqs, max_query_len, k_pool, v_pool,
+                  block_tables, context_lens, max_context_len, scale=None, out=None,
+                  partition_tokens=0, workspace=None, stream=None):
+    """Causal attention for a packed mixed batch, q [T, Hq, D] -> out [T, Hq, D]."""
+    T, Hq, D = q.shape
+    S = context_lens.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    hkv = k_pool.shape[2]
+    need = prefill_workspace_bytes(S, num_prefill_seqs, T, Hq, hkv, D, max_context_len,
+                                   partition_tokens)
+    wp, wb = _workspace(need, workspace, q.device)
+    st = lib().pa_prefill_chunk(_contig(q, "q"), _i32(query_start_loc, "query_start_loc"), T, S,
+                                int(num_prefill_seqs), int(max_query_len),
+                                _contig(k_pool, "k_pool"), _contig(v_pool, "v_pool"),
+                                pool_desc(k_pool), _i32(block_tables, "block_tables"),
+                                block_tables.shape[1], _i32(context_lens, "context_lens"),
+                                int(max_context_len), Hq, float(scale), _contig(out, "out"),
+                                int(partition_tokens), wp, wb, _stream(stream))
+    _check(st, "pa_prefill_chunk")
+    return out

@@ -1,0 +1,297 @@
+// C ABI of the library: host-side validation, path choice and launch.
+// Nothing here touches the GPU before every argument has been checked, and
+// nothing reads device memory: sizes come in as host integers.
+#include <stdint.h>
+
+#include "pa_internal.hpp"
+
+using namespace pa;
+
+namespace {
+
+int elem_size(int32_t dtype) {
+    if (dtype == PA_BF16) return 2;
+    if (dtype == PA_F32) return 4;
+    return 0;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t check_pool(const pa_pool_desc& p) {
+    if (elem_size(p.dtype) == 0) return PA_ERR_DTYPE;
+    if (p.num_blocks <= 0 || p.num_kv_heads <= 0 || p.head_dim <= 0 || p.block_size <= 0)
+        return PA_ERR_SHAPE;
+    if (p.block_size != kBlock) return PA_ERR_UNSUPPORTED;
+    if (p.head_dim != 64 && p.head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (p.num_kv_heads > 65535) return PA_ERR_SHAPE;
+    if ((int64_t)p.num_blocks * kBlock > INT32_MAX) return PA_ERR_SHAPE;  // slots are int32
+    return PA_OK;
+}
+
+int32_t check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
+    if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0) return PA_ERR_SHAPE;
+    const int32_t group = num_q_heads / num_kv_heads;
+    if (group > kMaxGroup) return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+// Split-context choice.  Enough workgroups to cover 256 compute units several
+// times over, and partitions short enough that a ragged batch does not leave a
+// long tail of single long sequences.
+int32_t choose_partition(int64_t items, int32_t num_kv_heads, int32_t max_context_len,
+                         int32_t requested) {
+    if (requested < 0) return -1;
+    if (requested > 0) return requested;
+    const int64_t units = items * num_kv_heads;
+    if (max_context_len <= 256 || units >= 8192) return -1;
+    int32_t part = 256;
+    while (part > 64 && units * ceil_div(max_context_len, part) < 2048) part /= 2;
+    return part;
+}
+
+size_t split_bytes(int64_t items, int32_t num_q_heads, int32_t head_dim,
+                   int32_t max_context_len, int32_t part) {
+    if (part <= 0 || items <= 0) return 0;
+    const int64_t nparts = ceil_div(max_context_len, part);
+    return (size_t)(items * num_q_heads * nparts * (int64_t)(head_dim + 2) * 4);
+}
+
+int32_t check_partition(int32_t requested) {
+    if (requested > 0 && requested % kBlock != 0) return PA_ERR_SHAPE;
+    return PA_OK;
+}
+
+// Fills the common part of a RowsArgs and checks the split workspace.
+int32_t prepare_rows(RowsArgs& a, int64_t items, int32_t part, void* workspace,
+                     size_t workspace_bytes) {
+    a.num_items = (int32_t)items;
+    a.part_tokens = part;
+    a.nparts = part > 0 ? ceil_div(a.max_context_len, part) : 1;
+    a.ws = static_cast<float*>(workspace);
+    if (part > 0) {
+        if (a.nparts > 65535) return PA_ERR_SHAPE;
+        const size_t need = split_bytes(items, a.num_q_heads, a.head_dim, a.max_context_len, part);
+        if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+        if (need > 0 && !aligned16(workspace)) return PA_ERR_ALIGN;
+    }
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_str(int32_t status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_ERR_NULL: return "null pointer argument";
+        case PA_ERR_SHAPE: return "size or count out of range or inconsistent";
+        case PA_ERR_DTYPE: return "unknown element type";
+        case PA_ERR_UNSUPPORTED: return "unsupported block size, head_dim or group size";
+        case PA_ERR_WORKSPACE: return "workspace missing or too small";
+        case PA_ERR_LAUNCH: return "kernel launch failed";
+        case PA_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+        default: return "unknown status";
+    }
+}
+
+int32_t pa_kv_write(const void* k, const void* v, int64_t k_token_stride, int64_t v_token_stride,
+                    const int32_t* slot_mapping, int32_t num_tokens, void* k_pool, void* v_pool,
+                    pa_pool_desc pool, void* stream) {
+    if (int32_t st = check_pool(pool)) return st;
+    if (num_tokens < 0) return PA_ERR_SHAPE;
+    if (num_tokens == 0) return PA_OK;
+    if (!k || !v || !slot_mapping || !k_pool || !v_pool) return PA_ERR_NULL;
+    const int es = elem_size(pool.dtype);
+    const int64_t row_elems = (int64_t)pool.num_kv_heads * pool.head_dim;
+    if (k_token_stride < row_elems || v_token_stride < row_elems) return PA_ERR_SHAPE;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_pool) || !aligned16(v_pool) ||
+        (k_token_stride * es) % 16 || (v_token_stride * es) % 16)
+        return PA_ERR_ALIGN;
+    KvWriteArgs a;
+    a.k = k;
+    a.v = v;
+    a.k_stride = k_token_stride * es;
+    a.v_stride = v_token_stride * es;
+    a.slots = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.pool_rows = (int64_t)pool.num_blocks * kBlock;
+    a.row_bytes = (int32_t)(row_elems * es);
+    return launch_kv_write(a, static_cast<hipStream_t>(stream));
+}
+
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                                   int32_t partition_tokens) {
+    return choose_partition(num_seqs, num_kv_heads > 0 ? num_kv_heads : 1, max_context_len,
+                            partition_tokens);
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_tokens) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        max_context_len < 0 || check_partition(partition_tokens))
+        return 0;
+    const int32_t part = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_tokens);
+    return split_bytes(num_seqs, num_q_heads, head_dim, max_context_len, part);
+}
+
+int32_t pa_decode(const void* q, const void* k_pool, const void* v_pool, pa_pool_desc pool,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                  int32_t num_q_heads, float scale, void* out, int32_t partition_tokens,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (int32_t st = check_pool(pool)) return st;
+    if (int32_t st = check_heads(num_q_heads, pool.num_kv_heads)) return st;
+    if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
+        (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlock)
+        return PA_ERR_SHAPE;
+    if (int32_t st = check_partition(partition_tokens)) return st;
+    if (num_seqs == 0) return PA_OK;
+    if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PA_ERR_ALIGN;
+
+    RowsArgs a = {};
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_tables = block_tables;
+    a.max_blocks = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.query_start_loc = nullptr;
+    a.seq_begin = 0;
+    a.seq_end = num_seqs;
+    a.row_begin = 0;
+    a.mfma_min_pairs = 0;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = pool.num_kv_heads;
+    a.head_dim = pool.head_dim;
+    a.num_blocks = pool.num_blocks;
+    a.dtype = pool.dtype;
+    a.max_context_len = max_context_len;
+    a.scale = scale;
+    a.out = out;
+    const int32_t part = choose_partition(num_seqs, pool.num_kv_heads, max_context_len, partition_tokens);
+    if (int32_t st = prepare_rows(a, num_seqs, part, workspace, workspace_bytes)) return st;
+    return launch_rows(a, static_cast<hipStream_t>(stream));
+}
+
+size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_prefill_seqs,
+                                  int32_t total_query_tokens, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len,
+                                  int32_t partition_tokens) {
+    if (num_seqs <= 0 || num_prefill_seqs < 0 || num_prefill_seqs > num_seqs ||
+        num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+        check_partition(partition_tokens))
+        return 0;
+    const int64_t num_decode = num_seqs - num_prefill_seqs;
+    const int64_t prefill_rows = (int64_t)total_query_tokens - num_decode;
+    size_t need = 0;
+    if (prefill_rows > 0) {
+        const int32_t part = choose_partition(prefill_rows, num_kv_heads, max_context_len, partition_tokens);
+        need = split_bytes(prefill_rows, num_q_heads, head_dim, max_context_len, part);
+    }
+    if (num_decode > 0) {
+        const int32_t part = choose_partition(num_decode, num_kv_heads, max_context_len, partition_tokens);
+        const size_t d = split_bytes(num_decode, num_q_heads, head_dim, max_context_len, part);
+        if (d > need) need = d;
+    }
+    return need;
+}
+
+int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t total_query_tokens,
+                         int32_t num_seqs, int32_t num_prefill_seqs, int32_t max_query_len,
+                         const void* k_pool, const void* v_pool, pa_pool_desc pool,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t max_context_len, int32_t num_q_heads,
+                         float scale, void* out, int32_t partition_tokens, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    if (int32_t st = check_pool(pool)) return st;
+    if (int32_t st = check_heads(num_q_heads, pool.num_kv_heads)) return st;
+    if (num_seqs < 0 || num_prefill_seqs < 0 || num_prefill_seqs > num_seqs ||
+        total_query_tokens < 0 || max_query_len < 0 || max_blocks_per_seq <= 0 ||
+        max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlock ||
+        max_query_len > max_context_len)
+        return PA_ERR_SHAPE;
+    const int64_t num_decode = num_seqs - num_prefill_seqs;
+    const int64_t prefill_rows = (int64_t)total_query_tokens - num_decode;
+    if (prefill_rows < 0 || (num_prefill_seqs == 0 && prefill_rows != 0)) return PA_ERR_SHAPE;
+    if (int32_t st = check_partition(partition_tokens)) return st;
+    if (num_seqs == 0 || total_query_tokens == 0) return PA_OK;
+    if (!q || !query_start_loc || !k_pool || !v_pool || !block_tables || !context_lens || !out)
+        return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PA_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int32_t group = num_q_heads / pool.num_kv_heads;
+
+    RowsArgs base = {};
+    base.q = q;
+    base.k_pool = k_pool;
+    base.v_pool = v_pool;
+    base.block_tables = block_tables;
+    base.max_blocks = max_blocks_per_seq;
+    base.context_lens = context_lens;
+    base.num_q_heads = num_q_heads;
+    base.num_kv_heads = pool.num_kv_heads;
+    base.head_dim = pool.head_dim;
+    base.num_blocks = pool.num_blocks;
+    base.dtype = pool.dtype;
+    base.max_context_len = max_context_len;
+    base.scale = scale;
+    base.out = out;
+
+    // Check both vector-path launches before enqueuing anything.
+    RowsArgs pre = base, dec = base;
+    pre.query_start_loc = query_start_loc;
+    pre.seq_begin = 0;
+    pre.seq_end = num_prefill_seqs;
+    pre.row_begin = 0;
+    const bool mfma = prefill_rows > 0 && chunks_supported(pool.dtype, pool.head_dim, group);
+    pre.mfma_min_pairs = mfma ? 16 : 0;
+    const int32_t ppart = choose_partition(prefill_rows, pool.num_kv_heads, max_context_len, partition_tokens);
+    if (int32_t st = prepare_rows(pre, prefill_rows, ppart, workspace, workspace_bytes)) return st;
+    dec.query_start_loc = nullptr;
+    dec.seq_begin = num_prefill_seqs;
+    dec.seq_end = num_seqs;
+    dec.row_begin = (int32_t)prefill_rows;
+    dec.mfma_min_pairs = 0;
+    const int32_t dpart = choose_partition(num_decode, pool.num_kv_heads, max_context_len, partition_tokens);
+    if (int32_t st = prepare_rows(dec, num_decode, dpart, workspace, workspace_bytes)) return st;
+
+    if (mfma) {
+        ChunkArgs c = {};
+        c.q = q;
+        c.query_start_loc = query_start_loc;
+        c.num_seqs = num_prefill_seqs;
+        c.max_query_len = max_query_len;
+        c.k_pool = k_pool;
+        c.v_pool = v_pool;
+        c.block_tables = block_tables;
+        c.max_blocks = max_blocks_per_seq;
+        c.context_lens = context_lens;
+        c.max_context_len = max_context_len;
+        c.num_q_heads = num_q_heads;
+        c.num_kv_heads = pool.num_kv_heads;
+        c.head_dim = pool.head_dim;
+        c.num_blocks = pool.num_blocks;
+        c.dtype = pool.dtype;
+        c.total_rows = total_query_tokens;
+        c.scale = scale;
+        c.out = out;
+        c.min_pairs = 16;
+        if (int32_t st = launch_chunks(c, s)) return st;
+    }
+    if (prefill_rows > 0)
+        if (int32_t st = launch_rows(pre, s)) return st;
+    if (num_decode > 0)
+        if (int32_t st = launch_rows(dec, s)) return st;
+    return PA_OK;
+}
+
+}  // extern "C"

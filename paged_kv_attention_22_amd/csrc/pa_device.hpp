@@ -1,0 +1,59 @@
+// Device helpers for gfx950 (CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bf16 halves of a 32-bit word -> fp32 (exact).
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+// 2-wide bf16 dot product accumulated into fp32 (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of R consecutive lanes; every lane of the group gets
+// the total.  Steps: swap neighbours (quad_perm 1,0,3,2), swap pairs
+// (quad_perm 2,3,0,1), then mirror within 8 lanes and within 16 lanes, which
+// pair each lane with one in the other half of the group.
+template <int R>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(R == 4 || R == 8 || R == 16 || R == 32 || R == 64, "group size");
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    if constexpr (R >= 8) x += dpp<0x141>(x);
+    if constexpr (R >= 16) x += dpp<0x140>(x);
+    if constexpr (R >= 32) x += __shfl_xor(x, 16);
+    if constexpr (R >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte global load / store.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+}  // namespace pa

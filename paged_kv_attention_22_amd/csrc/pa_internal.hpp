@@ -1,0 +1,84 @@
+// Internal interface between the C ABI layer (pa_api.cpp) and the kernel
+// translation units.  Not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pa.h"
+
+namespace pa {
+
+constexpr int kBlock = 16;   // tokens per KV block (fixed; the pages' default)
+constexpr int kMaxGroup = 8; // largest GQA group built
+
+// One launch of the vector-path attention over a set of query rows ("items").
+struct RowsArgs {
+    const void* q;
+    const void* k_pool;
+    const void* v_pool;
+    const int32_t* block_tables;
+    int32_t max_blocks;
+    const int32_t* context_lens;
+    // NULL: item z is sequence seq_begin+z with one row (row_begin+z).
+    // Otherwise item z is row row_begin+z, its sequence is found in
+    // [seq_begin, seq_end) by binary search over query_start_loc.
+    const int32_t* query_start_loc;
+    int32_t seq_begin, seq_end;
+    int32_t row_begin;
+    int32_t num_items;
+    // With query_start_loc: items whose sequence gives at least this many
+    // (row, head) pairs per kv head are left to the matrix-core kernel
+    // (0 = handle every item here).
+    int32_t mfma_min_pairs;
+    int32_t num_q_heads, num_kv_heads, head_dim, num_blocks, dtype;
+    int32_t max_context_len;
+    float scale;
+    void* out;
+    int32_t part_tokens;  // <= 0: one pass, else a multiple of 16
+    int32_t nparts;       // partitions per item when split
+    float* ws;            // split partials: acc [items,Hq,nparts,D], m, l [items,Hq,nparts]
+};
+
+int32_t launch_rows(const RowsArgs& a, hipStream_t stream);
+
+struct KvWriteArgs {
+    const void* k;
+    const void* v;
+    int64_t k_stride, v_stride;  // BYTES between consecutive tokens
+    const int32_t* slots;
+    int32_t num_tokens;
+    void* k_pool;
+    void* v_pool;
+    int64_t pool_rows;           // num_blocks * 16
+    int32_t row_bytes;           // num_kv_heads * head_dim * element size
+};
+
+int32_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
+
+// Matrix-core causal chunk attention for prefill sequences 0..num_seqs-1 whose
+// rows give at least `min_pairs` (row, head) pairs per kv head.
+struct ChunkArgs {
+    const void* q;
+    const int32_t* query_start_loc;
+    int32_t num_seqs;
+    int32_t max_query_len;
+    const void* k_pool;
+    const void* v_pool;
+    const int32_t* block_tables;
+    int32_t max_blocks;
+    const int32_t* context_lens;
+    int32_t max_context_len;
+    int32_t num_q_heads, num_kv_heads, head_dim, num_blocks, dtype;
+    int32_t total_rows;
+    float scale;
+    void* out;
+    int32_t min_pairs;
+};
+
+// Returns PA_ERR_UNSUPPORTED when no matrix-core kernel exists for the shape
+// (the caller then sends every row down the vector path).
+int32_t launch_chunks(const ChunkArgs& a, hipStream_t stream);
+bool chunks_supported(int32_t dtype, int32_t head_dim, int32_t group);
+
+}  // namespace pa

@@ -1,0 +1,81 @@
+"""Shared test helpers: device upload of generated batches, comparisons."""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "paged_kv_attention_22_amd", "libpa.so")
+
+# Tolerances: fp32 inputs, max-abs 1e-5; bf16 inputs, max-abs 2e-2 and a
+# relative L2 error of at most 1e-2 (both must hold).
+F32_ATOL = 1e-5
+BF16_ATOL = 2e-2
+BF16_REL_L2 = 1e-2
+
+
+def ensure_built():
+    """Build libpa.so if nothing is built (tests call the build only then)."""
+    if not os.path.exists(LIB):
+        sys.path.insert(0, ROOT)
+        from paged_kv_attention_22_amd import build
+        build.build()
+
+
+def dev(x: np.ndarray, device="cuda") -> torch.Tensor:
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bit patterns of a device tensor as numpy (uint16 / uint32)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    return t.numpy()
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().double().numpy()
+
+
+class DeviceBatch:
+    """Device copies of a workloads.PagedBatch."""
+
+    def __init__(self, b, device="cuda"):
+        self.b = b
+        self.k_pool = dev(b.k_pool, device)
+        self.v_pool = dev(b.v_pool, device)
+        self.q = dev(b.q, device)
+        self.new_k = dev(b.new_k, device)
+        self.new_v = dev(b.new_v, device)
+        self.slot_mapping = dev(b.slot_mapping, device)
+        self.block_tables = dev(b.block_tables, device)
+        self.context_lens = dev(b.context_lens, device)
+        self.query_start_loc = dev(b.query_start_loc, device)
+
+
+def errors(out: np.ndarray, ref: np.ndarray) -> tuple[float, float]:
+    diff = out - ref
+    max_abs = float(np.abs(diff).max()) if diff.size else 0.0
+    denom = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(diff)) / denom if denom > 0 else float(np.linalg.norm(diff))
+    return max_abs, rel
+
+
+def assert_close(out: np.ndarray, ref: np.ndarray, dtype: str, what: str = "") -> tuple[float, float]:
+    assert out.shape == ref.shape, (out.shape, ref.shape)
+    assert np.isfinite(out).all(), f"{what}: non-finite output"
+    max_abs, rel = errors(out, ref)
+    if dtype == "f32":
+        assert max_abs <= F32_ATOL, f"{what}: max-abs {max_abs:.3e} > {F32_ATOL}"
+    else:
+        assert max_abs <= BF16_ATOL and rel <= BF16_REL_L2, \
+            f"{what}: max-abs {max_abs:.3e} (<= {BF16_ATOL}), rel-L2 {rel:.3e} (<= {BF16_REL_L2})"
+    return max_abs, rel

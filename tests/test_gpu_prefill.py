@@ -1,0 +1,112 @@
+"""pa_prefill_chunk on the GPU: mixed prefill-chunk + decode batches against
+the fp64 oracle, and the chunk reductions (n = 1 rows are decode, a chunk
+split in two gives the same rows, a chunk's last row equals a decode)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import DeviceBatch, assert_close, dev, ensure_built, f64
+from workloads import mixed_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    ensure_built()
+    import paged_kv_attention_22_amd as m
+    return m
+
+
+WORKLOADS = {
+    "mixed_small": lambda: mixed_prefill(chunks=3, chunk_len=40, prior_hi=100, n_decode=5,
+                                         dec_lo=1, dec_hi=300),
+    "mixed_tiny_chunks": lambda: mixed_prefill(chunks=4, chunk_len=5, prior_hi=40, n_decode=3,
+                                               dec_lo=1, dec_hi=100),
+    "mixed_one_row_chunks": lambda: mixed_prefill(chunks=2, chunk_len=1, prior_hi=40,
+                                                  n_decode=2, dec_lo=1, dec_hi=50),
+    "prefill_only_p0": lambda: mixed_prefill(chunks=2, chunk_len=70, prior_hi=0, n_decode=0),
+    "mixed_full": mixed_prefill,
+}
+
+_cache = {}
+
+
+def prepared(name):
+    if name not in _cache:
+        b = WORKLOADS[name]()
+        kp, vp = oracle.kv_write(b.k_pool, b.v_pool, b.new_k, b.new_v, b.slot_mapping)
+        ref = oracle.attention(b.q, b.query_start_loc, kp, vp, b.block_tables, b.context_lens,
+                               b.scale, b.dtype)
+        _cache[name] = (b, ref)
+    return _cache[name]
+
+
+def run(pa, d, b, part=0, write=True):
+    if write:
+        pa.kv_write(d.new_k, d.new_v, d.slot_mapping, d.k_pool, d.v_pool)
+    o = pa.prefill_chunk(d.q, d.query_start_loc, b.num_prefill_seqs, b.max_query_len, d.k_pool,
+                         d.v_pool, d.block_tables, d.context_lens, b.max_context_len,
+                         scale=b.scale, partition_tokens=part)
+    torch.cuda.synchronize()
+    return o
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_prefill_matches_oracle(pa, name):
+    b, ref = prepared(name)
+    d = DeviceBatch(b)
+    for i, part in enumerate([0, -1, 64]):
+        print(f"[prefill] {name} S={b.num_seqs} prefill={b.num_prefill_seqs} "
+              f"T={b.total_query_tokens} part={part}", flush=True)
+        out = run(pa, d, b, part, write=(i == 0))
+        max_abs, rel = assert_close(f64(out), ref, b.dtype, f"{name} part={part}")
+        print(f"    max-abs {max_abs:.3e} rel-L2 {rel:.3e}", flush=True)
+
+
+def test_chunk_split_invariance(pa):
+    """One chunk of n rows equals two chunks of n/2 rows, the first seeing
+    the context truncated at its own end."""
+    b, _ = prepared("mixed_small")
+    d = DeviceBatch(b)
+    whole = f64(run(pa, d, b))
+    n = int(b.query_lens[0])
+    h = n // 2
+    L = int(b.context_lens[0])
+    for lo, hi, ctx in [(0, h, L - n + h), (h, n, L)]:
+        o = pa.prefill_chunk(d.q[lo:hi].contiguous(), dev(np.array([0, hi - lo], np.int32)), 1,
+                             hi - lo, d.k_pool, d.v_pool, d.block_tables[:1].contiguous(),
+                             dev(np.array([ctx], np.int32)), ctx, scale=b.scale)
+        torch.cuda.synchronize()
+        assert_close(f64(o), whole[lo:hi], b.dtype, f"rows {lo}:{hi}")
+
+
+def test_last_chunk_row_equals_decode(pa):
+    b, _ = prepared("mixed_small")
+    d = DeviceBatch(b)
+    whole = f64(run(pa, d, b))
+    last = (b.query_start_loc[1:b.num_prefill_seqs + 1] - 1).tolist()
+    o = pa.decode(d.q[last].contiguous(), d.k_pool, d.v_pool,
+                  d.block_tables[:b.num_prefill_seqs].contiguous(),
+                  d.context_lens[:b.num_prefill_seqs].contiguous(), b.max_context_len,
+                  scale=b.scale)
+    torch.cuda.synchronize()
+    assert_close(f64(o), whole[last], b.dtype, "last rows vs decode")
+
+
+def test_decode_rows_match_pa_decode(pa):
+    """The decode rows of a mixed batch are the same computation as pa_decode
+    (same split choice), so they agree bit for bit."""
+    b, _ = prepared("mixed_small")
+    d = DeviceBatch(b)
+    whole = run(pa, d, b, part=64)
+    npre = b.num_prefill_seqs
+    rows = b.query_start_loc[npre:-1].tolist()
+    o = pa.decode(d.q[rows].contiguous(), d.k_pool, d.v_pool,
+                  d.block_tables[npre:].contiguous(), d.context_lens[npre:].contiguous(),
+                  b.max_context_len, scale=b.scale, partition_tokens=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), whole[rows].view(torch.int16))
