@@ -1,11 +1,233 @@
-// Matrix-core causal attention for prefill chunks (placeholder until the
-// MFMA kernel lands: every chunk row takes the vector path).
+// Matrix-core causal attention for prefill chunks (bf16, gfx950 MFMA).
+//
+// A chunk of n new query tokens of a sequence with context length L holds
+// rows (token t, head hh) of the kv head's GQA group, n*G rows in all; row
+// (t, hh) sees keys 0 .. L-n+t.  One workgroup of 4 waves owns 64 rows of one
+// (sequence, kv head); each wave owns 16.  Keys arrive in tiles of 32 (two
+// 16-token blocks, gathered through the block table into LDS); the tile is
+// shared by all four waves.
+//
+// Per tile and wave (v_mfma_f32_16x16x32_bf16, D = A*B + C, lane l holds
+// A[l%16][k-slice l/16], B[k-slice l/16][l%16], D[4*(l/16)+r][l%16]):
+//   S^T = K * Q^T      A = K rows from LDS, B = the wave's Q rows (registers);
+//                      lane l ends with row l%16's scores for keys
+//                      4*(l/16)+r and 16+4*(l/16)+r, r = 0..3.
+//   online softmax     in that layout: max across the 4 lanes sharing a row,
+//                      the row sum kept per lane and added up at the end.
+//   O^T += V^T * P^T   A = V^T from LDS (V is transposed while staged),
+//                      B = the probabilities exactly as the S^T step left
+//                      them, so P never moves between lanes.
+// The contraction slot -> key mapping of the second product (slot p < 4: key
+// 4*(l/16)+p, p >= 4: key 16+4*(l/16)+p-4) is used by both of its operands.
+#include "pa_device.hpp"
 #include "pa_internal.hpp"
 
 namespace pa {
+namespace {
 
-bool chunks_supported(int32_t, int32_t, int32_t) { return false; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-int32_t launch_chunks(const ChunkArgs&, hipStream_t) { return PA_ERR_UNSUPPORTED; }
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kKeys = 32;   // keys per tile
+constexpr int kRowsPerWave = 16;
+constexpr int kWaves = 4;
+constexpr int kRowsPerGroup = kRowsPerWave * kWaves;
+
+__device__ __forceinline__ floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
+    constexpr int KS = D / 32;           // 32-wide slices of head_dim (first product)
+    constexpr int MT = D / 16;           // 16-dim tiles of the output (second product)
+    constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
+    constexpr int LOADS = kKeys * CPR / (kWaves * 64);  // chunks per thread per tile
+    constexpr int KROW = D * 2 + 16;     // LDS bytes per K row (padded)
+    constexpr int VROW = kKeys * 2 + 8;  // LDS bytes per V^T row (padded)
+    static_assert(LOADS >= 1, "tile loader");
+    __shared__ __align__(16) unsigned char lds_k[kKeys * KROW];
+    __shared__ __align__(16) unsigned char lds_v[D * VROW];
+
+    const int s = blockIdx.z, g = blockIdx.y;
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int qs = a.query_start_loc[s];
+    const int n = a.query_start_loc[s + 1] - qs;
+    const int rows = n * G;
+    if (rows < a.min_pairs) return;  // the vector path handles this sequence
+    const int row0 = blockIdx.x * kRowsPerGroup;
+    if (row0 >= rows) return;
+    const int cap = min(a.max_context_len, a.max_blocks * kBlock);
+    const int L = min(max(a.context_lens[s], 0), cap);
+    const int prior = L - n;  // keys before the chunk
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, kg = lane >> 4;
+    const int R = row0 + wave * kRowsPerWave + li;  // this lane's row
+    const bool row_ok = R < rows;
+    const int t = R / G, hh = R - t * G;
+    const int lim = prior + t;  // last visible key of the row
+
+    // Keys this workgroup / this wave needs.
+    const int last_row = min(row0 + kRowsPerGroup, rows) - 1;
+    const int kend = min(prior + last_row / G + 1, L);
+    const int ntiles = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
+    const int wrow0 = row0 + wave * kRowsPerWave;
+    const int wkend = wrow0 < rows ? min(prior + (min(wrow0 + kRowsPerWave, rows) - 1) / G + 1, L) : 0;
+
+    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+    const uint16_t* q = static_cast<const uint16_t*>(a.q);
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row_ok) v = ld16(q + ((int64_t)(qs + t) * Hq + g * G + hh) * D + ks * 32 + kg * 8);
+        qf[ks] = as_bf16x8(v);
+    }
+
+    const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
+    const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
+    const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
+    const int64_t tok_stride = (int64_t)Hkv * D;
+
+    // Loader: thread tid moves chunks ci = tid + 256*u of the tile (key ci/CPR,
+    // 16-byte piece ci%CPR) from the pool into registers.
+    uint4 kreg[LOADS], vreg[LOADS];
+    auto load_tile = [&](int j0) {
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+            const int ci = tid + u * kWaves * 64;
+            const int key = ci / CPR, c = ci % CPR;
+            const int j = j0 + key;
+            kreg[u] = make_uint4(0, 0, 0, 0);
+            vreg[u] = make_uint4(0, 0, 0, 0);
+            if (j < L) {
+                const int blk = min(max(bt[j / kBlock], 0), a.num_blocks - 1);
+                const int64_t off = ((int64_t)blk * kBlock + (j % kBlock)) * tok_stride + (int64_t)g * D + c * 8;
+                kreg[u] = ld16(kpool + off);
+                vreg[u] = ld16(vpool + off);
+            }
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+            const int ci = tid + u * kWaves * 64;
+            const int key = ci / CPR, c = ci % CPR;
+            *reinterpret_cast<uint4*>(lds_k + key * KROW + c * 16) = kreg[u];
+            const uint32_t w[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint16_t val = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+                *reinterpret_cast<uint16_t*>(lds_v + (c * 8 + e) * VROW + key * 2) = val;
+            }
+        }
+    };
+
+    const float sl2 = a.scale * kLog2e;
+    float m = kNegInf, lsum = 0.0f;
+    floatx4 acc[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (ntiles > 0) load_tile(0);
+    for (int it = 0; it < ntiles; ++it) {
+        const int j0 = it * kKeys;
+        store_tile();
+        __syncthreads();
+        if (it + 1 < ntiles) load_tile(j0 + kKeys);  // in flight during the math below
+
+        if (j0 < wkend) {
+            // S^T tiles for keys j0..j0+15 and j0+16..j0+31.
+            floatx4 st[2];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const uint4 kv = *reinterpret_cast<const uint4*>(
+                        lds_k + (mt * 16 + li) * KROW + (ks * 32 + kg * 8) * 2);
+                    c = mfma(as_bf16x8(kv), qf[ks], c);
+                }
+                st[mt] = c;
+            }
+            float sc[8];
+            float mx = kNegInf;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = j0 + mt * 16 + kg * 4 + r;
+                    const float v = (j <= lim) ? st[mt][r] * sl2 : kNegInf;
+                    sc[mt * 4 + r] = v;
+                    mx = fmaxf(mx, v);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mn = fmaxf(m, mx);
+            const float mref = (mn == kNegInf) ? 0.0f : mn;
+            const float alpha = fast_exp2(m - mref);
+            m = mn;
+            uint32_t pk[4];
+            float psum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const __bf16 lo = static_cast<__bf16>(fast_exp2(sc[2 * i] - mref));
+                const __bf16 hi = static_cast<__bf16>(fast_exp2(sc[2 * i + 1] - mref));
+                psum += static_cast<float>(lo) + static_cast<float>(hi);
+                pk[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+            }
+            lsum = lsum * alpha + psum;
+            const bf16x8 pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                acc[mt] *= alpha;
+                const unsigned char* vrow = lds_v + (mt * 16 + li) * VROW + kg * 8;
+                const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
+                const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 32);
+                acc[mt] = mfma(as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y)), pb, acc[mt]);
+            }
+        }
+        __syncthreads();
+    }
+
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (!row_ok) return;
+    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+    uint16_t* out = static_cast<uint16_t*>(a.out) + ((int64_t)(qs + t) * Hq + g * G + hh) * D + kg * 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const uint2 o = make_uint2(pack_bf16x2(acc[mt][0] * inv, acc[mt][1] * inv),
+                                   pack_bf16x2(acc[mt][2] * inv, acc[mt][3] * inv));
+        *reinterpret_cast<uint2*>(out + mt * 16) = o;
+    }
+}
+
+}  // namespace
+
+bool chunks_supported(int32_t dtype, int32_t head_dim, int32_t group) {
+    return dtype == PA_BF16 && (head_dim == 64 || head_dim == 128) && group >= 1 &&
+           group <= kMaxGroup;
+}
+
+int32_t launch_chunks(const ChunkArgs& a, hipStream_t stream) {
+    const int group = a.num_q_heads / a.num_kv_heads;
+    if (!chunks_supported(a.dtype, a.head_dim, group)) return PA_ERR_UNSUPPORTED;
+    if (a.num_seqs == 0 || a.max_query_len == 0) return PA_OK;
+    const int64_t tiles = ((int64_t)a.max_query_len * group + kRowsPerGroup - 1) / kRowsPerGroup;
+    if (tiles > INT32_MAX || a.num_seqs > 65535) return PA_ERR_SHAPE;
+    dim3 grid((unsigned)tiles, a.num_kv_heads, a.num_seqs);
+    if (a.head_dim == 128)
+        hipLaunchKernelGGL(chunk_kernel<128>, grid, dim3(kWaves * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL(chunk_kernel<64>, grid, dim3(kWaves * 64), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
 
 }  // namespace pa

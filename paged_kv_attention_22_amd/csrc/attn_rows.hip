@@ -7,12 +7,17 @@
 // partitions (split-context, flash-decoding style) give a long or ragged batch
 // enough workgroups; their partial softmax states are merged by merge_kernel.
 //
-// Lane layout inside a wave: a token's [head_dim] row of K (or V) is R
-// 16-byte chunks, so R consecutive lanes hold one token and a wave covers
-// 64/R tokens per load.  A block of 16 tokens is NT = 16*R/64 loads per lane.
-// Each lane group of R lanes keeps its own running max / sum / accumulator
-// (fp32 online softmax); the groups, then the waves, are merged at the end.
-// q.k partial sums are reduced across the R lanes with DPP row operations.
+// Lane layout inside a wave: a token's [head_dim] row of K (or V) is split
+// over R consecutive lanes, each holding V 16-byte chunks (V = 1: one load
+// instruction covers 64/R whole rows; two chunks per lane cut the DPP steps
+// but measured slower through the higher register count), and a wave covers
+// 64/R tokens at once.  A block of 16 tokens is
+// NT = 16*R/64 tokens per lane.  Each lane group of R lanes keeps its own
+// running max / sum / accumulator (fp32 online softmax); the groups, then the
+// waves, are merged at the end.  q.k partial sums are reduced across the R
+// lanes with DPP row operations.  The running max is only raised when a score
+// exceeds it by more than 2^8 (lazy rescaling): the exponentials stay below
+// 256, and the accumulator is rescaled rarely instead of every block.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -79,18 +84,23 @@ __device__ __forceinline__ void store_chunk(T* dst, const float* o) {
 struct Item {
     int seq;
     int row;
-    int len;   // keys visible to this row
+    int n;     // query rows of the sequence
+    int i;     // this row's index among them
     bool skip; // left to the matrix-core kernel
 };
 
-__device__ __forceinline__ Item resolve(const RowsArgs& a, int z, int group) {
+// Which sequence and q/out row grid index z stands for.  Decode items read
+// nothing but the optional processing order; the context length is loaded
+// separately so that its latency overlaps the first q and block-id loads.
+__device__ __forceinline__ Item locate(const RowsArgs& a, int z, int group) {
     Item it;
     it.skip = false;
-    const int cap = min(a.max_context_len, a.max_blocks * kBlock);
     if (a.query_start_loc == nullptr) {
-        it.seq = a.seq_begin + z;
-        it.row = a.row_begin + z;
-        it.len = min(max(a.context_lens[it.seq], 0), cap);
+        const int zz = a.order != nullptr ? a.order[z] : z;
+        it.seq = a.seq_begin + zz;
+        it.row = a.row_begin + zz;
+        it.n = 1;
+        it.i = 0;
         return it;
     }
     const int row = a.row_begin + z;
@@ -100,112 +110,191 @@ __device__ __forceinline__ Item resolve(const RowsArgs& a, int z, int group) {
         const int mid = (lo + hi + 1) >> 1;
         if (qsl[mid] <= row) lo = mid; else hi = mid - 1;
     }
-    const int n = qsl[lo + 1] - qsl[lo];
-    const int i = row - qsl[lo];
-    const int L = min(max(a.context_lens[lo], 0), cap);
     it.seq = lo;
     it.row = row;
-    it.len = min(max(L - n + i + 1, 0), L);
-    it.skip = a.mfma_min_pairs > 0 && n * group >= a.mfma_min_pairs;
+    it.n = qsl[lo + 1] - qsl[lo];
+    it.i = row - qsl[lo];
+    it.skip = a.mfma_min_pairs > 0 && it.n * group >= a.mfma_min_pairs;
     return it;
+}
+
+// Keys visible to the row: 0 .. L-n+i, with L clamped to what the table holds.
+__device__ __forceinline__ int visible_len(const RowsArgs& a, const Item& it, int L) {
+    const int cap = min(a.max_context_len, a.max_blocks * kBlock);
+    L = min(max(L, 0), cap);
+    return min(max(L - it.n + it.i + 1, 0), L);
+}
+
+// Workgroups are numbered with the kv head fastest, then the partition, then
+// the row: the kv heads of one row and partition read the same token rows of
+// the pool (each head a 2*D-byte slice of every row) at about the same time.
+__device__ __forceinline__ void unit_of(const RowsArgs& a, int& z, int& g, int& part) {
+    const int id = blockIdx.x;
+    const int nparts = a.part_tokens > 0 ? a.nparts : 1;
+    g = id % a.num_kv_heads;
+    const int rest = id / a.num_kv_heads;
+    part = rest % nparts;
+    z = rest / nparts;
 }
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
     constexpr int E = Elem<T>::kPerChunk;
-    constexpr int R = D / E;          // lanes per token row
-    constexpr int TPW = 64 / R;       // token rows per wave load
-    constexpr int NT = kBlock / TPW;  // tokens of one block per lane
-    static_assert(TPW >= 1 && NT >= 1, "lane layout");
+    constexpr int V = 1;                      // 16-byte chunks per lane per token
+    constexpr int EL = V * E;                 // elements per lane per token
+    constexpr int R = D / EL;                 // lanes per token row
+    constexpr int TPW = 64 / R;               // token rows per wave
+    constexpr int NT = kBlock / TPW;          // tokens of one block per lane
+    static_assert(TPW >= 1 && NT >= 1 && R >= 4, "lane layout");
+    constexpr float kLazy = 8.0f;             // log2 headroom before rescaling
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c = lane % R;
     const int rg = lane / R;
-    const int z = blockIdx.x, g = blockIdx.y, part = blockIdx.z;
+    int z, g, part;
+    unit_of(a, z, g, part);
 
-    const Item it = resolve(a, z, G);
+    const Item it = locate(a, z, G);
     if (it.skip) return;
-    const int nblk = (it.len + kBlock - 1) / kBlock;
     const bool split = a.part_tokens > 0;
-    int b0 = 0, b1 = nblk;
+    const int pb = split ? a.part_tokens / kBlock : 0;
+    const int b0 = split ? part * pb : 0;
+    const int first = b0 + wave;  // this wave's blocks: first + k*kWaves
+
+    // Issue the length, q and first block-id loads together.
+    const int Lraw = a.context_lens[it.seq];
+    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+    // Chunk u of this lane covers elements (u*R + c)*E .. +E of the row.
+    const T* qp = static_cast<const T*>(a.q) + ((int64_t)it.row * Hq + g * G) * D + c * E;
+    uint4 qv[G][V];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int u = 0; u < V; ++u) qv[h][u] = ld16(qp + h * D + u * R * E);
+    // Block ids: lane i holds the id of block k = kbase + i (one load per 64).
+    const int32_t* bt = a.block_tables + (int64_t)it.seq * a.max_blocks;
+    int ids = 0;
+    auto fetch_ids = [&](int kbase) {
+        const int jj = first + (kbase + lane) * kWaves;
+        ids = jj < a.max_blocks ? bt[jj] : 0;
+    };
+    fetch_ids(0);
+
+    const int len = visible_len(a, it, Lraw);
+    const int nblk = (len + kBlock - 1) / kBlock;
+    int b1 = nblk;
+    bool final_out = true;
     if (split) {
-        const int pb = a.part_tokens / kBlock;
-        b0 = part * pb;
         b1 = min(nblk, b0 + pb);
-        if (b0 >= b1) return;  // the merge kernel ignores missing partitions
+        if (b0 >= b1 && !(part == 0 && nblk == 0)) return;  // the merge ignores missing partitions
+        final_out = nblk <= pb;  // a single partition writes the output itself
     }
 
-    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
-    const T* qp = static_cast<const T*>(a.q) + ((int64_t)it.row * Hq + g * G) * D + c * E;
-    uint4 qv[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) qv[h] = ld16(qp + h * D);
-
-    float m[G], l[G], acc[G][E];
+    float m[G], l[G], acc[G][EL];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         m[h] = kNegInf;
         l[h] = 0.0f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[h][e] = 0.0f;
+        for (int e = 0; e < EL; ++e) acc[h][e] = 0.0f;
     }
 
-    const int32_t* bt = a.block_tables + (int64_t)it.seq * a.max_blocks;
+    // This wave's blocks are jb = first + k*kWaves, k < nk; blocks below
+    // len/16 are full, and only the sequence's last block can be partial.
+    const int nk = b1 > first ? (b1 - first + kWaves - 1) / kWaves : 0;
+    const int nfull = len / kBlock;
+    const int nkf = nfull > first ? min(nk, (nfull - first + kWaves - 1) / kWaves) : 0;
+    auto block_of = [&](int k) -> int {
+        if ((k & 63) == 0 && k != 0) fetch_ids(k);
+        const int blk = __builtin_amdgcn_readlane(ids, k & 63);
+        return min(max(blk, 0), a.num_blocks - 1);
+    };
+
     const int64_t tok_stride = (int64_t)Hkv * D;  // elements between tokens
     const T* kbase = static_cast<const T*>(a.k_pool) + (int64_t)g * D + c * E + rg * tok_stride;
     const T* vbase = static_cast<const T*>(a.v_pool) + (int64_t)g * D + c * E + rg * tok_stride;
     const float sl2 = a.scale * kLog2e;
 
-    for (int jb = b0 + wave; jb < b1; jb += kWaves) {
-        const int blk = min(max(bt[jb], 0), a.num_blocks - 1);
-        const int64_t off = (int64_t)blk * kBlock * tok_stride;
-        uint4 kc[NT], vc[NT];
+    auto load = [&](uint4 (&kk)[NT][V], uint4 (&vv)[NT][V], int k) {
+        const int64_t off = (int64_t)block_of(k) * kBlock * tok_stride;
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
-            kc[i] = ld16(kbase + off + (int64_t)(i * TPW) * tok_stride);
-            vc[i] = ld16(vbase + off + (int64_t)(i * TPW) * tok_stride);
-        }
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int u = 0; u < V; ++u) {
+                const int64_t o = off + (int64_t)(i * TPW) * tok_stride + u * R * E;
+                kk[i][u] = ld16_stream(kbase + o);
+                vv[i][u] = ld16_stream(vbase + o);
+            }
+    };
+    auto compute = [&](const uint4 (&kk)[NT][V], const uint4 (&vv)[NT][V], int k, bool masked) {
+        bool valid[NT];
+        const int tok0 = (first + k * kWaves) * kBlock + rg;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) valid[i] = !masked || tok0 + i * TPW < len;
         float sc[NT][G];
 #pragma unroll
         for (int i = 0; i < NT; ++i)
 #pragma unroll
-            for (int h = 0; h < G; ++h) sc[i][h] = group_sum<R>(chunk_dot<T>(qv[h], kc[i])) * sl2;
-
-        if ((jb + 1) * kBlock > it.len) {  // last block: mask tokens past the length
-            const int tok0 = jb * kBlock + rg;
+            for (int h = 0; h < G; ++h) {
+                float d = chunk_dot<T>(qv[h][0], kk[i][0]);
 #pragma unroll
-            for (int i = 0; i < NT; ++i) {
-                const bool valid = tok0 + i * TPW < it.len;
-#pragma unroll
-                for (int h = 0; h < G; ++h) sc[i][h] = valid ? sc[i][h] : kNegInf;
-                vc[i] = valid ? vc[i] : make_uint4(0, 0, 0, 0);
+                for (int u = 1; u < V; ++u) d += chunk_dot<T>(qv[h][u], kk[i][u]);
+                d = group_sum<R>(d) * sl2;
+                // excluded, never weighted by zero: past-the-length slots may hold NaN
+                sc[i][h] = valid[i] ? d : kNegInf;
             }
-        }
-        float vf[NT][E];
+        float vf[NT][EL];
 #pragma unroll
-        for (int i = 0; i < NT; ++i) unpack<T>(vc[i], vf[i]);
-
+        for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int u = 0; u < V; ++u) {
+                const uint4 w = valid[i] ? vv[i][u] : make_uint4(0, 0, 0, 0);
+                unpack<T>(w, &vf[i][u * E]);
+            }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float mb = sc[0][h];
 #pragma unroll
             for (int i = 1; i < NT; ++i) mb = fmaxf(mb, sc[i][h]);
-            const float mn = fmaxf(m[h], mb);
-            const float mref = (mn == kNegInf) ? 0.0f : mn;
-            const float alpha = fast_exp2(m[h] - mref);
-            l[h] *= alpha;
+            if (mb > m[h] + kLazy) {  // raise the reference and rescale
+                const float alpha = fast_exp2(m[h] - mb);
+                l[h] *= alpha;
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+                for (int e = 0; e < EL; ++e) acc[h][e] *= alpha;
+                m[h] = mb;
+            }
+            const float mref = (m[h] == kNegInf) ? 0.0f : m[h];
 #pragma unroll
             for (int i = 0; i < NT; ++i) {
                 const float p = fast_exp2(sc[i][h] - mref);
                 l[h] += p;
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[h][e] = fmaf(p, vf[i][e], acc[h][e]);
+                for (int e = 0; e < EL; ++e) acc[h][e] = fmaf(p, vf[i][e], acc[h][e]);
             }
-            m[h] = mn;
         }
+    };
+
+    // Full blocks, two register buffers: the next block's loads are in flight
+    // while the current one is computed.  The reload at the end of the loop
+    // is unconditional (clamped to the last full block, which is then already
+    // cached) so that both buffers keep their registers across iterations.
+    uint4 ka[NT][V], va[NT][V], kb[NT][V], vb[NT][V];
+    int k = 0;
+    if (nkf > 0) load(ka, va, 0);
+    for (; k + 1 < nkf; k += 2) {
+        load(kb, vb, k + 1);
+        compute(ka, va, k, false);
+        load(ka, va, min(k + 2, nkf - 1));
+        compute(kb, vb, k + 1, false);
+    }
+    if (k < nkf) {
+        compute(ka, va, k, false);
+        ++k;
+    }
+    if (k < nk) {  // the partial last block
+        load(ka, va, k);
+        compute(ka, va, k, true);
     }
 
     // Merge the lane groups of this wave (they hold disjoint token subsets).
@@ -220,7 +309,7 @@ __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
             const float a1 = fast_exp2(m[h] - mref), a2 = fast_exp2(mo - mref);
             l[h] = l[h] * a1 + lo * a2;
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
+            for (int e = 0; e < EL; ++e) {
                 const float ao = __shfl_xor(acc[h][e], o);
                 acc[h][e] = acc[h][e] * a1 + ao * a2;
             }
@@ -236,7 +325,7 @@ __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) s_acc[wave][h][c * E + e] = acc[h][e];
+            for (int e = 0; e < EL; ++e) s_acc[wave][h][((e / E) * R + c) * E + e % E] = acc[h][e];
             if (c == 0) {
                 s_m[wave][h] = m[h];
                 s_l[wave][h] = l[h];
@@ -244,8 +333,9 @@ __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
         }
     }
     __syncthreads();
-    for (int t = threadIdx.x; t < G * R; t += kWaves * 64) {
-        const int h = t / R, cc = t % R;
+    constexpr int CPR = D / E;  // 16-byte chunks per output row
+    for (int t = threadIdx.x; t < G * CPR; t += kWaves * 64) {
+        const int h = t / CPR, cc = t % CPR;
         float M = s_m[0][h];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
@@ -261,7 +351,7 @@ __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
             for (int e = 0; e < E; ++e) o[e] = fmaf(s_acc[w][h][cc * E + e], wt, o[e]);
         }
         const int hq = g * G + h;
-        if (!split) {
+        if (final_out) {
             const float inv = den > 0.0f ? 1.0f / den : 0.0f;
 #pragma unroll
             for (int e = 0; e < E; ++e) o[e] *= inv;
@@ -283,37 +373,59 @@ __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
 
 // Log-sum-exp merge of the partitions of one (row, q head):
 // out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
+// Rows whose context fits one partition were written by rows_kernel.  The
+// first eight partials are loaded before any reduction so that the loads
+// overlap instead of forming a chain.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void merge_kernel(const RowsArgs a, int group) {
+    constexpr int kPre = 8;
     const int z = blockIdx.x, hq = blockIdx.y;
-    const Item it = resolve(a, z, group);
+    const Item it = locate(a, z, group);
     if (it.skip) return;
+    const int len = visible_len(a, it, a.context_lens[it.seq]);
     const int pb = a.part_tokens / kBlock;
-    const int nblk = (it.len + kBlock - 1) / kBlock;
+    const int nblk = (len + kBlock - 1) / kBlock;
     const int np = (nblk + pb - 1) / pb;
+    if (np <= 1) return;
     const int Hq = a.num_q_heads;
+    const int lane = threadIdx.x;
     const int64_t slot0 = ((int64_t)z * Hq + hq) * a.nparts;
     const int64_t nslots = (int64_t)a.num_items * Hq * a.nparts;
     const float* ms = a.ws + nslots * D + slot0;
     const float* ls = ms + nslots;
     const float* acc = a.ws + slot0 * D;
+    const int d = min(lane * 2, D - 2);
 
+    float2 v[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u)
+        v[u] = u < np ? *reinterpret_cast<const float2*>(acc + (int64_t)u * D + d) : make_float2(0.0f, 0.0f);
     float M = kNegInf;
-    for (int p = 0; p < np; ++p) M = fmaxf(M, ms[p]);
+    for (int p = lane; p < np; p += 64) M = fmaxf(M, ms[p]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     const float mref = (M == kNegInf) ? 0.0f : M;
-    float den = 0.0f;
-    for (int p = 0; p < np; ++p) den = fmaf(ls[p], fast_exp2(ms[p] - mref), den);
+    float den = 0.0f, wl = 0.0f;
+    for (int p = lane; p < np; p += 64) den = fmaf(ls[p], fast_exp2(ms[p] - mref), den);
+    if (lane < np) wl = fast_exp2(ms[lane] - mref);  // weight of partial `lane`
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
 
-    const int d = threadIdx.x * 2;
-    if (d >= D) return;
     float o0 = 0.0f, o1 = 0.0f;
-    for (int p = 0; p < np; ++p) {
-        const float wt = fast_exp2(ms[p] - mref);
-        const float2 v = *reinterpret_cast<const float2*>(acc + (int64_t)p * D + d);
-        o0 = fmaf(v.x, wt, o0);
-        o1 = fmaf(v.y, wt, o1);
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const float wt = __shfl(wl, u);
+        o0 = fmaf(v[u].x, wt, o0);
+        o1 = fmaf(v[u].y, wt, o1);
     }
+    for (int p = kPre; p < np; ++p) {
+        const float wt = fast_exp2(ms[p] - mref);
+        const float2 w = *reinterpret_cast<const float2*>(acc + (int64_t)p * D + d);
+        o0 = fmaf(w.x, wt, o0);
+        o1 = fmaf(w.y, wt, o1);
+    }
+    if (lane * 2 >= D) return;
     o0 *= inv;
     o1 *= inv;
     T* dst = static_cast<T*>(a.out) + ((int64_t)it.row * Hq + hq) * D + d;
@@ -324,11 +436,61 @@ __global__ __launch_bounds__(64) void merge_kernel(const RowsArgs a, int group) 
     }
 }
 
+// Counting sort of the sequences by context length, longest first, in one
+// workgroup: histogram of (length >> shift) in LDS, exclusive scan in
+// descending key order, then each sequence takes the next slot of its key.
+// Equal keys come out in no particular order (every order is correct; only
+// the scheduling changes).
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBuckets = 4096;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* context_lens, int seq_begin,
+                                                            int n, int cap, int shift, int32_t* order) {
+    __shared__ int start[kPlanBuckets];
+    __shared__ int wave_sum[kPlanThreads / 64];
+    const int t = threadIdx.x;
+    for (int b = t; b < kPlanBuckets; b += kPlanThreads) start[b] = 0;
+    __syncthreads();
+    auto key_of = [&](int i) {
+        const int L = min(max(context_lens[seq_begin + i], 0), cap);
+        return min(L >> shift, kPlanBuckets - 1);
+    };
+    for (int i = t; i < n; i += kPlanThreads) atomicAdd(&start[key_of(i)], 1);
+    __syncthreads();
+    // Thread t owns descending positions r = 4t .. 4t+3, i.e. keys kPlanBuckets-1-r.
+    constexpr int kPer = kPlanBuckets / kPlanThreads;
+    int cnt[kPer], sum = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        cnt[j] = start[kPlanBuckets - 1 - (t * kPer + j)];
+        sum += cnt[j];
+    }
+    int incl = sum;  // inclusive scan over threads: within the wave, then across waves
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if ((t & 63) >= o) incl += y;
+    }
+    if ((t & 63) == 63) wave_sum[t >> 6] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < (t >> 6); ++w) before += wave_sum[w];
+    int excl = before + incl - sum;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        start[kPlanBuckets - 1 - (t * kPer + j)] = excl;
+        excl += cnt[j];
+    }
+    __syncthreads();
+    for (int i = t; i < n; i += kPlanThreads) order[atomicAdd(&start[key_of(i)], 1)] = i;
+}
+
 template <typename T, int D, int G>
 int32_t launch_typed(const RowsArgs& a, hipStream_t stream) {
     const bool split = a.part_tokens > 0;
-    dim3 grid(a.num_items, a.num_kv_heads, split ? a.nparts : 1);
-    hipLaunchKernelGGL((rows_kernel<T, D, G>), grid, dim3(kWaves * 64), 0, stream, a);
+    const int64_t units = (int64_t)a.num_items * a.num_kv_heads * (split ? a.nparts : 1);
+    if (units > INT32_MAX) return PA_ERR_SHAPE;
+    hipLaunchKernelGGL((rows_kernel<T, D, G>), dim3((unsigned)units), dim3(kWaves * 64), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
     if (split) {
         hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.num_items, a.num_q_heads), dim3(64), 0,
@@ -354,6 +516,16 @@ int32_t launch_group(const RowsArgs& a, int group, hipStream_t stream) {
 }
 
 }  // namespace
+
+int32_t launch_plan(const int32_t* context_lens, int32_t seq_begin, int32_t n,
+                    int32_t max_context_len, int32_t* order, hipStream_t stream) {
+    if (n <= 0) return PA_OK;
+    int shift = 0;
+    while ((max_context_len >> shift) >= kPlanBuckets) ++shift;
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, context_lens, seq_begin, n,
+                       max_context_len, shift, order);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
 
 int32_t launch_rows(const RowsArgs& a, hipStream_t stream) {
     if (a.num_items == 0) return PA_OK;

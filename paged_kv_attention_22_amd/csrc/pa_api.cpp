@@ -37,18 +37,20 @@ int32_t check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
-// Split-context choice.  Enough workgroups to cover 256 compute units several
-// times over, and partitions short enough that a ragged batch does not leave a
-// long tail of single long sequences.
+// Split-context choice.  With at least 1024 (row, kv head) units the batch
+// already covers the 256 compute units several times over: one pass, with the
+// longest-first order keeping the tail short.  Fewer units (few sequences,
+// long contexts) are split into partitions, the longest that still give
+// about 2048 workgroups.
 int32_t choose_partition(int64_t items, int32_t num_kv_heads, int32_t max_context_len,
                          int32_t requested) {
     if (requested < 0) return -1;
     if (requested > 0) return requested;
     const int64_t units = items * num_kv_heads;
-    if (max_context_len <= 256 || units >= 8192) return -1;
-    int32_t part = 256;
+    if (units >= 1024 || max_context_len <= 128) return -1;
+    int32_t part = 1024;
     while (part > 64 && units * ceil_div(max_context_len, part) < 2048) part /= 2;
-    return part;
+    return ceil_div(max_context_len, part) > 1 ? part : -1;
 }
 
 size_t split_bytes(int64_t items, int32_t num_q_heads, int32_t head_dim,
@@ -58,25 +60,66 @@ size_t split_bytes(int64_t items, int32_t num_q_heads, int32_t head_dim,
     return (size_t)(items * num_q_heads * nparts * (int64_t)(head_dim + 2) * 4);
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Longest-first processing order for decode rows: with a ragged batch the
+// workgroups of the longest sequences start first and the short ones fill the
+// end, instead of a long sequence starting last and running alone.  Worth its
+// extra (one-workgroup) launch once the batch spans several waves of
+// workgroups.
+bool use_plan(int64_t items, int32_t num_kv_heads, int32_t max_context_len, int32_t part) {
+    const int64_t units = items * num_kv_heads * (part > 0 ? ceil_div(max_context_len, part) : 1);
+    return items >= 16 && units >= 1024;
+}
+
+size_t plan_bytes(int64_t items) { return align256((size_t)items * 4); }
+
+// Workspace of one vector-path launch: [order (decode rows, when planned)]
+// [split partials].
+size_t rows_bytes(int64_t items, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t max_context_len, int32_t part, bool decode_rows) {
+    if (items <= 0) return 0;
+    size_t n = 0;
+    if (decode_rows && use_plan(items, num_kv_heads, max_context_len, part)) n += plan_bytes(items);
+    return n + split_bytes(items, num_q_heads, head_dim, max_context_len, part);
+}
+
 int32_t check_partition(int32_t requested) {
     if (requested > 0 && requested % kBlock != 0) return PA_ERR_SHAPE;
     return PA_OK;
 }
 
-// Fills the common part of a RowsArgs and checks the split workspace.
+// Fills the common part of a RowsArgs and checks the workspace.  Decode rows
+// (no query_start_loc) may get a longest-first order in front of the partials.
 int32_t prepare_rows(RowsArgs& a, int64_t items, int32_t part, void* workspace,
                      size_t workspace_bytes) {
     a.num_items = (int32_t)items;
     a.part_tokens = part;
     a.nparts = part > 0 ? ceil_div(a.max_context_len, part) : 1;
-    a.ws = static_cast<float*>(workspace);
-    if (part > 0) {
-        if (a.nparts > 65535) return PA_ERR_SHAPE;
-        const size_t need = split_bytes(items, a.num_q_heads, a.head_dim, a.max_context_len, part);
-        if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PA_ERR_WORKSPACE;
-        if (need > 0 && !aligned16(workspace)) return PA_ERR_ALIGN;
+    if (part > 0 && a.nparts > 65535) return PA_ERR_SHAPE;
+    const bool decode_rows = a.query_start_loc == nullptr;
+    const bool plan = decode_rows && use_plan(items, a.num_kv_heads, a.max_context_len, part);
+    const size_t need = rows_bytes(items, a.num_q_heads, a.num_kv_heads, a.head_dim,
+                                   a.max_context_len, part, decode_rows);
+    if (need > 0) {
+        if (workspace == nullptr || workspace_bytes < need) return PA_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return PA_ERR_ALIGN;
     }
+    char* w = static_cast<char*>(workspace);
+    a.order = plan ? reinterpret_cast<int32_t*>(w) : nullptr;
+    a.ws = part > 0 ? reinterpret_cast<float*>(w + (plan ? plan_bytes(items) : 0)) : nullptr;
     return PA_OK;
+}
+
+// Plan (when chosen) and vector-path attention for one prepared launch.
+int32_t run_rows(const RowsArgs& a, hipStream_t s) {
+    if (a.num_items == 0) return PA_OK;
+    if (a.order != nullptr) {
+        if (int32_t st = launch_plan(a.context_lens, a.seq_begin, a.num_items, a.max_context_len,
+                                     const_cast<int32_t*>(a.order), s))
+            return st;
+    }
+    return launch_rows(a, s);
 }
 
 }  // namespace
@@ -137,7 +180,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
         max_context_len < 0 || check_partition(partition_tokens))
         return 0;
     const int32_t part = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_tokens);
-    return split_bytes(num_seqs, num_q_heads, head_dim, max_context_len, part);
+    return rows_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, part, true);
 }
 
 int32_t pa_decode(const void* q, const void* k_pool, const void* v_pool, pa_pool_desc pool,
@@ -178,7 +221,7 @@ int32_t pa_decode(const void* q, const void* k_pool, const void* v_pool, pa_pool
     a.out = out;
     const int32_t part = choose_partition(num_seqs, pool.num_kv_heads, max_context_len, partition_tokens);
     if (int32_t st = prepare_rows(a, num_seqs, part, workspace, workspace_bytes)) return st;
-    return launch_rows(a, static_cast<hipStream_t>(stream));
+    return run_rows(a, static_cast<hipStream_t>(stream));
 }
 
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_prefill_seqs,
@@ -194,11 +237,11 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_prefill_seqs,
     size_t need = 0;
     if (prefill_rows > 0) {
         const int32_t part = choose_partition(prefill_rows, num_kv_heads, max_context_len, partition_tokens);
-        need = split_bytes(prefill_rows, num_q_heads, head_dim, max_context_len, part);
+        need = rows_bytes(prefill_rows, num_q_heads, num_kv_heads, head_dim, max_context_len, part, false);
     }
     if (num_decode > 0) {
         const int32_t part = choose_partition(num_decode, num_kv_heads, max_context_len, partition_tokens);
-        const size_t d = split_bytes(num_decode, num_q_heads, head_dim, max_context_len, part);
+        const size_t d = rows_bytes(num_decode, num_q_heads, num_kv_heads, head_dim, max_context_len, part, true);
         if (d > need) need = d;
     }
     return need;
@@ -288,9 +331,9 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
         if (int32_t st = launch_chunks(c, s)) return st;
     }
     if (prefill_rows > 0)
-        if (int32_t st = launch_rows(pre, s)) return st;
+        if (int32_t st = run_rows(pre, s)) return st;
     if (num_decode > 0)
-        if (int32_t st = launch_rows(dec, s)) return st;
+        if (int32_t st = run_rows(dec, s)) return st;
     return PA_OK;
 }
 

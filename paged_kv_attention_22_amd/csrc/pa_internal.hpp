@@ -27,6 +27,9 @@ struct RowsArgs {
     int32_t seq_begin, seq_end;
     int32_t row_begin;
     int32_t num_items;
+    // Without query_start_loc: optional processing order, item order[z] is
+    // handled z-th (longest first, written by launch_plan); NULL = index order.
+    const int32_t* order;
     // With query_start_loc: items whose sequence gives at least this many
     // (row, head) pairs per kv head are left to the matrix-core kernel
     // (0 = handle every item here).
@@ -41,6 +44,11 @@ struct RowsArgs {
 };
 
 int32_t launch_rows(const RowsArgs& a, hipStream_t stream);
+
+// Counting sort of sequences seq_begin .. seq_begin+n-1 by context length,
+// longest first, into order[0..n) (indices relative to seq_begin).
+int32_t launch_plan(const int32_t* context_lens, int32_t seq_begin, int32_t n,
+                    int32_t max_context_len, int32_t* order, hipStream_t stream);
 
 struct KvWriteArgs {
     const void* k;

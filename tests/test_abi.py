@@ -113,7 +113,11 @@ def test_partition_choice_and_workspace(pa):
     assert pa.decode_partition_tokens(4, 1, 64, 0) == -1
     p = pa.decode_partition_tokens(64, 4, 8192, 0)
     assert p > 0 and p % 16 == 0
-    # workspace = items * Hq * nparts * (D + 2) fp32 values
+    # many (row, kv head) units: one pass, longest first
+    assert pa.decode_partition_tokens(256, 8, 2048, 0) == -1
+    # workspace = the longest-first order (items int32, 256-byte aligned) when
+    # the batch is large, then items * Hq * nparts * (D + 2) fp32 partials
     n = -(-2048 // 256)
-    assert pa.decode_workspace_bytes(256, 16, 8, 128, 2048, 256) == 256 * 16 * n * 130 * 4
-    assert pa.decode_workspace_bytes(256, 16, 8, 128, 2048, -1) == 0
+    assert pa.decode_workspace_bytes(256, 16, 8, 128, 2048, 256) == 1024 + 256 * 16 * n * 130 * 4
+    assert pa.decode_workspace_bytes(256, 16, 8, 128, 2048, -1) == 1024
+    assert pa.decode_workspace_bytes(4, 2, 1, 64, 64, -1) == 0     # small batch: nothing

@@ -222,3 +222,19 @@ def test_rejected_call_leaves_output(pa):
                   out=out, partition_tokens=24)
     torch.cuda.synchronize()
     assert (out == 3.0).all()
+
+
+def test_longest_first_order_is_bit_identical(pa):
+    """A large batch is processed longest-first (an internal schedule); every
+    row must come out bit-identical to decoding it in a small batch, which is
+    processed in index order."""
+    b, _ = prepared("qwen3_full")
+    d = DeviceBatch(b)
+    full = bits(run_decode(pa, d, b, -1))
+    for lo in range(0, b.num_seqs, 64):
+        idx = list(range(lo, min(lo + 8, b.num_seqs)))
+        o = pa.decode(d.q[idx].contiguous(), d.k_pool, d.v_pool, d.block_tables[idx].contiguous(),
+                      d.context_lens[idx].contiguous(), b.max_context_len, scale=b.scale,
+                      partition_tokens=-1)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(o), full[idx]), lo
