@@ -66,9 +66,98 @@ def decode_bytes(b) -> int:
     return kv + qo + tables + 4 * b.num_seqs
 
 
+def chunk_flops(b) -> int:
+    """Algorithmic flops of the prefill chunks: every visible (row, key) pair
+    costs 2*D for q.k and 2*D for the weighted V sum, per q head."""
+    total = 0
+    for s in range(b.num_prefill_seqs):
+        n, L = int(b.query_lens[s]), int(b.context_lens[s])
+        pairs = n * (L - n) + n * (n + 1) // 2
+        total += pairs * b.num_q_heads * 4 * b.head_dim
+    return total
+
+
 def kv_write_bytes(b) -> int:
     T = int((b.slot_mapping >= 0).sum())
     return 2 * 2 * T * b.num_kv_heads * b.head_dim * b.elem_bytes + 4 * b.slot_mapping.size
+
+
+def time_calls(fn, steps: int, warmup: int):
+    """Per-call durations (us) from HIP events on the current stream."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+
+
+def bench_mixed(args, b, up, dev) -> dict:
+    """Mixed chunked-prefill step: KV write of every new token, then
+    pa_prefill_chunk over the chunks and the decode rows.  Also times the
+    chunk rows alone (matrix cores) and the decode rows alone."""
+    import numpy as np
+    import torch
+
+    import paged_kv_attention_22_amd as pa
+    pools = [(up(b.k_pool), up(b.v_pool)) for _ in range(2)]
+    q, new_k, new_v = up(b.q), up(b.new_k), up(b.new_v)
+    slots, tables, lens = up(b.slot_mapping), up(b.block_tables), up(b.context_lens)
+    qsl = up(b.query_start_loc)
+    out = torch.empty_like(q)
+    npre, S = b.num_prefill_seqs, b.num_seqs
+    for kp, vp in pools:
+        pa.kv_write(new_k, new_v, slots, kp, vp)
+    rows_pre = int(b.query_start_loc[npre])
+    sub = dict(q=q[:rows_pre], qsl=qsl[:npre + 1].contiguous(), tables=tables[:npre].contiguous(),
+               lens=lens[:npre].contiguous())
+    dec = dict(q=q[rows_pre:].contiguous(), tables=tables[npre:].contiguous(),
+               lens=lens[npre:].contiguous())
+    maxc = b.max_context_len
+
+    def step(i):
+        kp, vp = pools[i & 1]
+        pa.kv_write(new_k, new_v, slots, kp, vp)
+        pa.prefill_chunk(q, qsl, npre, b.max_query_len, kp, vp, tables, lens, maxc,
+                         scale=b.scale, out=out)
+
+    def chunks(i):
+        kp, vp = pools[i & 1]
+        pa.prefill_chunk(sub["q"], sub["qsl"], npre, b.max_query_len, kp, vp, sub["tables"],
+                         sub["lens"], maxc, scale=b.scale)
+
+    def decode_rows(i):
+        kp, vp = pools[i & 1]
+        pa.decode(dec["q"], kp, vp, dec["tables"], dec["lens"], maxc, scale=b.scale)
+
+    log(f"[bench] timing {args.steps} mixed steps")
+    step_us = time_calls(step, args.steps, args.warmup)
+    chunk_us = time_calls(chunks, args.steps, args.warmup)
+    dec_us = time_calls(decode_rows, args.steps, args.warmup)
+    flops = chunk_flops(b)
+    es = b.elem_bytes
+    dec_bytes = int(b.context_lens[npre:].sum()) * 2 * b.num_kv_heads * b.head_dim * es
+    ms = float(np.mean(step_us)) * 1e-3
+    return {
+        "metric": "pa_prefill_chunk mixed batch step time (KV write + chunks + decode rows)",
+        "value": round(ms * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": b.dtype, "data": "synthetic",
+        "config": {"workload": b.name, "recipe": b.recipe, "seed": b.seed, "num_seqs": S,
+                   "num_prefill_seqs": npre, "total_query_tokens": b.total_query_tokens},
+        "chunks": {"us": round(float(np.median(chunk_us)), 2), "gflop": round(flops / 1e9, 3),
+                   "tflops": round(flops / (float(np.median(chunk_us)) * 1e-6) / 1e12, 2),
+                   "peak_tflops": 2500.0},
+        "decode_rows": {"us": round(float(np.median(dec_us)), 2), "bytes": dec_bytes,
+                        "gbs": round(dec_bytes / (float(np.median(dec_us)) * 1e-6) / 1e9, 1)},
+    }
 
 
 def cpu_baseline(b, min_seconds: float = 10.0) -> dict:
@@ -103,6 +192,8 @@ def main() -> int:
     ap.add_argument("--workload", default="qwen3_06b_decode",
                     help="generator preset (default: the Qwen3-0.6B batch-256 decode step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -115,15 +206,24 @@ def main() -> int:
     import paged_kv_attention_22_amd as pa
     from workloads import PRESETS
 
+    if args.calibrate_copy:
+        # An elementwise kernel that reads 1 GiB and writes 1 GiB: the
+        # counters' readings for it convert counter units to bytes.
+        x = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.mul(x, 1, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "torch.mul int32, 1 GiB read + 1 GiB written per launch",
+                          "launches": 3}))
+        return 0
+
     if not os.path.exists(pa.LIB_PATH):
         from paged_kv_attention_22_amd import build as pa_build
         pa_build.build()
 
     log(f"[bench] generating {args.workload}")
     b = PRESETS[args.workload]()
-    if b.num_prefill_seqs:
-        print("bench.py measures decode steps; pick a decode workload", file=sys.stderr)
-        return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
@@ -134,6 +234,10 @@ def main() -> int:
         if x.dtype == np.uint16:
             return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(x).to(dev)
+
+    if b.num_prefill_seqs:
+        print(json.dumps(bench_mixed(args, b, up, dev)), flush=True)
+        return 0
 
     pools = [(up(b.k_pool), up(b.v_pool)) for _ in range(2)]
     q, new_k, new_v = up(b.q), up(b.new_k), up(b.new_v)

@@ -439,25 +439,37 @@ __global__ __launch_bounds__(64) void merge_kernel(const RowsArgs a, int group) 
 // Counting sort of the sequences by context length, longest first, in one
 // workgroup: histogram of (length >> shift) in LDS, exclusive scan in
 // descending key order, then each sequence takes the next slot of its key.
-// Equal keys come out in no particular order (every order is correct; only
-// the scheduling changes).
-constexpr int kPlanThreads = 1024;
-constexpr int kPlanBuckets = 4096;
+// Each length is read from memory once (kept in registers for up to
+// kPlanKeep items per thread).  Equal keys come out in no particular order
+// (every order is correct; only the scheduling changes).
+constexpr int kPlanThreads = 256;
+constexpr int kPlanBuckets = 1024;
+constexpr int kPlanKeep = 8;
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* context_lens, int seq_begin,
                                                             int n, int cap, int shift, int32_t* order) {
     __shared__ int start[kPlanBuckets];
     __shared__ int wave_sum[kPlanThreads / 64];
     const int t = threadIdx.x;
-    for (int b = t; b < kPlanBuckets; b += kPlanThreads) start[b] = 0;
-    __syncthreads();
     auto key_of = [&](int i) {
         const int L = min(max(context_lens[seq_begin + i], 0), cap);
         return min(L >> shift, kPlanBuckets - 1);
     };
-    for (int i = t; i < n; i += kPlanThreads) atomicAdd(&start[key_of(i)], 1);
+    int key[kPlanKeep];
+#pragma unroll
+    for (int j = 0; j < kPlanKeep; ++j) {
+        const int i = t + j * kPlanThreads;
+        key[j] = i < n ? key_of(i) : -1;
+    }
+    for (int b = t; b < kPlanBuckets; b += kPlanThreads) start[b] = 0;
     __syncthreads();
-    // Thread t owns descending positions r = 4t .. 4t+3, i.e. keys kPlanBuckets-1-r.
+#pragma unroll
+    for (int j = 0; j < kPlanKeep; ++j)
+        if (key[j] >= 0) atomicAdd(&start[key[j]], 1);
+    for (int i = t + kPlanKeep * kPlanThreads; i < n; i += kPlanThreads) atomicAdd(&start[key_of(i)], 1);
+    __syncthreads();
+    // Thread t owns descending positions r = kPer*t .. kPer*t+kPer-1, i.e.
+    // keys kPlanBuckets-1-r.
     constexpr int kPer = kPlanBuckets / kPlanThreads;
     int cnt[kPer], sum = 0;
 #pragma unroll
@@ -482,7 +494,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* conte
         excl += cnt[j];
     }
     __syncthreads();
-    for (int i = t; i < n; i += kPlanThreads) order[atomicAdd(&start[key_of(i)], 1)] = i;
+#pragma unroll
+    for (int j = 0; j < kPlanKeep; ++j)
+        if (key[j] >= 0) order[atomicAdd(&start[key[j]], 1)] = t + j * kPlanThreads;
+    for (int i = t + kPlanKeep * kPlanThreads; i < n; i += kPlanThreads)
+        order[atomicAdd(&start[key_of(i)], 1)] = i;
 }
 
 template <typename T, int D, int G>

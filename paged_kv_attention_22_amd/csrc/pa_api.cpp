@@ -146,6 +146,8 @@ int32_t pa_kv_write(const void* k, const void* v, int64_t k_token_stride, int64_
     if (int32_t st = check_pool(pool)) return st;
     if (num_tokens < 0) return PA_ERR_SHAPE;
     if (num_tokens == 0) return PA_OK;
+    if ((int64_t)pool.num_kv_heads * pool.head_dim * elem_size(pool.dtype) > INT32_MAX)
+        return PA_ERR_SHAPE;
     if (!k || !v || !slot_mapping || !k_pool || !v_pool) return PA_ERR_NULL;
     const int es = elem_size(pool.dtype);
     const int64_t row_elems = (int64_t)pool.num_kv_heads * pool.head_dim;
