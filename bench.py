@@ -310,7 +310,8 @@ def main() -> int:
                       "p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                       "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2)},
         "roofline": {
-            "kernel": "pa_decode (split partials + merge)" if part > 0 else "pa_decode (one pass)",
+            "kernel": ("pa_decode call: plan + rows (split partials) + merge kernels" if part > 0
+                       else "pa_decode call: plan + rows kernels (one pass, longest first)"),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
