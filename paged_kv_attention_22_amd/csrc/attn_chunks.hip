@@ -3,22 +3,27 @@
 // A chunk of n new query tokens of a sequence with context length L holds
 // rows (token t, head hh) of the kv head's GQA group, n*G rows in all; row
 // (t, hh) sees keys 0 .. L-n+t.  One workgroup of 4 waves owns 64 rows of one
-// (sequence, kv head); each wave owns 16.  Keys arrive in tiles of 32 (two
-// 16-token blocks, gathered through the block table into LDS); the tile is
-// shared by all four waves.
+// (sequence, kv head); each wave owns 16.  Keys arrive in tiles of 64 (four
+// 16-token blocks, gathered through the block table into LDS, K and V both
+// row-major); the tile is shared by all four waves.
 //
 // Per tile and wave (v_mfma_f32_16x16x32_bf16, D = A*B + C, lane l holds
 // A[l%16][k-slice l/16], B[k-slice l/16][l%16], D[4*(l/16)+r][l%16]):
 //   S^T = K * Q^T      A = K rows from LDS, B = the wave's Q rows (registers);
 //                      lane l ends with row l%16's scores for keys
-//                      4*(l/16)+r and 16+4*(l/16)+r, r = 0..3.
+//                      16*mt + 4*(l/16) + r, mt = 0..3, r = 0..3.
 //   online softmax     in that layout: max across the 4 lanes sharing a row,
 //                      the row sum kept per lane and added up at the end.
-//   O^T += V^T * P^T   A = V^T from LDS (V is transposed while staged),
-//                      B = the probabilities exactly as the S^T step left
-//                      them, so P never moves between lanes.
-// The contraction slot -> key mapping of the second product (slot p < 4: key
-// 4*(l/16)+p, p >= 4: key 16+4*(l/16)+p-4) is used by both of its operands.
+//   O^T += V^T * P^T   per 32 keys: B = the probabilities exactly as the S^T
+//                      step left them (contraction slot p < 4: key
+//                      4*(l/16)+p, p >= 4: key 16+4*(l/16)+p-4), A = V^T read
+//                      from the row-major V tile with ds_read_b64_tr_b16, whose
+//                      16-lane transpose hands lane i element i%4 of lanes
+//                      i/4 + 4k: lanes 4k..4k+3 of a group point at key row k
+//                      (dims 4 apart), and every lane receives one dim of four
+//                      consecutive keys.
+// Two LDS buffers: the next tile is written while the current one is read,
+// one barrier per tile; the tile after that is already loading from memory.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -27,13 +32,16 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kKeys = 32;   // keys per tile
+constexpr int kKeys = 64;   // keys per tile
 constexpr int kRowsPerWave = 16;
 constexpr int kWaves = 4;
 constexpr int kRowsPerGroup = kRowsPerWave * kWaves;
+constexpr int kMaxLdsBlocks = 512;  // block ids staged in LDS (8192 keys)
 
 __device__ __forceinline__ floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -41,17 +49,23 @@ __device__ __forceinline__ floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+__device__ __forceinline__ uint2 ld_tr(const unsigned char* p) {
+    const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
 template <int D>
 __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
     constexpr int KS = D / 32;           // 32-wide slices of head_dim (first product)
     constexpr int MT = D / 16;           // 16-dim tiles of the output (second product)
     constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
     constexpr int LOADS = kKeys * CPR / (kWaves * 64);  // chunks per thread per tile
-    constexpr int KROW = D * 2 + 16;     // LDS bytes per K row (padded)
-    constexpr int VROW = kKeys * 2 + 8;  // LDS bytes per V^T row (padded)
+    constexpr int ROW = D * 2 + 16;      // LDS bytes per key row (padded)
+    constexpr int TILE = kKeys * ROW;
     static_assert(LOADS >= 1, "tile loader");
-    __shared__ __align__(16) unsigned char lds_k[kKeys * KROW];
-    __shared__ __align__(16) unsigned char lds_v[D * VROW];
+    __shared__ __align__(16) unsigned char lds_k[2 * TILE];
+    __shared__ __align__(16) unsigned char lds_v[2 * TILE];
+    __shared__ int lds_bt[kMaxLdsBlocks];
 
     const int s = blockIdx.z, g = blockIdx.y;
     const int G = a.num_q_heads / a.num_kv_heads;
@@ -79,6 +93,12 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
     const int wrow0 = row0 + wave * kRowsPerWave;
     const int wkend = wrow0 < rows ? min(prior + (min(wrow0 + kRowsPerWave, rows) - 1) / G + 1, L) : 0;
 
+    const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
+    const int nb = (kend + kBlock - 1) / kBlock;
+    const bool bt_lds = nb <= kMaxLdsBlocks;
+    if (bt_lds)
+        for (int i = tid; i < nb; i += kWaves * 64) lds_bt[i] = min(max(bt[i], 0), a.num_blocks - 1);
+
     const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
     const uint16_t* q = static_cast<const uint16_t*>(a.q);
     bf16x8 qf[KS];
@@ -88,14 +108,17 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
         if (row_ok) v = ld16(q + ((int64_t)(qs + t) * Hq + g * G + hh) * D + ks * 32 + kg * 8);
         qf[ks] = as_bf16x8(v);
     }
+    __syncthreads();  // lds_bt
 
-    const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
     const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
     const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
     const int64_t tok_stride = (int64_t)Hkv * D;
 
-    // Loader: thread tid moves chunks ci = tid + 256*u of the tile (key ci/CPR,
-    // 16-byte piece ci%CPR) from the pool into registers.
+    // Loader: thread tid moves chunks ci = tid + 256*u of a tile (key ci/CPR,
+    // 16-byte piece ci%CPR) from the pool into registers.  Only keys below
+    // kend are loaded (no row of this workgroup sees a later key, and their
+    // block ids are exactly the ones staged in LDS); the others become zeros,
+    // whatever their slots hold (NaN included).
     uint4 kreg[LOADS], vreg[LOADS];
     auto load_tile = [&](int j0) {
 #pragma unroll
@@ -105,26 +128,22 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
             const int j = j0 + key;
             kreg[u] = make_uint4(0, 0, 0, 0);
             vreg[u] = make_uint4(0, 0, 0, 0);
-            if (j < L) {
-                const int blk = min(max(bt[j / kBlock], 0), a.num_blocks - 1);
+            if (j < kend) {
+                const int bi = j / kBlock;  // < nb
+                const int blk = min(max(bt_lds ? lds_bt[bi] : bt[bi], 0), a.num_blocks - 1);
                 const int64_t off = ((int64_t)blk * kBlock + (j % kBlock)) * tok_stride + (int64_t)g * D + c * 8;
                 kreg[u] = ld16(kpool + off);
                 vreg[u] = ld16(vpool + off);
             }
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int buf) {
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {
             const int ci = tid + u * kWaves * 64;
             const int key = ci / CPR, c = ci % CPR;
-            *reinterpret_cast<uint4*>(lds_k + key * KROW + c * 16) = kreg[u];
-            const uint32_t w[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint16_t val = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
-                *reinterpret_cast<uint16_t*>(lds_v + (c * 8 + e) * VROW + key * 2) = val;
-            }
+            *reinterpret_cast<uint4*>(lds_k + buf * TILE + key * ROW + c * 16) = kreg[u];
+            *reinterpret_cast<uint4*>(lds_v + buf * TILE + key * ROW + c * 16) = vreg[u];
         }
     };
 
@@ -134,31 +153,33 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
 #pragma unroll
     for (int i = 0; i < MT; ++i) acc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    if (ntiles > 0) load_tile(0);
+    if (ntiles > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    if (ntiles > 1) load_tile(kKeys);
+    __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
         const int j0 = it * kKeys;
-        store_tile();
-        __syncthreads();
-        if (it + 1 < ntiles) load_tile(j0 + kKeys);  // in flight during the math below
-
+        const int buf = it & 1;
         if (j0 < wkend) {
-            // S^T tiles for keys j0..j0+15 and j0+16..j0+31.
-            floatx4 st[2];
+            const unsigned char* kt = lds_k + buf * TILE;
+            const unsigned char* vt = lds_v + buf * TILE;
+            floatx4 st[4];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
+            for (int mt = 0; mt < 4; ++mt) {
                 floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const uint4 kv = *reinterpret_cast<const uint4*>(
-                        lds_k + (mt * 16 + li) * KROW + (ks * 32 + kg * 8) * 2);
+                    const uint4 kv = *reinterpret_cast<const uint4*>(kt + (mt * 16 + li) * ROW + (ks * 32 + kg * 8) * 2);
                     c = mfma(as_bf16x8(kv), qf[ks], c);
                 }
                 st[mt] = c;
             }
-            float sc[8];
+            float sc[16];
             float mx = kNegInf;
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int j = j0 + mt * 16 + kg * 4 + r;
@@ -172,10 +193,10 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
             const float mref = (mn == kNegInf) ? 0.0f : mn;
             const float alpha = fast_exp2(m - mref);
             m = mn;
-            uint32_t pk[4];
+            uint32_t pk[8];
             float psum = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 8; ++i) {
                 const __bf16 lo = static_cast<__bf16>(fast_exp2(sc[2 * i] - mref));
                 const __bf16 hi = static_cast<__bf16>(fast_exp2(sc[2 * i + 1] - mref));
                 psum += static_cast<float>(lo) + static_cast<float>(hi);
@@ -183,16 +204,24 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
                         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
             }
             lsum = lsum * alpha + psum;
-            const bf16x8 pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                acc[mt] *= alpha;
-                const unsigned char* vrow = lds_v + (mt * 16 + li) * VROW + kg * 8;
-                const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
-                const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 32);
-                acc[mt] = mfma(as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y)), pb, acc[mt]);
+            for (int i = 0; i < MT; ++i) acc[i] *= alpha;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                // keys 32*kk .. 32*kk+31: slots 0-3 from st[2kk], 4-7 from st[2kk+1]
+                const bf16x8 pb = as_bf16x8(make_uint4(pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]));
+                const int k4 = lane >> 2 & 3;  // key row within the lane's group of 4
+                const unsigned char* v0 = vt + (32 * kk + 4 * kg + k4) * ROW + (lane & 3) * 8;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const uint2 lo = ld_tr(v0 + mt * 32);
+                    const uint2 hi = ld_tr(v0 + 16 * ROW + mt * 32);
+                    acc[mt] = mfma(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, acc[mt]);
+                }
             }
         }
+        if (it + 1 < ntiles) store_tile(buf ^ 1);
+        if (it + 2 < ntiles) load_tile(j0 + 2 * kKeys);
         __syncthreads();
     }
 
