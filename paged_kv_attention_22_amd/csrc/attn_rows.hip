@@ -29,6 +29,23 @@ namespace {
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
+// Smallest GQA group that takes the matrix-core decode path (bf16).
+constexpr int kMfmaMinGroup = 4;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-lane transposing LDS read: lane i of each group of 16 receives element
+// i%4 of the 8-byte words addressed by lanes i/4 + 4k, k = 0..3.
+__device__ __forceinline__ uint2 ld_tr16(const unsigned char* p) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p)));
+}
 
 template <typename T>
 struct Elem;
@@ -135,6 +152,53 @@ __device__ __forceinline__ void unit_of(const RowsArgs& a, int& z, int& g, int& 
     const int rest = id / a.num_kv_heads;
     part = rest % nparts;
     z = rest / nparts;
+}
+
+// Merge the per-wave softmax states kWaves x (m, l, acc[D]) of the G heads
+// of one (row, kv head, partition) left in LDS, then write the normalised
+// output (final_out) or the partition's partial state for merge_kernel.
+template <typename T, int D, int G>
+__device__ __forceinline__ void combine_waves(const RowsArgs& a, const Item& it, int z, int g, int part,
+                                              bool final_out, const float (&s_acc)[kWaves][G][D],
+                                              const float (&s_m)[kWaves][G], const float (&s_l)[kWaves][G]) {
+    constexpr int E = Elem<T>::kPerChunk;
+    constexpr int CPR = D / E;  // 16-byte chunks per output row
+    const int Hq = a.num_q_heads;
+    for (int t = threadIdx.x; t < G * CPR; t += kWaves * 64) {
+        const int h = t / CPR, cc = t % CPR;
+        float M = s_m[0][h];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+        const float mref = (M == kNegInf) ? 0.0f : M;
+        float den = 0.0f, o[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float wt = fast_exp2(s_m[w][h] - mref);
+            den = fmaf(s_l[w][h], wt, den);
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = fmaf(s_acc[w][h][cc * E + e], wt, o[e]);
+        }
+        const int hq = g * G + h;
+        if (final_out) {
+            const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] *= inv;
+            store_chunk<T>(static_cast<T*>(a.out) + ((int64_t)it.row * Hq + hq) * D + cc * E, o);
+        } else {
+            const int64_t slot = ((int64_t)z * Hq + hq) * a.nparts + part;
+            float* wa = a.ws + slot * D + cc * E;
+#pragma unroll
+            for (int e = 0; e < E; e += 4) st16(wa + e, make_uint4(__float_as_uint(o[e]), __float_as_uint(o[e + 1]),
+                                                                   __float_as_uint(o[e + 2]), __float_as_uint(o[e + 3])));
+            if (cc == 0) {
+                const int64_t nslots = (int64_t)a.num_items * Hq * a.nparts;
+                a.ws[nslots * D + slot] = M;
+                a.ws[nslots * D + nslots + slot] = den;
+            }
+        }
+    }
 }
 
 template <typename T, int D, int G>
@@ -333,42 +397,210 @@ __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
         }
     }
     __syncthreads();
-    constexpr int CPR = D / E;  // 16-byte chunks per output row
-    for (int t = threadIdx.x; t < G * CPR; t += kWaves * 64) {
-        const int h = t / CPR, cc = t % CPR;
-        float M = s_m[0][h];
+    combine_waves<T, D, G>(a, it, z, g, part, final_out, s_acc, s_m, s_l);
+}
+
+// Decode rows on the matrix cores, for large GQA groups (bf16).  Same work
+// unit, partitions, processing order and wave merge as rows_kernel; the
+// per-token arithmetic moves to v_mfma_f32_16x16x32_bf16 so that the vector
+// units no longer pay G dot products, reductions and FMAs per loaded byte.
+// Each wave streams its own 32-token steps (two blocks):
+//   S^T = K * Q^T    A = the K rows straight from memory (lane l: token l%16,
+//                    dims 32*ks + 8*(l/16) .. +7), B = the group's q rows
+//                    (heads padded to 16 with zeros) held in registers; lane
+//                    l ends with head l%16's scores for tokens 16*mt +
+//                    4*(l/16) + r.
+//   O^T += V^T P^T   B = those probabilities (slot p < 4: token 4*(l/16)+p,
+//                    p >= 4: 16+4*(l/16)+p-4), A = V^T read with
+//                    ds_read_b64_tr_b16 from the wave's own row-major V tile in
+//                    LDS (written with 16-byte stores; no barrier needed, the
+//                    tile is private to the wave).
+template <int D, int G>
+__global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a) {
+    constexpr int KS = D / 32;                // 32-dim slices (first product)
+    constexpr int MT = D / 16;                // 16-dim output tiles (second product)
+    constexpr int CPR = D / 8;                // 16-byte chunks per token row
+    constexpr int VL = 32 * CPR / 64;         // V chunks per lane per step
+    constexpr int VROW = D * 2 + 16;          // LDS bytes per V row (padded)
+    constexpr int VT = 32 * VROW;             // one wave's V tile
+    constexpr float kLazy = 8.0f;
+    static_assert(G <= 16, "group fits the 16 columns of one MFMA tile");
+    __shared__ __align__(16) unsigned char s_v[kWaves * VT];
+    __shared__ float s_acc[kWaves][G][D];
+    __shared__ float s_m[kWaves][G];
+    __shared__ float s_l[kWaves][G];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int li = lane & 15, kg = lane >> 4;
+    int z, g, part;
+    unit_of(a, z, g, part);
+    const Item it = locate(a, z, G);
+    if (it.skip) return;
+    const bool split = a.part_tokens > 0;
+    const int pb = split ? a.part_tokens / kBlock : 0;
+    const int b0 = split ? part * pb : 0;
+
+    const int Lraw = a.context_lens[it.seq];
+    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+    bf16x8 qf[KS];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-        const float mref = (M == kNegInf) ? 0.0f : M;
-        float den = 0.0f, o[E];
+    for (int ks = 0; ks < KS; ++ks) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (li < G)
+            v = ld16(static_cast<const uint16_t*>(a.q) + ((int64_t)it.row * Hq + g * G + li) * D + ks * 32 + kg * 8);
+        qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+    // Block ids: lane i holds the id of block (b0 + 2*(wave + (kbase + i/2)*kWaves) + i%2).
+    const int32_t* bt = a.block_tables + (int64_t)it.seq * a.max_blocks;
+    int ids = 0;
+    auto fetch_ids = [&](int kbase) {
+        const int jj = b0 + 2 * (wave + (kbase + (lane >> 1)) * kWaves) + (lane & 1);
+        ids = jj < a.max_blocks ? bt[jj] : 0;
+    };
+    fetch_ids(0);
+
+    const int len = visible_len(a, it, Lraw);
+    const int nblk = (len + kBlock - 1) / kBlock;
+    int b1 = nblk;
+    bool final_out = true;
+    if (split) {
+        b1 = min(nblk, b0 + pb);
+        if (b0 >= b1 && !(part == 0 && nblk == 0)) return;
+        final_out = nblk <= pb;
+    }
+    // Steps of this wave: pair k covers blocks jb = b0 + 2*(wave + k*kWaves)
+    // and jb + 1; the steps with both blocks full come first, then at most one
+    // step that needs masking.
+    const int first = b0 + 2 * wave;
+    const int nk = b1 > first ? (b1 - first + 2 * kWaves - 1) / (2 * kWaves) : 0;
+    const int full_end = min(b1, len / kBlock);  // blocks below this are full
+    const int nkf = full_end >= first + 2 ? min(nk, (full_end - first - 2) / (2 * kWaves) + 1) : 0;
+    auto block_of = [&](int k, int half) -> int {
+        if ((k & 31) == 0 && k != 0 && half == 0) fetch_ids(k);
+        const int blk = __builtin_amdgcn_readlane(ids, ((k & 31) << 1) | half);
+        return min(max(blk, 0), a.num_blocks - 1);
+    };
+
+    const int64_t tok_stride = (int64_t)Hkv * D;
+    const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool) + (int64_t)g * D;
+    const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool) + (int64_t)g * D;
+    unsigned char* vt = s_v + wave * VT;
+    const float sl2 = a.scale * kLog2e;
+
+    float m = kNegInf, lsum = 0.0f;
+    floatx4 acc[MT];
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = 0.0f;
+    for (int i = 0; i < MT; ++i) acc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto load = [&](uint4 (&kf)[2][KS], uint4 (&vr)[VL], int k) {
+        const int jb = first + 2 * kWaves * k;
+        const int blk0 = block_of(k, 0);
+        const int blk1 = jb + 1 < b1 ? block_of(k, 1) : blk0;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float wt = fast_exp2(s_m[w][h] - mref);
-            den = fmaf(s_l[w][h], wt, den);
+        for (int mt = 0; mt < 2; ++mt) {
+            const int blk = mt ? blk1 : blk0;
 #pragma unroll
-            for (int e = 0; e < E; ++e) o[e] = fmaf(s_acc[w][h][cc * E + e], wt, o[e]);
+            for (int ks = 0; ks < KS; ++ks)
+                kf[mt][ks] = ld16_stream(kpool + ((int64_t)blk * kBlock + li) * tok_stride + ks * 32 + kg * 8);
         }
-        const int hq = g * G + h;
-        if (final_out) {
-            const float inv = den > 0.0f ? 1.0f / den : 0.0f;
 #pragma unroll
-            for (int e = 0; e < E; ++e) o[e] *= inv;
-            store_chunk<T>(static_cast<T*>(a.out) + ((int64_t)it.row * Hq + hq) * D + cc * E, o);
-        } else {
-            const int64_t slot = ((int64_t)z * Hq + hq) * a.nparts + part;
-            float* wa = a.ws + slot * D + cc * E;
+        for (int u = 0; u < VL; ++u) {
+            const int c = lane + 64 * u, tk = c / CPR, piece = c % CPR;
+            const int blk = tk < 16 ? blk0 : blk1;
+            vr[u] = ld16_stream(vpool + ((int64_t)blk * kBlock + (tk & 15)) * tok_stride + piece * 8);
+        }
+    };
+    auto compute = [&](const uint4 (&kf)[2][KS], const uint4 (&vr)[VL], int k, bool masked) {
+        const int pos0 = (first + 2 * kWaves * k) * kBlock;  // first token of the step
+        const int pend = min(len, b1 * kBlock);              // tokens at or past this are excluded
 #pragma unroll
-            for (int e = 0; e < E; e += 4) st16(wa + e, make_uint4(__float_as_uint(o[e]), __float_as_uint(o[e + 1]),
-                                                                   __float_as_uint(o[e + 2]), __float_as_uint(o[e + 3])));
-            if (cc == 0) {
-                const int64_t nslots = (int64_t)a.num_items * Hq * a.nparts;
-                a.ws[nslots * D + slot] = M;
-                a.ws[nslots * D + nslots + slot] = den;
+        for (int u = 0; u < VL; ++u) {
+            const int c = lane + 64 * u, tk = c / CPR, piece = c % CPR;
+            // excluded tokens are zeroed, never weighted by zero (their slots may hold NaN)
+            const uint4 w = (!masked || pos0 + tk < pend) ? vr[u] : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(vt + tk * VROW + piece * 16) = w;
+        }
+        floatx4 st[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) c = mfma16(__builtin_bit_cast(bf16x8, kf[mt][ks]), qf[ks], c);
+            st[mt] = c;
+        }
+        float sc[8];
+        float mx = kNegInf;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float v = st[mt][r] * sl2;
+                const bool ok = !masked || pos0 + mt * 16 + kg * 4 + r < pend;
+                sc[mt * 4 + r] = ok ? v : kNegInf;
+                mx = fmaxf(mx, sc[mt * 4 + r]);
             }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (mx > m + kLazy) {  // raise the reference and rescale
+            const float alpha = fast_exp2(m - mx);
+            lsum *= alpha;
+#pragma unroll
+            for (int i = 0; i < MT; ++i) acc[i] *= alpha;
+            m = mx;
+        }
+        const float mref = (m == kNegInf) ? 0.0f : m;
+        uint32_t pk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const __bf16 lo = static_cast<__bf16>(fast_exp2(sc[2 * i] - mref));
+            const __bf16 hi = static_cast<__bf16>(fast_exp2(sc[2 * i + 1] - mref));
+            lsum += static_cast<float>(lo) + static_cast<float>(hi);
+            pk[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's V tile is in LDS
+        const unsigned char* v0 = vt + (4 * kg + ((lane >> 2) & 3)) * VROW + (lane & 3) * 8;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const uint2 lo = ld_tr16(v0 + mt * 32);
+            const uint2 hi = ld_tr16(v0 + 16 * VROW + mt * 32);
+            acc[mt] = mfma16(__builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, acc[mt]);
+        }
+    };
+
+    uint4 ka[2][KS], va[VL], kb[2][KS], vb[VL];
+    int k = 0;
+    if (nkf > 0) load(ka, va, 0);
+    for (; k + 1 < nkf; k += 2) {
+        load(kb, vb, k + 1);
+        compute(ka, va, k, false);
+        load(ka, va, min(k + 2, nkf - 1));
+        compute(kb, vb, k + 1, false);
+    }
+    if (k < nkf) {
+        compute(ka, va, k, false);
+        ++k;
+    }
+    if (k < nk) {  // the step holding the partial block and/or the partition end
+        load(ka, va, k);
+        compute(ka, va, k, true);
+    }
+
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if (li < G) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_acc[wave][li][mt * 16 + kg * 4 + r] = acc[mt][r];
+        if (kg == 0) {
+            s_m[wave][li] = m;
+            s_l[wave][li] = lsum;
         }
     }
+    __syncthreads();
+    combine_waves<uint16_t, D, G>(a, it, z, g, part, final_out, s_acc, s_m, s_l);
 }
 
 // Log-sum-exp merge of the partitions of one (row, q head):
@@ -506,7 +738,10 @@ int32_t launch_typed(const RowsArgs& a, hipStream_t stream) {
     const bool split = a.part_tokens > 0;
     const int64_t units = (int64_t)a.num_items * a.num_kv_heads * (split ? a.nparts : 1);
     if (units > INT32_MAX) return PA_ERR_SHAPE;
-    hipLaunchKernelGGL((rows_kernel<T, D, G>), dim3((unsigned)units), dim3(kWaves * 64), 0, stream, a);
+    if constexpr (std::is_same_v<T, uint16_t> && G >= kMfmaMinGroup)
+        hipLaunchKernelGGL((mfma_rows_kernel<D, G>), dim3((unsigned)units), dim3(kWaves * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((rows_kernel<T, D, G>), dim3((unsigned)units), dim3(kWaves * 64), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
     if (split) {
         hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.num_items, a.num_q_heads), dim3(64), 0,

@@ -40,16 +40,17 @@ int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 // Split-context choice.  With at least 1024 (row, kv head) units the batch
 // already covers the 256 compute units several times over: one pass, with the
 // longest-first order keeping the tail short.  Fewer units (few sequences,
-// long contexts) are split into partitions, the longest that still give
-// about 2048 workgroups.
+// long contexts) are split into partitions, the longest that still give about
+// 1024 workgroups (longer partitions keep each wave streaming longer; shorter
+// ones add partial-state traffic and merge work).
 int32_t choose_partition(int64_t items, int32_t num_kv_heads, int32_t max_context_len,
                          int32_t requested) {
     if (requested < 0) return -1;
     if (requested > 0) return requested;
     const int64_t units = items * num_kv_heads;
     if (units >= 1024 || max_context_len <= 128) return -1;
-    int32_t part = 1024;
-    while (part > 64 && units * ceil_div(max_context_len, part) < 2048) part /= 2;
+    int32_t part = 2048;
+    while (part > 64 && units * ceil_div(max_context_len, part) < 1024) part /= 2;
     return ceil_div(max_context_len, part) > 1 ? part : -1;
 }
 

@@ -33,6 +33,14 @@ WORKLOADS = {
     "qwen3_full": qwen3_06b_decode,
     "long_small": lambda: long_context(batch=3, ctx=1500, shared_blocks=40),
     "long_full": long_context,
+    # the matrix-core decode path (bf16, group >= 4) at both head dims
+    "g4_d128": lambda: make_batch(61, name="g4_d128", dtype="bf16", num_q_heads=16, num_kv_heads=4,
+                                  head_dim=128, draw_lens=lambda rng: rng.integers(1, 700, size=21)),
+    "g8_d64": lambda: make_batch(62, name="g8_d64", dtype="bf16", num_q_heads=16, num_kv_heads=2,
+                                 head_dim=64, draw_lens=lambda rng: rng.integers(1, 900, size=19)),
+    "g5_d128_f32": lambda: make_batch(63, name="g5_d128_f32", dtype="f32", num_q_heads=10,
+                                      num_kv_heads=2, head_dim=128,
+                                      draw_lens=lambda rng: rng.integers(1, 300, size=6)),
 }
 
 _cache = {}
