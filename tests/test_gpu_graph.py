@@ -1,0 +1,95 @@
+"""Capture of a decode step (pa_kv_write + pa_decode) in a HIP graph, and a
+large batch that exercises every branch of the longest-first plan."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import assert_close, bits, dev, ensure_built, f64
+from workloads import f32_to_bf16_bits, make_batch, qwen3_06b_decode
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    ensure_built()
+    import paged_kv_attention_22_amd as m
+    return m
+
+
+def test_decode_step_graph_replays(pa):
+    """Capture once, replay four times with new q, new tokens, shorter
+    lengths and matching slots written eagerly in between; every replay must
+    match the oracle for the pool state it produced."""
+    b = qwen3_06b_decode(seed=71, batch=40, prompt=(30, 400), gen=(0, 300))
+    maxL = b.max_context_len
+    k_pool, v_pool = dev(b.k_pool), dev(b.v_pool)
+    q, new_k, new_v = dev(b.q), dev(b.new_k), dev(b.new_v)
+    slots, tables, lens = dev(b.slot_mapping), dev(b.block_tables), dev(b.context_lens)
+    out = torch.empty_like(q)
+    part = 64  # split path: plan, partials and merge all inside the graph
+    nbytes = pa.decode_workspace_bytes(b.num_seqs, 16, 8, 128, maxL, part)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def step():
+        pa.kv_write(new_k, new_v, slots, k_pool, v_pool)
+        pa.decode(q, k_pool, v_pool, tables, lens, maxL, scale=b.scale, out=out,
+                  partition_tokens=part, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                   # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+
+    kp_h, vp_h = b.k_pool.copy(), b.v_pool.copy()
+    kp_h, vp_h = oracle.kv_write(kp_h, vp_h, b.new_k, b.new_v, b.slot_mapping)  # warm-up's write
+    rng = np.random.default_rng(5)
+    L = b.context_lens.astype(np.int64)
+    for rep in range(4):
+        # eager work between replays: new inputs, lengths cut by up to 20 tokens
+        L = np.maximum(L - rng.integers(0, 20, size=L.shape), 1)
+        pos = L - 1
+        slots_h = (b.block_tables[np.arange(b.num_seqs), pos // 16].astype(np.int64) * 16
+                   + pos % 16).astype(np.int32)
+        q_h = f32_to_bf16_bits(rng.standard_normal(b.q.shape, dtype=np.float32))
+        nk_h = f32_to_bf16_bits(rng.standard_normal(b.new_k.shape, dtype=np.float32))
+        nv_h = f32_to_bf16_bits(rng.standard_normal(b.new_v.shape, dtype=np.float32))
+        q.copy_(dev(q_h)); new_k.copy_(dev(nk_h)); new_v.copy_(dev(nv_h))
+        slots.copy_(dev(slots_h)); lens.copy_(dev(L.astype(np.int32)))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        kp_h, vp_h = oracle.kv_write(kp_h, vp_h, nk_h, nv_h, slots_h)
+        ref = oracle.decode(q_h, kp_h, vp_h, b.block_tables, L, b.scale, "bf16")
+        print(f"[graph] replay {rep}: max L {int(L.max())}", flush=True)
+        assert_close(f64(out), ref, "bf16", f"replay {rep}")
+        assert np.array_equal(bits(k_pool), kp_h), f"replay {rep}: pool write"
+
+
+def test_large_batch_plan(pa):
+    """3000 short sequences: the plan keeps 2048 lengths in registers and
+    re-reads the rest; the longest-first result must equal the oracle and
+    small-batch (index order) decodes bit for bit."""
+    b = make_batch(72, name="many", dtype="bf16", num_q_heads=4, num_kv_heads=2, head_dim=64,
+                   draw_lens=lambda rng: rng.integers(1, 60, size=3000))
+    d_k, d_v = dev(b.k_pool), dev(b.v_pool)
+    pa.kv_write(dev(b.new_k), dev(b.new_v), dev(b.slot_mapping), d_k, d_v)
+    q, tables, lens = dev(b.q), dev(b.block_tables), dev(b.context_lens)
+    out = pa.decode(q, d_k, d_v, tables, lens, b.max_context_len, scale=b.scale)
+    torch.cuda.synchronize()
+    kp, vp = oracle.kv_write(b.k_pool, b.v_pool, b.new_k, b.new_v, b.slot_mapping)
+    ref = oracle.decode(b.q, kp, vp, b.block_tables, b.context_lens, b.scale, "bf16")
+    assert_close(f64(out), ref, "bf16", "3000 sequences")
+    full = bits(out)
+    for lo in (0, 1500, 2990):
+        idx = list(range(lo, lo + 10))
+        o = pa.decode(q[idx].contiguous(), d_k, d_v, tables[idx].contiguous(),
+                      lens[idx].contiguous(), b.max_context_len, scale=b.scale)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(o), full[idx])
