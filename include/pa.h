@@ -21,8 +21,11 @@
  * Conventions shared by every call
  * --------------------------------
  * - Every tensor pointer is DEVICE memory owned by the caller.  The library
- *   allocates nothing, keeps no handle between calls, and is reentrant.  Scratch
- *   memory is passed in as `workspace`, sized by the matching *_workspace_bytes.
+ *   allocates no device memory and is reentrant.  Scratch memory is passed in
+ *   as `workspace`, sized by the matching *_workspace_bytes.  The only state it
+ *   keeps is one auxiliary stream and two events per device, created by the
+ *   first pa_prefill_chunk call that mixes matrix-core chunks with decode rows
+ *   and kept for the life of the process (see pa_prefill_chunk).
  * - Every call validates its host arguments first.  On failure it returns a
  *   non-zero pa_status, enqueues nothing and leaves every output untouched.
  * - On success the work is enqueued on `stream` (a hipStream_t; NULL means the
@@ -115,7 +118,9 @@ int32_t pa_kv_write(const void* k, const void* v,
  *
  * pa_decode_partition_tokens returns the partition size the library uses for
  * these arguments (-1 = one pass).  pa_decode_workspace_bytes returns the
- * workspace pa_decode needs for the same arguments (0 when one pass).
+ * workspace pa_decode needs for the same arguments: the longest-first
+ * processing order (num_seqs int32, 256-byte aligned) when the batch is large
+ * enough to use one, then the split partials; 0 when neither is used.
  */
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                    int32_t max_context_len, int32_t partition_tokens);
@@ -158,8 +163,14 @@ int32_t pa_decode(const void* q, const void* k_pool, const void* v_pool,
  * Row i of a sequence with n rows and context length L sits at position
  * L-n+i and attends to keys 0 .. L-n+i (causal, aligned to the context end).
  * Chunks giving at least 16 (row, head) pairs per kv head run on the matrix
- * cores; the rest, and the decode rows, run on the vector path.
- * The workspace covers the vector path's split-context partials.
+ * cores; the rest, and the decode rows, run on the vector path.  When both
+ * kinds are present the matrix-core kernel runs on the library's auxiliary
+ * stream for the device, concurrently with the vector path on `stream`: it
+ * waits for the work enqueued on `stream` before the call, and work enqueued
+ * on `stream` after the call waits for it (event fork/join, which HIP graph
+ * capture records as well).
+ * The workspace covers the vector path's processing order and split-context
+ * partials.
  */
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_prefill_seqs,
                                   int32_t total_query_tokens, int32_t num_q_heads,

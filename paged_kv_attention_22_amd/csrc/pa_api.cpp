@@ -3,11 +3,50 @@
 // nothing reads device memory: sizes come in as host integers.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "pa_internal.hpp"
 
 using namespace pa;
 
 namespace {
+
+// Auxiliary stream of one device: pa_prefill_chunk runs the matrix-core chunk
+// kernel on it, concurrently with the decode rows on the caller's stream
+// (forked from and joined back into the caller's stream with the two events).
+// Created on first use, kept for the life of the process; the mutex makes the
+// record / wait / launch sequence atomic across host threads.
+struct AuxStream {
+    std::once_flag once;
+    std::mutex mu;
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr;
+    hipEvent_t join = nullptr;
+    bool ok = false;
+};
+constexpr int kMaxDevices = 64;
+AuxStream g_aux[kMaxDevices];
+
+AuxStream* aux_for(hipStream_t s) {
+    int dev = 0;
+    if (s != nullptr) {
+        if (hipStreamGetDevice(s, &dev) != hipSuccess) return nullptr;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    AuxStream& a = g_aux[dev];
+    std::call_once(a.once, [&] {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return;
+        a.ok = hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking) == hipSuccess &&
+               hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) == hipSuccess &&
+               hipEventCreateWithFlags(&a.join, hipEventDisableTiming) == hipSuccess;
+        if (cur != dev) (void)hipSetDevice(cur);
+    });
+    return a.ok ? &a : nullptr;
+}
 
 int elem_size(int32_t dtype) {
     if (dtype == PA_BF16) return 2;
@@ -310,8 +349,8 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
     const int32_t dpart = choose_partition(num_decode, pool.num_kv_heads, max_context_len, partition_tokens);
     if (int32_t st = prepare_rows(dec, num_decode, dpart, workspace, workspace_bytes)) return st;
 
+    ChunkArgs c = {};
     if (mfma) {
-        ChunkArgs c = {};
         c.q = q;
         c.query_start_loc = query_start_loc;
         c.num_seqs = num_prefill_seqs;
@@ -331,8 +370,27 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
         c.scale = scale;
         c.out = out;
         c.min_pairs = 16;
-        if (int32_t st = launch_chunks(c, s)) return st;
     }
+    // The chunks (matrix cores, LDS) and the decode rows (HBM) use different
+    // parts of the chip: with both present, the chunks run on the auxiliary
+    // stream while the vector path runs on the caller's stream.  They read the
+    // same pools and write disjoint rows of out; only the vector path uses the
+    // workspace.
+    AuxStream* ax = (mfma && num_decode > 0) ? aux_for(s) : nullptr;
+    if (ax != nullptr) {
+        std::lock_guard<std::mutex> lock(ax->mu);
+        if (hipEventRecord(ax->fork, s) != hipSuccess ||
+            hipStreamWaitEvent(ax->stream, ax->fork, 0) != hipSuccess)
+            return PA_ERR_LAUNCH;
+        if (int32_t st = launch_chunks(c, ax->stream)) return st;
+        if (hipEventRecord(ax->join, ax->stream) != hipSuccess) return PA_ERR_LAUNCH;
+        if (prefill_rows > 0)
+            if (int32_t st = run_rows(pre, s)) return st;
+        if (int32_t st = run_rows(dec, s)) return st;
+        return hipStreamWaitEvent(s, ax->join, 0) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+    }
+    if (mfma)
+        if (int32_t st = launch_chunks(c, s)) return st;
     if (prefill_rows > 0)
         if (int32_t st = run_rows(pre, s)) return st;
     if (num_decode > 0)

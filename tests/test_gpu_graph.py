@@ -93,3 +93,48 @@ def test_large_batch_plan(pa):
                       lens[idx].contiguous(), b.max_context_len, scale=b.scale)
         torch.cuda.synchronize()
         assert np.array_equal(bits(o), full[idx])
+
+
+def test_mixed_step_graph_replays(pa):
+    """A mixed step (KV write + pa_prefill_chunk, whose MFMA chunks run on the
+    library's auxiliary stream) captured in a graph: the fork/join is captured
+    too, and replays with new q values match the oracle."""
+    from workloads import mixed_prefill
+    b = mixed_prefill(seed=73, chunks=2, chunk_len=48, prior_hi=120, n_decode=20,
+                      dec_lo=20, dec_hi=400)
+    k_pool, v_pool = dev(b.k_pool), dev(b.v_pool)
+    q, new_k, new_v = dev(b.q), dev(b.new_k), dev(b.new_v)
+    slots, tables, lens, qsl = (dev(b.slot_mapping), dev(b.block_tables),
+                                dev(b.context_lens), dev(b.query_start_loc))
+    out = torch.empty_like(q)
+    nbytes = pa.prefill_workspace_bytes(b.num_seqs, b.num_prefill_seqs, b.total_query_tokens,
+                                        16, 8, 128, b.max_context_len)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        pa.kv_write(new_k, new_v, slots, k_pool, v_pool)
+        pa.prefill_chunk(q, qsl, b.num_prefill_seqs, b.max_query_len, k_pool, v_pool, tables,
+                         lens, b.max_context_len, scale=b.scale, out=out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    kp, vp = oracle.kv_write(b.k_pool, b.v_pool, b.new_k, b.new_v, b.slot_mapping)
+    rng = np.random.default_rng(9)
+    for rep in range(3):
+        q_h = f32_to_bf16_bits(rng.standard_normal(b.q.shape, dtype=np.float32))
+        q.copy_(dev(q_h))
+        out.fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = oracle.attention(q_h, b.query_start_loc, kp, vp, b.block_tables, b.context_lens,
+                               b.scale, "bf16")
+        print(f"[graph] mixed replay {rep}", flush=True)
+        assert_close(f64(out), ref, "bf16", f"mixed replay {rep}")
