@@ -35,6 +35,10 @@ def common_flags() -> list[str]:
     return ["-O3", "-fPIC", "-std=c++17", "-Wall", f"--offload-arch={ARCH}",
             # no packed-fp32 instructions in device code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in ordinary VGPRs: the softmax and rescaling
+            # touch them with vector instructions, and AGPR accumulators then
+            # cost a copy each way per tile
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-I", os.path.join(ROOT, "include")]
 
 

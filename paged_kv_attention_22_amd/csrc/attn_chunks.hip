@@ -13,7 +13,9 @@
 //                      lane l ends with row l%16's scores for keys
 //                      16*mt + 4*(l/16) + r, mt = 0..3, r = 0..3.
 //   online softmax     in that layout: max across the 4 lanes sharing a row,
-//                      the row sum kept per lane and added up at the end.
+//                      the row sum kept per lane and added up at the end;
+//                      the reference max moves only by more than 2^8 (lazy
+//                      rescaling).
 //   O^T += V^T * P^T   per 32 keys: B = the probabilities exactly as the S^T
 //                      step left them (contraction slot p < 4: key
 //                      4*(l/16)+p, p >= 4: key 16+4*(l/16)+p-4), A = V^T read
@@ -33,6 +35,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 constexpr float kNegInf = -__builtin_inff();
@@ -41,7 +45,6 @@ constexpr int kKeys = 64;   // keys per tile
 constexpr int kRowsPerWave = 16;
 constexpr int kWaves = 4;
 constexpr int kRowsPerGroup = kRowsPerWave * kWaves;
-constexpr int kMaxLdsBlocks = 512;  // block ids staged in LDS (8192 keys)
 
 __device__ __forceinline__ floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -60,12 +63,18 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
     constexpr int MT = D / 16;           // 16-dim tiles of the output (second product)
     constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
     constexpr int LOADS = kKeys * CPR / (kWaves * 64);  // chunks per thread per tile
-    constexpr int ROW = D * 2 + 16;      // LDS bytes per key row (padded)
-    constexpr int TILE = kKeys * ROW;
-    static_assert(LOADS >= 1, "tile loader");
-    __shared__ __align__(16) unsigned char lds_k[2 * TILE];
-    __shared__ __align__(16) unsigned char lds_v[2 * TILE];
-    __shared__ int lds_bt[kMaxLdsBlocks];
+    // LDS row strides: K rows are read 16 lanes x 16 bytes down a column, a
+    // 16-byte pad spreads those rows over the banks; V rows are read by the
+    // transposing loads as 4 rows x 32 bytes per 16 lanes, which a 32-byte pad
+    // keeps apart.
+    constexpr int KROW = D * 2 + 16;
+    constexpr int VROW = D * 2 + 32;
+    constexpr int KTILE = kKeys * KROW;
+    constexpr int VTILE = kKeys * VROW;
+    constexpr int KEYS_PER_WAVE_LOAD = 64 / CPR;  // keys one wave covers per load slot
+    static_assert(LOADS >= 1 && kBlock % KEYS_PER_WAVE_LOAD == 0, "tile loader");
+    __shared__ __align__(16) unsigned char lds_k[2 * KTILE];
+    __shared__ __align__(16) unsigned char lds_v[2 * VTILE];
 
     const int s = blockIdx.z, g = blockIdx.y;
     const int G = a.num_q_heads / a.num_kv_heads;
@@ -79,7 +88,8 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
     const int L = min(max(a.context_lens[s], 0), cap);
     const int prior = L - n;  // keys before the chunk
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform branches below
     const int li = lane & 15, kg = lane >> 4;
     const int R = row0 + wave * kRowsPerWave + li;  // this lane's row
     const bool row_ok = R < rows;
@@ -92,12 +102,13 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
     const int ntiles = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
     const int wrow0 = row0 + wave * kRowsPerWave;
     const int wkend = wrow0 < rows ? min(prior + (min(wrow0 + kRowsPerWave, rows) - 1) / G + 1, L) : 0;
+    const int wlim_min = prior + wrow0 / G;  // smallest last-visible key among the wave's rows
 
-    const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
-    const int nb = (kend + kBlock - 1) / kBlock;
-    const bool bt_lds = nb <= kMaxLdsBlocks;
-    if (bt_lds)
-        for (int i = tid; i < nb; i += kWaves * 64) lds_bt[i] = min(max(bt[i], 0), a.num_blocks - 1);
+    // The block table is read-only for the whole kernel: reading it through
+    // the constant address space makes the (wave-uniform) id loads scalar, so
+    // they do not queue behind the K/V loads.
+    typedef __attribute__((address_space(4))) const int32_t const_i32;
+    const const_i32* bt = (const const_i32*)(a.block_tables + (int64_t)s * a.max_blocks);
 
     const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
     const uint16_t* q = static_cast<const uint16_t*>(a.q);
@@ -106,21 +117,35 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
     for (int ks = 0; ks < KS; ++ks) {
         uint4 v = make_uint4(0, 0, 0, 0);
         if (row_ok) v = ld16(q + ((int64_t)(qs + t) * Hq + g * G + hh) * D + ks * 32 + kg * 8);
+        // An identity DPP move makes the q registers the result of a vector
+        // instruction: the tile loop then never waits on memory for them (its
+        // memory waits are for the tile prefetch only).
+        v.x = __builtin_amdgcn_update_dpp(v.x, v.x, 0xE4, 0xf, 0xf, false);
+        v.y = __builtin_amdgcn_update_dpp(v.y, v.y, 0xE4, 0xf, 0xf, false);
+        v.z = __builtin_amdgcn_update_dpp(v.z, v.z, 0xE4, 0xf, 0xf, false);
+        v.w = __builtin_amdgcn_update_dpp(v.w, v.w, 0xE4, 0xf, 0xf, false);
         qf[ks] = as_bf16x8(v);
     }
-    __syncthreads();  // lds_bt
 
     const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
     const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
     const int64_t tok_stride = (int64_t)Hkv * D;
 
     // Loader: thread tid moves chunks ci = tid + 256*u of a tile (key ci/CPR,
-    // 16-byte piece ci%CPR) from the pool into registers.  Only keys below
-    // kend are loaded (no row of this workgroup sees a later key, and their
-    // block ids are exactly the ones staged in LDS); the others become zeros,
-    // whatever their slots hold (NaN included).
+    // 16-byte piece ci%CPR) from the pool into registers.  For one u the 64
+    // lanes of a wave cover 64/CPR consecutive keys inside one block, so the
+    // block id is wave-uniform: one scalar load per (wave, u).  Only keys below
+    // kend are loaded (no row of this workgroup sees a later key); the others
+    // become zeros, whatever their slots hold (NaN included).
     uint4 kreg[LOADS], vreg[LOADS];
     auto load_tile = [&](int j0) {
+        int blk[LOADS];
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {  // scalar loads first, one wait for all
+            const int key0 = (wave * 64 + u * kWaves * 64) / CPR;  // wave-uniform
+            const int bi = min((j0 + key0) / kBlock, a.max_blocks - 1);
+            blk[u] = min(max(bt[bi], 0), a.num_blocks - 1);
+        }
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {
             const int ci = tid + u * kWaves * 64;
@@ -129,9 +154,7 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
             kreg[u] = make_uint4(0, 0, 0, 0);
             vreg[u] = make_uint4(0, 0, 0, 0);
             if (j < kend) {
-                const int bi = j / kBlock;  // < nb
-                const int blk = min(max(bt_lds ? lds_bt[bi] : bt[bi], 0), a.num_blocks - 1);
-                const int64_t off = ((int64_t)blk * kBlock + (j % kBlock)) * tok_stride + (int64_t)g * D + c * 8;
+                const int64_t off = ((int64_t)blk[u] * kBlock + (j % kBlock)) * tok_stride + (int64_t)g * D + c * 8;
                 kreg[u] = ld16(kpool + off);
                 vreg[u] = ld16(vpool + off);
             }
@@ -142,8 +165,8 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
         for (int u = 0; u < LOADS; ++u) {
             const int ci = tid + u * kWaves * 64;
             const int key = ci / CPR, c = ci % CPR;
-            *reinterpret_cast<uint4*>(lds_k + buf * TILE + key * ROW + c * 16) = kreg[u];
-            *reinterpret_cast<uint4*>(lds_v + buf * TILE + key * ROW + c * 16) = vreg[u];
+            *reinterpret_cast<uint4*>(lds_k + buf * KTILE + key * KROW + c * 16) = kreg[u];
+            *reinterpret_cast<uint4*>(lds_v + buf * VTILE + key * VROW + c * 16) = vreg[u];
         }
     };
 
@@ -163,59 +186,73 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
         const int j0 = it * kKeys;
         const int buf = it & 1;
         if (j0 < wkend) {
-            const unsigned char* kt = lds_k + buf * TILE;
-            const unsigned char* vt = lds_v + buf * TILE;
+            const unsigned char* kt = lds_k + buf * KTILE;
+            const unsigned char* vt = lds_v + buf * VTILE;
             floatx4 st[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const uint4 kv = *reinterpret_cast<const uint4*>(kt + (mt * 16 + li) * ROW + (ks * 32 + kg * 8) * 2);
+                    const uint4 kv = *reinterpret_cast<const uint4*>(kt + (mt * 16 + li) * KROW + (ks * 32 + kg * 8) * 2);
                     c = mfma(as_bf16x8(kv), qf[ks], c);
                 }
                 st[mt] = c;
             }
+            // Raw scores; only a tile that crosses some row's last visible key
+            // (wave-uniform test) needs the causal mask.
             float sc[16];
-            float mx = kNegInf;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = j0 + mt * 16 + kg * 4 + r;
-                    const float v = (j <= lim) ? st[mt][r] * sl2 : kNegInf;
-                    sc[mt * 4 + r] = v;
-                    mx = fmaxf(mx, v);
-                }
+                for (int r = 0; r < 4; ++r) sc[mt * 4 + r] = st[mt][r];
+            if (j0 + kKeys - 1 > wlim_min) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (j0 + mt * 16 + kg * 4 + r > lim) sc[mt * 4 + r] = kNegInf;
+            }
+            float mx = kNegInf;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[i]);
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mn = fmaxf(m, mx);
-            const float mref = (mn == kNegInf) ? 0.0f : mn;
-            const float alpha = fast_exp2(m - mref);
-            m = mn;
+            mx *= sl2;  // sl2 > 0: the max of the scaled scores
+            // Lazy rescaling: the reference max moves only when a score exceeds
+            // it by more than 2^8, so the accumulators (kept in the MFMA
+            // registers) are rescaled rarely; the exponentials stay below 256.
+            // The test is made wave-uniform so it stays a real branch.
+            const bool need = mx > m + 8.0f;
+            if (__builtin_amdgcn_ballot_w64(need) != 0) {
+                const float mn = need ? mx : m;
+                const float alpha = fast_exp2(m - mn);
+                lsum *= alpha;
+#pragma unroll
+                for (int i = 0; i < MT; ++i) acc[i] *= alpha;
+                m = mn;
+            }
+            const float nmref = (m == kNegInf) ? 0.0f : -m;
             uint32_t pk[8];
             float psum = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const __bf16 lo = static_cast<__bf16>(fast_exp2(sc[2 * i] - mref));
-                const __bf16 hi = static_cast<__bf16>(fast_exp2(sc[2 * i + 1] - mref));
-                psum += static_cast<float>(lo) + static_cast<float>(hi);
-                pk[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+                const float p0 = fast_exp2(fmaf(sc[2 * i], sl2, nmref));
+                const float p1 = fast_exp2(fmaf(sc[2 * i + 1], sl2, nmref));
+                psum += p0 + p1;
+                pk[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){p0, p1}, bf16x2v));
             }
-            lsum = lsum * alpha + psum;
-#pragma unroll
-            for (int i = 0; i < MT; ++i) acc[i] *= alpha;
+            lsum += psum;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 // keys 32*kk .. 32*kk+31: slots 0-3 from st[2kk], 4-7 from st[2kk+1]
                 const bf16x8 pb = as_bf16x8(make_uint4(pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]));
                 const int k4 = lane >> 2 & 3;  // key row within the lane's group of 4
-                const unsigned char* v0 = vt + (32 * kk + 4 * kg + k4) * ROW + (lane & 3) * 8;
+                const unsigned char* v0 = vt + (32 * kk + 4 * kg + k4) * VROW + (lane & 3) * 8;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     const uint2 lo = ld_tr(v0 + mt * 32);
-                    const uint2 hi = ld_tr(v0 + 16 * ROW + mt * 32);
+                    const uint2 hi = ld_tr(v0 + 16 * VROW + mt * 32);
                     acc[mt] = mfma(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, acc[mt]);
                 }
             }

@@ -421,7 +421,8 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a
     constexpr int MT = D / 16;                // 16-dim output tiles (second product)
     constexpr int CPR = D / 8;                // 16-byte chunks per token row
     constexpr int VL = 32 * CPR / 64;         // V chunks per lane per step
-    constexpr int VROW = D * 2 + 16;          // LDS bytes per V row (padded)
+    constexpr int VROW = D * 2 + 32;          // LDS bytes per V row (padded: the
+                                              // transposing reads take 4 rows x 32 B)
     constexpr int VT = 32 * VROW;             // one wave's V tile
     constexpr float kLazy = 8.0f;
     static_assert(G <= 16, "group fits the 16 columns of one MFMA tile");
