@@ -2,8 +2,9 @@
 //
 // A chunk of n new query tokens of a sequence with context length L holds
 // rows (token t, head hh) of the kv head's GQA group, n*G rows in all; row
-// (t, hh) sees keys 0 .. L-n+t.  One workgroup of 4 waves owns 64 rows of one
-// (sequence, kv head); each wave owns 16.  Keys arrive in tiles of 64 (four
+// (t, hh) sees keys 0 .. L-n+t.  One workgroup of 4 waves owns 128 rows of
+// one (sequence, kv head); each wave owns two tiles of 16 rows, so every K and
+// V fragment it reads from LDS feeds two MFMAs.  Keys arrive in tiles of 64 (four
 // 16-token blocks, gathered through the block table into LDS, K and V both
 // row-major); the tile is shared by all four waves.
 //
@@ -42,9 +43,12 @@ typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kKeys = 64;   // keys per tile
-constexpr int kRowsPerWave = 16;
 constexpr int kWaves = 4;
-constexpr int kRowsPerGroup = kRowsPerWave * kWaves;
+// Shape of the launch: 16-row tiles per wave (register blocking) and tiles of
+// keys in flight from memory (register buffers) while one is computed.
+constexpr int kNT = 2;
+constexpr int kDepth = 1;
+constexpr int kRowsPerGroup = 16 * kNT * kWaves;
 
 __device__ __forceinline__ floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -57,8 +61,11 @@ __device__ __forceinline__ uint2 ld_tr(const unsigned char* p) {
     return __builtin_bit_cast(uint2, v);
 }
 
-template <int D>
+template <int D, int NT, int DEPTH>
 __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
+    constexpr int kNT = NT;
+    constexpr int kRowsPerWave = 16 * NT;
+    constexpr int kRowsPerGroup = kRowsPerWave * kWaves;
     constexpr int KS = D / 32;           // 32-wide slices of head_dim (first product)
     constexpr int MT = D / 16;           // 16-dim tiles of the output (second product)
     constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
@@ -91,16 +98,23 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform branches below
     const int li = lane & 15, kg = lane >> 4;
-    const int R = row0 + wave * kRowsPerWave + li;  // this lane's row
-    const bool row_ok = R < rows;
-    const int t = R / G, hh = R - t * G;
-    const int lim = prior + t;  // last visible key of the row
+    const int wrow0 = row0 + wave * kRowsPerWave;
+    // This lane's rows: wrow0 + 16*nt + li, nt = 0..kNT-1.
+    bool row_ok[kNT];
+    int trow[kNT], hh[kNT], lim[kNT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+        const int R = wrow0 + nt * 16 + li;
+        row_ok[nt] = R < rows;
+        trow[nt] = R / G;
+        hh[nt] = R - trow[nt] * G;
+        lim[nt] = prior + trow[nt];  // last visible key of the row
+    }
 
     // Keys this workgroup / this wave needs.
     const int last_row = min(row0 + kRowsPerGroup, rows) - 1;
     const int kend = min(prior + last_row / G + 1, L);
     const int ntiles = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
-    const int wrow0 = row0 + wave * kRowsPerWave;
     const int wkend = wrow0 < rows ? min(prior + (min(wrow0 + kRowsPerWave, rows) - 1) / G + 1, L) : 0;
     const int wlim_min = prior + wrow0 / G;  // smallest last-visible key among the wave's rows
 
@@ -112,20 +126,22 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
 
     const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
     const uint16_t* q = static_cast<const uint16_t*>(a.q);
-    bf16x8 qf[KS];
+    bf16x8 qf[kNT][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row_ok) v = ld16(q + ((int64_t)(qs + t) * Hq + g * G + hh) * D + ks * 32 + kg * 8);
-        // An identity DPP move makes the q registers the result of a vector
-        // instruction: the tile loop then never waits on memory for them (its
-        // memory waits are for the tile prefetch only).
-        v.x = __builtin_amdgcn_update_dpp(v.x, v.x, 0xE4, 0xf, 0xf, false);
-        v.y = __builtin_amdgcn_update_dpp(v.y, v.y, 0xE4, 0xf, 0xf, false);
-        v.z = __builtin_amdgcn_update_dpp(v.z, v.z, 0xE4, 0xf, 0xf, false);
-        v.w = __builtin_amdgcn_update_dpp(v.w, v.w, 0xE4, 0xf, 0xf, false);
-        qf[ks] = as_bf16x8(v);
-    }
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (row_ok[nt]) v = ld16(q + ((int64_t)(qs + trow[nt]) * Hq + g * G + hh[nt]) * D + ks * 32 + kg * 8);
+            // An identity DPP move makes the q registers the result of a vector
+            // instruction: the tile loop then never waits on memory for them
+            // (its memory waits are for the tile prefetch only).
+            v.x = __builtin_amdgcn_update_dpp(v.x, v.x, 0xE4, 0xf, 0xf, false);
+            v.y = __builtin_amdgcn_update_dpp(v.y, v.y, 0xE4, 0xf, 0xf, false);
+            v.z = __builtin_amdgcn_update_dpp(v.z, v.z, 0xE4, 0xf, 0xf, false);
+            v.w = __builtin_amdgcn_update_dpp(v.w, v.w, 0xE4, 0xf, 0xf, false);
+            qf[nt][ks] = as_bf16x8(v);
+        }
 
     const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
     const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
@@ -137,8 +153,8 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
     // block id is wave-uniform: one scalar load per (wave, u).  Only keys below
     // kend are loaded (no row of this workgroup sees a later key); the others
     // become zeros, whatever their slots hold (NaN included).
-    uint4 kreg[LOADS], vreg[LOADS];
-    auto load_tile = [&](int j0) {
+    uint4 kreg[DEPTH][LOADS], vreg[DEPTH][LOADS];
+    auto load_tile = [&](int j0, uint4 (&kr)[LOADS], uint4 (&vr)[LOADS]) {
         int blk[LOADS];
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {  // scalar loads first, one wait for all
@@ -151,127 +167,175 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
             const int ci = tid + u * kWaves * 64;
             const int key = ci / CPR, c = ci % CPR;
             const int j = j0 + key;
-            kreg[u] = make_uint4(0, 0, 0, 0);
-            vreg[u] = make_uint4(0, 0, 0, 0);
+            kr[u] = make_uint4(0, 0, 0, 0);
+            vr[u] = make_uint4(0, 0, 0, 0);
             if (j < kend) {
                 const int64_t off = ((int64_t)blk[u] * kBlock + (j % kBlock)) * tok_stride + (int64_t)g * D + c * 8;
-                kreg[u] = ld16(kpool + off);
-                vreg[u] = ld16(vpool + off);
+                kr[u] = ld16(kpool + off);
+                vr[u] = ld16(vpool + off);
             }
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf, const uint4 (&kr)[LOADS], const uint4 (&vr)[LOADS]) {
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {
             const int ci = tid + u * kWaves * 64;
             const int key = ci / CPR, c = ci % CPR;
-            *reinterpret_cast<uint4*>(lds_k + buf * KTILE + key * KROW + c * 16) = kreg[u];
-            *reinterpret_cast<uint4*>(lds_v + buf * VTILE + key * VROW + c * 16) = vreg[u];
+            *reinterpret_cast<uint4*>(lds_k + buf * KTILE + key * KROW + c * 16) = kr[u];
+            *reinterpret_cast<uint4*>(lds_v + buf * VTILE + key * VROW + c * 16) = vr[u];
         }
     };
 
     const float sl2 = a.scale * kLog2e;
-    float m = kNegInf, lsum = 0.0f;
-    floatx4 acc[MT];
+    float m[kNT], lsum[kNT];
+    floatx4 acc[kNT][MT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) acc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    if (ntiles > 0) {
-        load_tile(0);
-        store_tile(0);
+    for (int nt = 0; nt < kNT; ++nt) {
+        m[nt] = kNegInf;
+        lsum[nt] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[nt][i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    if (ntiles > 1) load_tile(kKeys);
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-        const int j0 = it * kKeys;
-        const int buf = it & 1;
+
+    // One tile of math on LDS buffer `buf` (keys j0 .. j0+63).
+    auto compute_tile = [&](int j0, int buf) {
         if (j0 < wkend) {
             const unsigned char* kt = lds_k + buf * KTILE;
             const unsigned char* vt = lds_v + buf * VTILE;
-            floatx4 st[4];
+            // S^T for keys j0 .. j0+63; each K fragment feeds both row tiles.
+            floatx4 st[kNT][4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt) st[nt][mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const uint4 kv = *reinterpret_cast<const uint4*>(kt + (mt * 16 + li) * KROW + (ks * 32 + kg * 8) * 2);
-                    c = mfma(as_bf16x8(kv), qf[ks], c);
+                    const bf16x8 kv = as_bf16x8(*reinterpret_cast<const uint4*>(
+                        kt + (mt * 16 + li) * KROW + (ks * 32 + kg * 8) * 2));
+#pragma unroll
+                    for (int nt = 0; nt < kNT; ++nt) st[nt][mt] = mfma(kv, qf[nt][ks], st[nt][mt]);
                 }
-                st[mt] = c;
             }
-            // Raw scores; only a tile that crosses some row's last visible key
-            // (wave-uniform test) needs the causal mask.
-            float sc[16];
+            // Only a tile that crosses some row's last visible key (a
+            // wave-uniform test) needs the causal mask.
+            const bool masked = j0 + kKeys - 1 > wlim_min;
+            float sc[kNT][16], mx[kNT];
+            bool need_any = false;
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sc[mt * 4 + r] = st[mt][r];
-            if (j0 + kKeys - 1 > wlim_min) {
+            for (int nt = 0; nt < kNT; ++nt) {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (j0 + mt * 16 + kg * 4 + r > lim) sc[mt * 4 + r] = kNegInf;
-            }
-            float mx = kNegInf;
+                    for (int r = 0; r < 4; ++r) sc[nt][mt * 4 + r] = st[nt][mt][r];
+                if (masked) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            mx *= sl2;  // sl2 > 0: the max of the scaled scores
+                    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (j0 + mt * 16 + kg * 4 + r > lim[nt]) sc[nt][mt * 4 + r] = kNegInf;
+                }
+                float x = kNegInf;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) x = fmaxf(x, sc[nt][i]);
+                x = fmaxf(x, __shfl_xor(x, 16));
+                x = fmaxf(x, __shfl_xor(x, 32));
+                mx[nt] = x * sl2;  // sl2 > 0: the max of the scaled scores
+                need_any |= mx[nt] > m[nt] + 8.0f;
+            }
             // Lazy rescaling: the reference max moves only when a score exceeds
-            // it by more than 2^8, so the accumulators (kept in the MFMA
-            // registers) are rescaled rarely; the exponentials stay below 256.
-            // The test is made wave-uniform so it stays a real branch.
-            const bool need = mx > m + 8.0f;
-            if (__builtin_amdgcn_ballot_w64(need) != 0) {
-                const float mn = need ? mx : m;
-                const float alpha = fast_exp2(m - mn);
-                lsum *= alpha;
+            // it by more than 2^8, so the accumulators are rescaled rarely and
+            // the exponentials stay below 256.  The test is made wave-uniform
+            // so it stays a real branch.
+            if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
 #pragma unroll
-                for (int i = 0; i < MT; ++i) acc[i] *= alpha;
-                m = mn;
-            }
-            const float nmref = (m == kNegInf) ? 0.0f : -m;
-            uint32_t pk[8];
-            float psum = 0.0f;
+                for (int nt = 0; nt < kNT; ++nt) {
+                    const float mn = mx[nt] > m[nt] + 8.0f ? mx[nt] : m[nt];
+                    const float alpha = fast_exp2(m[nt] - mn);
+                    lsum[nt] *= alpha;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float p0 = fast_exp2(fmaf(sc[2 * i], sl2, nmref));
-                const float p1 = fast_exp2(fmaf(sc[2 * i + 1], sl2, nmref));
-                psum += p0 + p1;
-                pk[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){p0, p1}, bf16x2v));
+                    for (int i = 0; i < MT; ++i) acc[nt][i] *= alpha;
+                    m[nt] = mn;
+                }
             }
-            lsum += psum;
+            uint32_t pk[kNT][8];
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                const float nmref = (m[nt] == kNegInf) ? 0.0f : -m[nt];
+                float psum = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float p0 = fast_exp2(fmaf(sc[nt][2 * i], sl2, nmref));
+                    const float p1 = fast_exp2(fmaf(sc[nt][2 * i + 1], sl2, nmref));
+                    psum += p0 + p1;
+                    pk[nt][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){p0, p1}, bf16x2v));
+                }
+                lsum[nt] += psum;
+            }
+            // O^T += V^T P^T; each V^T fragment feeds both row tiles.
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                // keys 32*kk .. 32*kk+31: slots 0-3 from st[2kk], 4-7 from st[2kk+1]
-                const bf16x8 pb = as_bf16x8(make_uint4(pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]));
+                // keys 32*kk .. 32*kk+31: slots 0-3 from st[.][2kk], 4-7 from st[.][2kk+1]
+                bf16x8 pb[kNT];
+#pragma unroll
+                for (int nt = 0; nt < kNT; ++nt)
+                    pb[nt] = as_bf16x8(make_uint4(pk[nt][4 * kk], pk[nt][4 * kk + 1], pk[nt][4 * kk + 2], pk[nt][4 * kk + 3]));
                 const int k4 = lane >> 2 & 3;  // key row within the lane's group of 4
                 const unsigned char* v0 = vt + (32 * kk + 4 * kg + k4) * VROW + (lane & 3) * 8;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     const uint2 lo = ld_tr(v0 + mt * 32);
                     const uint2 hi = ld_tr(v0 + 16 * VROW + mt * 32);
-                    acc[mt] = mfma(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, acc[mt]);
+                    const bf16x8 va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+                    for (int nt = 0; nt < kNT; ++nt) acc[nt][mt] = mfma(va, pb[nt], acc[nt][mt]);
                 }
             }
         }
-        if (it + 1 < ntiles) store_tile(buf ^ 1);
-        if (it + 2 < ntiles) load_tile(j0 + 2 * kKeys);
-        __syncthreads();
+    };
+
+    // Pipeline: LDS holds the tile being computed and the next one; DEPTH
+    // register buffers hold the tiles after that, loading from memory.  The
+    // tile loaded at iteration it is stored to LDS at iteration it+DEPTH.
+#pragma unroll
+    for (int d = 0; d <= DEPTH; ++d) {  // unrolled: static register buffers
+        if (d < ntiles) {
+            if (d == 0) {
+                load_tile(0, kreg[0], vreg[0]);
+                store_tile(0, kreg[0], vreg[0]);
+            } else {
+                load_tile(d * kKeys, kreg[(d - 1) % DEPTH], vreg[(d - 1) % DEPTH]);
+            }
+        }
+    }
+    __syncthreads();
+    for (int it0 = 0; it0 < ntiles; it0 += DEPTH) {
+#pragma unroll
+        for (int r = 0; r < DEPTH; ++r) {  // unrolled: static register buffers
+            const int it = it0 + r;
+            if (it < ntiles) {
+                const int j0 = it * kKeys;
+                compute_tile(j0, it & 1);
+                if (it + 1 < ntiles) store_tile((it + 1) & 1, kreg[r], vreg[r]);
+                if (it + 1 + DEPTH < ntiles) load_tile((it + 1 + DEPTH) * kKeys, kreg[r], vreg[r]);
+                __syncthreads();
+            }
+        }
     }
 
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    if (!row_ok) return;
-    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-    uint16_t* out = static_cast<uint16_t*>(a.out) + ((int64_t)(qs + t) * Hq + g * G + hh) * D + kg * 4;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const uint2 o = make_uint2(pack_bf16x2(acc[mt][0] * inv, acc[mt][1] * inv),
-                                   pack_bf16x2(acc[mt][2] * inv, acc[mt][3] * inv));
-        *reinterpret_cast<uint2*>(out + mt * 16) = o;
+    for (int nt = 0; nt < kNT; ++nt) {
+        float l = lsum[nt];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (!row_ok[nt]) continue;
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        uint16_t* out = static_cast<uint16_t*>(a.out) + ((int64_t)(qs + trow[nt]) * Hq + g * G + hh[nt]) * D + kg * 4;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const uint2 o = make_uint2(pack_bf16x2(acc[nt][mt][0] * inv, acc[nt][mt][1] * inv),
+                                       pack_bf16x2(acc[nt][mt][2] * inv, acc[nt][mt][3] * inv));
+            *reinterpret_cast<uint2*>(out + mt * 16) = o;
+        }
     }
 }
 
@@ -290,9 +354,9 @@ int32_t launch_chunks(const ChunkArgs& a, hipStream_t stream) {
     if (tiles > INT32_MAX || a.num_seqs > 65535) return PA_ERR_SHAPE;
     dim3 grid((unsigned)tiles, a.num_kv_heads, a.num_seqs);
     if (a.head_dim == 128)
-        hipLaunchKernelGGL(chunk_kernel<128>, grid, dim3(kWaves * 64), 0, stream, a);
+        hipLaunchKernelGGL((chunk_kernel<128, kNT, kDepth>), grid, dim3(kWaves * 64), 0, stream, a);
     else
-        hipLaunchKernelGGL(chunk_kernel<64>, grid, dim3(kWaves * 64), 0, stream, a);
+        hipLaunchKernelGGL((chunk_kernel<64, kNT, kDepth>), grid, dim3(kWaves * 64), 0, stream, a);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
