@@ -61,6 +61,19 @@ __device__ __forceinline__ uint2 ld_tr(const unsigned char* p) {
     return __builtin_bit_cast(uint2, v);
 }
 
+// Max over the four lanes l, l^16, l^32, l^48 (the lanes holding one row's
+// scores): the gfx950 swaps exchange the upper 32 lanes of one operand with the
+// lower 32 of the other (and odd 16-lane rows with even ones), so with both
+// operands equal to x the two results are x and its partner lanes; no LDS trip.
+__device__ __forceinline__ float max_across_row_lanes(float x) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, x);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    x = fmaxf(__builtin_bit_cast(float, s32[0]), __builtin_bit_cast(float, s32[1]));
+    const uint32_t c = __builtin_bit_cast(uint32_t, x);
+    const auto s16 = __builtin_amdgcn_permlane16_swap(c, c, false, false);
+    return fmaxf(__builtin_bit_cast(float, s16[0]), __builtin_bit_cast(float, s16[1]));
+}
+
 template <int D, int NT, int DEPTH>
 __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
     constexpr int kNT = NT;
@@ -126,23 +139,18 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
 
     const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
     const uint16_t* q = static_cast<const uint16_t*>(a.q);
+    // q rows: every lane loads (rows past the chunk read its last row and are
+    // zeroed after), so the loads are issued together and waited for once.
+    uint4 qraw[kNT][KS];
     bf16x8 qf[kNT][KS];
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
+    for (int nt = 0; nt < kNT; ++nt) {
+        const int R = min(wrow0 + nt * 16 + li, rows - 1);
+        const int t = R / G, h = R - t * G;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (row_ok[nt]) v = ld16(q + ((int64_t)(qs + trow[nt]) * Hq + g * G + hh[nt]) * D + ks * 32 + kg * 8);
-            // An identity DPP move makes the q registers the result of a vector
-            // instruction: the tile loop then never waits on memory for them
-            // (its memory waits are for the tile prefetch only).
-            v.x = __builtin_amdgcn_update_dpp(v.x, v.x, 0xE4, 0xf, 0xf, false);
-            v.y = __builtin_amdgcn_update_dpp(v.y, v.y, 0xE4, 0xf, 0xf, false);
-            v.z = __builtin_amdgcn_update_dpp(v.z, v.z, 0xE4, 0xf, 0xf, false);
-            v.w = __builtin_amdgcn_update_dpp(v.w, v.w, 0xE4, 0xf, 0xf, false);
-            qf[nt][ks] = as_bf16x8(v);
-        }
-
+        for (int ks = 0; ks < KS; ++ks)
+            qraw[nt][ks] = ld16(q + ((int64_t)(qs + t) * Hq + g * G + h) * D + ks * 32 + kg * 8);
+    }
     const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
     const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
     const int64_t tok_stride = (int64_t)Hkv * D;
@@ -150,11 +158,17 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
     // Loader: thread tid moves chunks ci = tid + 256*u of a tile (key ci/CPR,
     // 16-byte piece ci%CPR) from the pool into registers.  For one u the 64
     // lanes of a wave cover 64/CPR consecutive keys inside one block, so the
-    // block id is wave-uniform: one scalar load per (wave, u).  Only keys below
-    // kend are loaded (no row of this workgroup sees a later key); the others
-    // become zeros, whatever their slots hold (NaN included).
+    // block id is wave-uniform: one scalar load per (wave, u).  Every lane
+    // loads, and every step loads a tile (past the last tile it reloads the
+    // last one; the clamped ids keep each address inside the pool): loads that
+    // are never skipped are counted exactly by the memory counter, so the wait
+    // before storing one register buffer leaves the later buffers in flight.
+    // Keys at or past kend (no row of this workgroup sees them) are masked out
+    // of the scores; their V rows, whatever the slots hold (NaN included), are
+    // stored as zeros so that a zero probability times them stays zero.
     uint4 kreg[DEPTH][LOADS], vreg[DEPTH][LOADS];
-    auto load_tile = [&](int j0, uint4 (&kr)[LOADS], uint4 (&vr)[LOADS]) {
+    auto load_tile = [&](int tile, uint4 (&kr)[LOADS], uint4 (&vr)[LOADS]) {
+        const int j0 = min(tile, ntiles - 1) * kKeys;
         int blk[LOADS];
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {  // scalar loads first, one wait for all
@@ -166,23 +180,20 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
         for (int u = 0; u < LOADS; ++u) {
             const int ci = tid + u * kWaves * 64;
             const int key = ci / CPR, c = ci % CPR;
-            const int j = j0 + key;
-            kr[u] = make_uint4(0, 0, 0, 0);
-            vr[u] = make_uint4(0, 0, 0, 0);
-            if (j < kend) {
-                const int64_t off = ((int64_t)blk[u] * kBlock + (j % kBlock)) * tok_stride + (int64_t)g * D + c * 8;
-                kr[u] = ld16(kpool + off);
-                vr[u] = ld16(vpool + off);
-            }
+            const int64_t off = ((int64_t)blk[u] * kBlock + ((j0 + key) % kBlock)) * tok_stride + (int64_t)g * D + c * 8;
+            kr[u] = ld16(kpool + off);
+            vr[u] = ld16(vpool + off);
         }
     };
-    auto store_tile = [&](int buf, const uint4 (&kr)[LOADS], const uint4 (&vr)[LOADS]) {
+    auto store_tile = [&](int buf, int j0, const uint4 (&kr)[LOADS], const uint4 (&vr)[LOADS]) {
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {
             const int ci = tid + u * kWaves * 64;
             const int key = ci / CPR, c = ci % CPR;
+            const uint32_t keep = 0u - (uint32_t)(j0 + key < kend);  // all ones or zero
+            const uint4 v = make_uint4(vr[u].x & keep, vr[u].y & keep, vr[u].z & keep, vr[u].w & keep);
             *reinterpret_cast<uint4*>(lds_k + buf * KTILE + key * KROW + c * 16) = kr[u];
-            *reinterpret_cast<uint4*>(lds_v + buf * VTILE + key * VROW + c * 16) = vr[u];
+            *reinterpret_cast<uint4*>(lds_v + buf * VTILE + key * VROW + c * 16) = v;
         }
     };
 
@@ -202,18 +213,40 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
         if (j0 < wkend) {
             const unsigned char* kt = lds_k + buf * KTILE;
             const unsigned char* vt = lds_v + buf * VTILE;
-            // S^T for keys j0 .. j0+63; each K fragment feeds both row tiles.
+            // S^T for keys j0 .. j0+63.  Every K fragment is read first and
+            // the products follow, so the LDS reads overlap one another
+            // instead of each waiting in front of its product; each fragment
+            // feeds the kNT row tiles.
+            uint4 kf[4][KS];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    kf[mt][ks] = *reinterpret_cast<const uint4*>(kt + (mt * 16 + li) * KROW + (ks * 32 + kg * 8) * 2);
+            __builtin_amdgcn_sched_barrier(0);
             floatx4 st[kNT][4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
+            for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-                for (int nt = 0; nt < kNT; ++nt) st[nt][mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+                for (int mt = 0; mt < 4; ++mt) st[nt][mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 kv = as_bf16x8(*reinterpret_cast<const uint4*>(
-                        kt + (mt * 16 + li) * KROW + (ks * 32 + kg * 8) * 2));
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                    for (int nt = 0; nt < kNT; ++nt) st[nt][mt] = mfma(kv, qf[nt][ks], st[nt][mt]);
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < kNT; ++nt) st[nt][mt] = mfma(as_bf16x8(kf[mt][ks]), qf[nt][ks], st[nt][mt]);
+            // The V^T fragments of the second product do not depend on the
+            // probabilities: reading them now overlaps the reads with the
+            // softmax.
+            const int k4 = lane >> 2 & 3;  // key row within the lane's group of 4
+            uint2 vlo[2][MT], vhi[2][MT];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const unsigned char* v0 = vt + (32 * kk + 4 * kg + k4) * VROW + (lane & 3) * 8;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    vlo[kk][mt] = ld_tr(v0 + mt * 32);
+                    vhi[kk][mt] = ld_tr(v0 + 16 * VROW + mt * 32);
                 }
             }
             // Only a tile that crosses some row's last visible key (a
@@ -237,8 +270,7 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
                 float x = kNegInf;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) x = fmaxf(x, sc[nt][i]);
-                x = fmaxf(x, __shfl_xor(x, 16));
-                x = fmaxf(x, __shfl_xor(x, 32));
+                x = max_across_row_lanes(x);
                 mx[nt] = x * sl2;  // sl2 > 0: the max of the scaled scores
                 need_any |= mx[nt] > m[nt] + 8.0f;
             }
@@ -279,13 +311,9 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt)
                     pb[nt] = as_bf16x8(make_uint4(pk[nt][4 * kk], pk[nt][4 * kk + 1], pk[nt][4 * kk + 2], pk[nt][4 * kk + 3]));
-                const int k4 = lane >> 2 & 3;  // key row within the lane's group of 4
-                const unsigned char* v0 = vt + (32 * kk + 4 * kg + k4) * VROW + (lane & 3) * 8;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    const uint2 lo = ld_tr(v0 + mt * 32);
-                    const uint2 hi = ld_tr(v0 + 16 * VROW + mt * 32);
-                    const bf16x8 va = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+                    const bf16x8 va = as_bf16x8(make_uint4(vlo[kk][mt].x, vlo[kk][mt].y, vhi[kk][mt].x, vhi[kk][mt].y));
 #pragma unroll
                     for (int nt = 0; nt < kNT; ++nt) acc[nt][mt] = mfma(va, pb[nt], acc[nt][mt]);
                 }
@@ -295,28 +323,41 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
 
     // Pipeline: LDS holds the tile being computed and the next one; DEPTH
     // register buffers hold the tiles after that, loading from memory.  The
-    // tile loaded at iteration it is stored to LDS at iteration it+DEPTH.
+    // tile loaded at step it is stored to LDS at step it+DEPTH.  The step count
+    // is rounded up to a multiple of DEPTH so the unrolled body runs whole:
+    // steps past the last tile compute nothing and store unused buffers.
+    if (ntiles > 0) {  // ntiles == 0 only for a sequence with no visible keys
+        uint4 tile0k[LOADS], tile0v[LOADS];
+        load_tile(0, tile0k, tile0v);
 #pragma unroll
-    for (int d = 0; d <= DEPTH; ++d) {  // unrolled: static register buffers
-        if (d < ntiles) {
-            if (d == 0) {
-                load_tile(0, kreg[0], vreg[0]);
-                store_tile(0, kreg[0], vreg[0]);
-            } else {
-                load_tile(d * kKeys, kreg[(d - 1) % DEPTH], vreg[(d - 1) % DEPTH]);
+        for (int d = 0; d < DEPTH; ++d) load_tile(d + 1, kreg[d], vreg[d]);
+        // An identity DPP move makes the q registers the result of a vector
+        // instruction: the tile loop then never waits on memory for them (its
+        // memory waits are for the tile prefetch only).
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            const uint32_t keep = 0u - (uint32_t)row_ok[nt];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                uint4 v = qraw[nt][ks];
+                v.x = __builtin_amdgcn_update_dpp(0u, v.x & keep, 0xE4, 0xf, 0xf, false);
+                v.y = __builtin_amdgcn_update_dpp(0u, v.y & keep, 0xE4, 0xf, 0xf, false);
+                v.z = __builtin_amdgcn_update_dpp(0u, v.z & keep, 0xE4, 0xf, 0xf, false);
+                v.w = __builtin_amdgcn_update_dpp(0u, v.w & keep, 0xE4, 0xf, 0xf, false);
+                qf[nt][ks] = as_bf16x8(v);
             }
         }
-    }
-    __syncthreads();
-    for (int it0 = 0; it0 < ntiles; it0 += DEPTH) {
+        store_tile(0, 0, tile0k, tile0v);
+        __syncthreads();
+        const int nsteps = (ntiles + DEPTH - 1) / DEPTH * DEPTH;
+        for (int it0 = 0; it0 < nsteps; it0 += DEPTH) {
 #pragma unroll
-        for (int r = 0; r < DEPTH; ++r) {  // unrolled: static register buffers
-            const int it = it0 + r;
-            if (it < ntiles) {
+            for (int r = 0; r < DEPTH; ++r) {  // unrolled: static register buffers
+                const int it = it0 + r;
                 const int j0 = it * kKeys;
                 compute_tile(j0, it & 1);
-                if (it + 1 < ntiles) store_tile((it + 1) & 1, kreg[r], vreg[r]);
-                if (it + 1 + DEPTH < ntiles) load_tile((it + 1 + DEPTH) * kKeys, kreg[r], vreg[r]);
+                store_tile((it + 1) & 1, j0 + kKeys, kreg[r], vreg[r]);
+                load_tile(it + 1 + DEPTH, kreg[r], vreg[r]);
                 __syncthreads();
             }
         }

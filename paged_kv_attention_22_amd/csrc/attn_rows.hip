@@ -120,8 +120,17 @@ __device__ __forceinline__ Item locate(const RowsArgs& a, int z, int group) {
         it.i = 0;
         return it;
     }
-    const int row = a.row_begin + z;
     const int32_t* qsl = a.query_start_loc;
+    if (a.small_rows > 0) {
+        it.seq = a.seq_begin + z / a.small_rows;
+        it.i = z % a.small_rows;
+        const int q0 = qsl[it.seq];
+        it.n = qsl[it.seq + 1] - q0;
+        it.row = q0 + it.i;
+        it.skip = it.i >= it.n || it.n * group >= a.mfma_min_pairs;
+        return it;
+    }
+    const int row = a.row_begin + z;
     int lo = a.seq_begin, hi = a.seq_end - 1;  // last s with qsl[s] <= row
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;

@@ -102,6 +102,12 @@ size_t split_bytes(int64_t items, int32_t num_q_heads, int32_t head_dim,
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// A prefill chunk goes to the matrix cores when it gives at least one 16-row
+// tile of (row, head) pairs per kv head; smaller chunks stay on the vector
+// path, and have at most small_rows_for(group) rows.
+constexpr int32_t kMfmaMinPairs = 16;
+int32_t small_rows_for(int32_t group) { return group >= 1 ? (kMfmaMinPairs - 1) / group : 0; }
+
 // Longest-first processing order for decode rows: with a ragged batch the
 // workgroups of the longest sequences start first and the short ones fill the
 // end, instead of a long sequence starting last and running alone.  Worth its
@@ -278,8 +284,15 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_prefill_seqs,
     const int64_t prefill_rows = (int64_t)total_query_tokens - num_decode;
     size_t need = 0;
     if (prefill_rows > 0) {
-        const int32_t part = choose_partition(prefill_rows, num_kv_heads, max_context_len, partition_tokens);
-        need = rows_bytes(prefill_rows, num_q_heads, num_kv_heads, head_dim, max_context_len, part, false);
+        // The vector path covers either every prefill row or, when the matrix
+        // cores take the large chunks, a few row slots per prefill sequence;
+        // the element type decides which, so size for both.
+        const int64_t slots = (int64_t)num_prefill_seqs * small_rows_for(num_q_heads / num_kv_heads);
+        for (const int64_t items : {prefill_rows, slots}) {
+            const int32_t part = choose_partition(items, num_kv_heads, max_context_len, partition_tokens);
+            const size_t p = rows_bytes(items, num_q_heads, num_kv_heads, head_dim, max_context_len, part, false);
+            if (p > need) need = p;
+        }
     }
     if (num_decode > 0) {
         const int32_t part = choose_partition(num_decode, num_kv_heads, max_context_len, partition_tokens);
@@ -338,9 +351,12 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
     pre.seq_end = num_prefill_seqs;
     pre.row_begin = 0;
     const bool mfma = prefill_rows > 0 && chunks_supported(pool.dtype, pool.head_dim, group);
-    pre.mfma_min_pairs = mfma ? 16 : 0;
-    const int32_t ppart = choose_partition(prefill_rows, pool.num_kv_heads, max_context_len, partition_tokens);
-    if (int32_t st = prepare_rows(pre, prefill_rows, ppart, workspace, workspace_bytes)) return st;
+    pre.mfma_min_pairs = mfma ? kMfmaMinPairs : 0;
+    pre.small_rows = mfma ? small_rows_for(group) : 0;
+    const int64_t pre_items = mfma ? (int64_t)num_prefill_seqs * pre.small_rows : prefill_rows;
+    if (pre_items > INT32_MAX) return PA_ERR_SHAPE;
+    const int32_t ppart = choose_partition(pre_items, pool.num_kv_heads, max_context_len, partition_tokens);
+    if (int32_t st = prepare_rows(pre, pre_items, ppart, workspace, workspace_bytes)) return st;
     dec.query_start_loc = nullptr;
     dec.seq_begin = num_prefill_seqs;
     dec.seq_end = num_seqs;
@@ -369,7 +385,7 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
         c.total_rows = total_query_tokens;
         c.scale = scale;
         c.out = out;
-        c.min_pairs = 16;
+        c.min_pairs = kMfmaMinPairs;
     }
     // The chunks (matrix cores, LDS) and the decode rows (HBM) use different
     // parts of the chip: with both present, the chunks run on the auxiliary
@@ -384,15 +400,13 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
             return PA_ERR_LAUNCH;
         if (int32_t st = launch_chunks(c, ax->stream)) return st;
         if (hipEventRecord(ax->join, ax->stream) != hipSuccess) return PA_ERR_LAUNCH;
-        if (prefill_rows > 0)
-            if (int32_t st = run_rows(pre, s)) return st;
+        if (int32_t st = run_rows(pre, s)) return st;
         if (int32_t st = run_rows(dec, s)) return st;
         return hipStreamWaitEvent(s, ax->join, 0) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
     }
     if (mfma)
         if (int32_t st = launch_chunks(c, s)) return st;
-    if (prefill_rows > 0)
-        if (int32_t st = run_rows(pre, s)) return st;
+    if (int32_t st = run_rows(pre, s)) return st;
     if (num_decode > 0)
         if (int32_t st = run_rows(dec, s)) return st;
     return PA_OK;

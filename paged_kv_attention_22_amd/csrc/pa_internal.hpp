@@ -34,6 +34,12 @@ struct RowsArgs {
     // (row, head) pairs per kv head are left to the matrix-core kernel
     // (0 = handle every item here).
     int32_t mfma_min_pairs;
+    // With query_start_loc and small_rows > 0: item z is row z % small_rows of
+    // sequence seq_begin + z / small_rows (a slot past the sequence's rows, or
+    // of a sequence left to the matrix cores, does nothing).  small_rows is the
+    // most rows a sequence below mfma_min_pairs can have, so the launch covers
+    // only the chunks that stay on the vector path, not every prefill row.
+    int32_t small_rows;
     int32_t num_q_heads, num_kv_heads, head_dim, num_blocks, dtype;
     int32_t max_context_len;
     float scale;

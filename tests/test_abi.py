@@ -121,3 +121,16 @@ def test_partition_choice_and_workspace(pa):
     assert pa.decode_workspace_bytes(256, 16, 8, 128, 2048, 256) == 1024 + 256 * 16 * n * 130 * 4
     assert pa.decode_workspace_bytes(256, 16, 8, 128, 2048, -1) == 1024
     assert pa.decode_workspace_bytes(4, 2, 1, 64, 64, -1) == 0     # small batch: nothing
+
+
+def test_prefill_workspace_covers_both_vector_path_layouts(pa):
+    """With matrix-core chunks the vector path covers (Hq/Hkv = 2) 7 row slots
+    per prefill sequence instead of every prefill row; the workspace size holds
+    whichever of the two needs more.  Four one-row chunks, no decode rows, 2048
+    context: 4 rows x 8 kv heads split into 64-token parts (32 parts) against
+    28 slots x 8 kv heads split into 256-token parts (8 parts)."""
+    rows = 4 * 16 * 32 * 130 * 4
+    slots = 28 * 16 * 8 * 130 * 4
+    assert pa.prefill_workspace_bytes(4, 4, 4, 16, 8, 128, 2048, 0) == max(rows, slots)
+    # one pass requested: no partials, and no longest-first order for chunk rows
+    assert pa.prefill_workspace_bytes(4, 4, 4, 16, 8, 128, 2048, -1) == 0

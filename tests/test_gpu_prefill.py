@@ -30,6 +30,10 @@ WORKLOADS = {
                                                   n_decode=2, dec_lo=1, dec_hi=50),
     "prefill_only_p0": lambda: mixed_prefill(chunks=2, chunk_len=70, prior_hi=0, n_decode=0),
     "mixed_full": mixed_prefill,
+    # chunks on both paths in one batch: 3, 7 and 1 rows give fewer than 16
+    # (row, head) pairs per kv head at G = 2 (vector path), 40 and 64 do not
+    "mixed_ragged_chunks": lambda: mixed_prefill(seed=8, chunk_lens=[3, 40, 7, 1, 64], prior_hi=300,
+                                                 n_decode=6, dec_lo=1, dec_hi=400),
     # a group of 7 (decode rows on the matrix-core decode path, chunks on MFMA)
     "mixed_g7": lambda: mixed_prefill(seed=7, chunks=2, chunk_len=33, prior_hi=200, n_decode=9,
                                       dec_lo=1, dec_hi=500, num_q_heads=28, num_kv_heads=4),

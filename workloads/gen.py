@@ -271,23 +271,32 @@ def qwen3_06b_decode(seed: int = 3, batch: int = 256, prompt=(100, 1024),
 def mixed_prefill(seed: int = 4, chunks: int = 4, chunk_len: int = 512,
                   prior_hi: int = 1536, n_decode: int = 192,
                   dec_lo: int = 256, dec_hi: int = 2048, num_q_heads: int = 16,
-                  num_kv_heads: int = 8, head_dim: int = 128) -> PagedBatch:
+                  num_kv_heads: int = 8, head_dim: int = 128,
+                  chunk_lens=None) -> PagedBatch:
     """Mixed chunked-prefill batch, by default the Qwen3-0.6B head shape (16 / 8 / 128, bf16):
-    ``chunks`` prefill chunks of ``chunk_len`` new tokens after a cached prior
-    context U[0, prior_hi], followed by ``n_decode`` decode sequences with
-    length U[dec_lo, dec_hi].  Prefill sequences come first."""
+    ``chunks`` prefill chunks of ``chunk_len`` new tokens (or the lengths listed
+    in ``chunk_lens``) after a cached prior context U[0, prior_hi], followed by
+    ``n_decode`` decode sequences with length U[dec_lo, dec_hi].  Prefill
+    sequences come first."""
+    if chunk_lens is not None:
+        chunks = len(chunk_lens)
+        new_tokens = np.asarray(chunk_lens, np.int64)
+    else:
+        new_tokens = np.full(chunks, chunk_len, np.int64)
+
     def lens(rng):
         prior = rng.integers(0, prior_hi + 1, size=chunks)
         dec = rng.integers(dec_lo, dec_hi + 1, size=n_decode)
-        return np.concatenate([prior + chunk_len, dec])
+        return np.concatenate([prior + new_tokens, dec])
 
     def qlens(rng, L):
-        return np.concatenate([np.full(chunks, chunk_len), np.ones(n_decode, np.int64)])
+        return np.concatenate([new_tokens, np.ones(n_decode, np.int64)])
     return make_batch(
         seed, name="mixed_prefill", dtype="bf16", num_q_heads=num_q_heads,
         num_kv_heads=num_kv_heads, head_dim=head_dim, draw_lens=lens, draw_query_lens=qlens,
         num_prefill_seqs=chunks,
-        recipe=(f"{chunks} chunks x {chunk_len} after prior U[0,{prior_hi}]; "
+        recipe=(f"{chunks} chunks x {[int(x) for x in new_tokens] if chunk_lens is not None else chunk_len} "
+                f"after prior U[0,{prior_hi}]; "
                 f"{n_decode} decode seqs L~U[{dec_lo},{dec_hi}]; pool 1.2x; N(0,1)->bf16"))
 
 
