@@ -2,11 +2,13 @@
 //
 // A chunk of n new query tokens of a sequence with context length L holds
 // rows (token t, head hh) of the kv head's GQA group, n*G rows in all; row
-// (t, hh) sees keys 0 .. L-n+t.  One workgroup of 4 waves owns 128 rows of
-// one (sequence, kv head); each wave owns two tiles of 16 rows, so every K and
-// V fragment it reads from LDS feeds two MFMAs.  Keys arrive in tiles of 64 (four
-// 16-token blocks, gathered through the block table into LDS, K and V both
-// row-major); the tile is shared by all four waves.
+// (t, hh) sees keys 0 .. L-n+t.  One workgroup owns 64 or 128 rows of one
+// (sequence, kv head), one or two 16-row tiles per wave (two tiles let one K
+// or V fragment read from LDS feed two MFMAs).  Keys arrive in
+// tiles of 64 (four 16-token blocks, gathered through the block table into
+// LDS, K and V both row-major); a tile is shared by the four row waves.  With
+// key halves, a second set of four waves takes every other tile for the same
+// rows and the two softmax states are merged at the end.
 //
 // Per tile and wave (v_mfma_f32_16x16x32_bf16, D = A*B + C, lane l holds
 // A[l%16][k-slice l/16], B[k-slice l/16][l%16], D[4*(l/16)+r][l%16]):
@@ -25,8 +27,9 @@
 //                      i/4 + 4k: lanes 4k..4k+3 of a group point at key row k
 //                      (dims 4 apart), and every lane receives one dim of four
 //                      consecutive keys.
-// Two LDS buffers: the next tile is written while the current one is read,
-// one barrier per tile; the tile after that is already loading from memory.
+// Two LDS buffers per key half: the next tile is written while the current
+// one is read, one barrier per tile; the tile after that is already loading
+// from memory.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -42,13 +45,24 @@ typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kKeys = 64;   // keys per tile
-constexpr int kWaves = 4;
-// Shape of the launch: 16-row tiles per wave (register blocking) and tiles of
-// keys in flight from memory (register buffers) while one is computed.
-constexpr int kNT = 2;
+constexpr int kKeys = 64;     // keys per tile
+constexpr int kRowWaves = 4;  // waves splitting a workgroup's rows
+// Shape of the launch: 16-row tiles per wave (register blocking), tiles of
+// keys in flight from memory (register buffers) while one is computed, and
+// key halves (a second set of waves takes every other tile of the same rows;
+// the two softmax states are merged at the end).
 constexpr int kDepth = 1;
-constexpr int kRowsPerGroup = 16 * kNT * kWaves;
+// Two launch shapes.  A launch with fewer workgroups than the chip has compute
+// units is bound by its longest chain of tiles: there each workgroup owns 64
+// rows (one 16-row tile per wave) and runs two key halves (twice the waves and
+// LDS, half the chain).  A larger launch is bound by throughput and shares
+// the chip with the decode rows of a mixed batch: there each workgroup owns 128
+// rows (two row tiles per wave, so each K/V fragment read from LDS feeds two
+// MFMAs) and one key range, which leaves a compute unit's LDS and wave slots
+// for the other kernel.
+constexpr int kSplitBelow = 256;
+constexpr int kRowsSmall = 16 * 1 * kRowWaves;
+constexpr int kRowsLarge = 16 * 2 * kRowWaves;
 
 __device__ __forceinline__ floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -61,28 +75,61 @@ __device__ __forceinline__ uint2 ld_tr(const unsigned char* p) {
     return __builtin_bit_cast(uint2, v);
 }
 
-// Max over the four lanes l, l^16, l^32, l^48 (the lanes holding one row's
-// scores): the gfx950 swaps exchange the upper 32 lanes of one operand with the
-// lower 32 of the other (and odd 16-lane rows with even ones), so with both
-// operands equal to x the two results are x and its partner lanes; no LDS trip.
-__device__ __forceinline__ float max_across_row_lanes(float x) {
+// Cross-lane steps for the four lanes l, l^16, l^32, l^48 that hold one row's
+// scores.  The gfx950 swaps exchange the upper 32 lanes of their first operand
+// with the lower 32 of the second (and odd 16-lane rows of the first with even
+// rows of the second); with both operands holding x, the two results hold x
+// and its partner lanes, without a trip through LDS.  The results are copied
+// out element by element: bit-casting an element of the returned vector in
+// place reads element 0 for both.
+__device__ __forceinline__ float2 swap_halves(float x) {  // (x, lanes l^32)
     const uint32_t b = __builtin_bit_cast(uint32_t, x);
-    const auto s32 = __builtin_amdgcn_permlane32_swap(b, b, false, false);
-    x = fmaxf(__builtin_bit_cast(float, s32[0]), __builtin_bit_cast(float, s32[1]));
-    const uint32_t c = __builtin_bit_cast(uint32_t, x);
-    const auto s16 = __builtin_amdgcn_permlane16_swap(c, c, false, false);
-    return fmaxf(__builtin_bit_cast(float, s16[0]), __builtin_bit_cast(float, s16[1]));
+    const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    return make_float2(__uint_as_float(r0), __uint_as_float(r1));
+}
+__device__ __forceinline__ float2 swap_rows(float x) {  // (x, lanes l^16)
+    const uint32_t b = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    return make_float2(__uint_as_float(r0), __uint_as_float(r1));
+}
+__device__ __forceinline__ float max_across_row_lanes(float x) {
+    const float2 a = swap_halves(x);
+    const float2 b = swap_rows(fmaxf(a.x, a.y));
+    return fmaxf(b.x, b.y);
+}
+__device__ __forceinline__ float sum_across_row_lanes(float x) {
+    const float2 a = swap_halves(x);
+    const float2 b = swap_rows(a.x + a.y);
+    return b.x + b.y;
 }
 
-template <int D, int NT, int DEPTH>
-__global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
+// Loads from a wave-uniform base plus a 32-bit lane offset.  The base goes
+// through readfirstlane, so the compiler keeps it in scalar registers and uses
+// the scalar-base form of the global load (no 64-bit vector address arithmetic
+// per load); the pointer stays in the global address space.
+typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+__device__ __forceinline__ uint4 ld16_at(const unsigned char* base, uint32_t off) {
+    const uint64_t v = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    typedef __attribute__((address_space(1))) const unsigned char global_u8;
+    const global_u8* b = reinterpret_cast<const global_u8*>(((uint64_t)hi << 32) | lo);
+    const u32x4 x = *reinterpret_cast<const global_u32x4*>(b + off);
+    return make_uint4(x.x, x.y, x.z, x.w);
+}
+
+template <int D, int NT, int DEPTH, int KSPLIT>
+__global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const ChunkArgs a) {
     constexpr int kNT = NT;
     constexpr int kRowsPerWave = 16 * NT;
-    constexpr int kRowsPerGroup = kRowsPerWave * kWaves;
+    constexpr int kRowsPerGroup = kRowsPerWave * kRowWaves;
     constexpr int KS = D / 32;           // 32-wide slices of head_dim (first product)
     constexpr int MT = D / 16;           // 16-dim tiles of the output (second product)
     constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
-    constexpr int LOADS = kKeys * CPR / (kWaves * 64);  // chunks per thread per tile
+    constexpr int HT = kRowWaves * 64;   // threads of one key half
+    constexpr int LOADS = kKeys * CPR / HT;  // chunks per thread per tile
     // LDS row strides: K rows are read 16 lanes x 16 bytes down a column, a
     // 16-byte pad spreads those rows over the banks; V rows are read by the
     // transposing loads as 4 rows x 32 bytes per 16 lanes, which a 32-byte pad
@@ -93,8 +140,10 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
     constexpr int VTILE = kKeys * VROW;
     constexpr int KEYS_PER_WAVE_LOAD = 64 / CPR;  // keys one wave covers per load slot
     static_assert(LOADS >= 1 && kBlock % KEYS_PER_WAVE_LOAD == 0, "tile loader");
-    __shared__ __align__(16) unsigned char lds_k[2 * KTILE];
-    __shared__ __align__(16) unsigned char lds_v[2 * VTILE];
+    // Two buffers per key half; the halves' states are merged through lds_k.
+    static_assert(KSPLIT == 1 || (kRowWaves * 64 * NT * (MT * 4 + 2) * 4 <= KSPLIT * 2 * KTILE), "merge space");
+    __shared__ __align__(16) unsigned char lds_k[KSPLIT * 2 * KTILE];
+    __shared__ __align__(16) unsigned char lds_v[KSPLIT * 2 * VTILE];
 
     const int s = blockIdx.z, g = blockIdx.y;
     const int G = a.num_q_heads / a.num_kv_heads;
@@ -110,8 +159,11 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform branches below
+    const int half = wave / kRowWaves;  // which key half this wave works on
+    const int rw = wave % kRowWaves;    // which rows
+    const int htid = tid % HT;          // thread index within the half
     const int li = lane & 15, kg = lane >> 4;
-    const int wrow0 = row0 + wave * kRowsPerWave;
+    const int wrow0 = row0 + rw * kRowsPerWave;
     // This lane's rows: wrow0 + 16*nt + li, nt = 0..kNT-1.
     bool row_ok[kNT];
     int trow[kNT], hh[kNT], lim[kNT];
@@ -151,49 +203,68 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
         for (int ks = 0; ks < KS; ++ks)
             qraw[nt][ks] = ld16(q + ((int64_t)(qs + t) * Hq + g * G + h) * D + ks * 32 + kg * 8);
     }
-    const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
-    const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
+
     const int64_t tok_stride = (int64_t)Hkv * D;
 
-    // Loader: thread tid moves chunks ci = tid + 256*u of a tile (key ci/CPR,
-    // 16-byte piece ci%CPR) from the pool into registers.  For one u the 64
-    // lanes of a wave cover 64/CPR consecutive keys inside one block, so the
-    // block id is wave-uniform: one scalar load per (wave, u).  Every lane
-    // loads, and every step loads a tile (past the last tile it reloads the
-    // last one; the clamped ids keep each address inside the pool): loads that
-    // are never skipped are counted exactly by the memory counter, so the wait
-    // before storing one register buffer leaves the later buffers in flight.
-    // Keys at or past kend (no row of this workgroup sees them) are masked out
-    // of the scores; their V rows, whatever the slots hold (NaN included), are
-    // stored as zeros so that a zero probability times them stays zero.
+    // Loader: thread htid of a half moves chunks ci = htid + 256*u of a tile
+    // (key ci/CPR, 16-byte piece ci%CPR) from the pool into registers.  For one
+    // u the 64 lanes of a wave cover 64/CPR consecutive keys inside one block,
+    // so the block id is wave-uniform: one scalar load per (wave, u).  Every
+    // lane loads, and every step loads a tile (past the last tile it reloads
+    // the last one; the clamped ids keep each address inside the pool): loads
+    // that are never skipped are counted exactly by the memory counter, so the
+    // wait before storing one register buffer leaves the later buffers in
+    // flight.  Keys at or past kend (no row of this workgroup sees them) are
+    // masked out of the scores; their V rows, whatever the slots hold (NaN
+    // included), are stored as zeros so that a zero probability times them
+    // stays zero.
     uint4 kreg[DEPTH][LOADS], vreg[DEPTH][LOADS];
+    // A tile starts on a block boundary, so each chunk's row inside its block,
+    // and with it the chunk's byte offset inside the block, is the same for
+    // every tile: only the (wave-uniform) block base changes, and the loads
+    // take it as a scalar base plus this per-lane offset.
+    const int64_t blk_bytes = (int64_t)kBlock * tok_stride * 2;
+    uint32_t lane_off[LOADS];
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+        const int ci = htid + u * HT;
+        const int key = ci / CPR, c = ci % CPR;
+        lane_off[u] = (uint32_t)(((key % kBlock) * tok_stride + g * D + c * 8) * 2);
+    }
+    const unsigned char* kbase = static_cast<const unsigned char*>(a.k_pool);
+    const unsigned char* vbase = static_cast<const unsigned char*>(a.v_pool);
     auto load_tile = [&](int tile, uint4 (&kr)[LOADS], uint4 (&vr)[LOADS]) {
         const int j0 = min(tile, ntiles - 1) * kKeys;
         int blk[LOADS];
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {  // scalar loads first, one wait for all
-            const int key0 = (wave * 64 + u * kWaves * 64) / CPR;  // wave-uniform
+            const int key0 = (rw * 64 + u * HT) / CPR;  // wave-uniform
             const int bi = min((j0 + key0) / kBlock, a.max_blocks - 1);
             blk[u] = min(max(bt[bi], 0), a.num_blocks - 1);
         }
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {
-            const int ci = tid + u * kWaves * 64;
-            const int key = ci / CPR, c = ci % CPR;
-            const int64_t off = ((int64_t)blk[u] * kBlock + ((j0 + key) % kBlock)) * tok_stride + (int64_t)g * D + c * 8;
-            kr[u] = ld16(kpool + off);
-            vr[u] = ld16(vpool + off);
+            const int64_t boff = (int64_t)blk[u] * blk_bytes;
+            kr[u] = ld16_at(kbase + boff, lane_off[u]);
+            vr[u] = ld16_at(vbase + boff, lane_off[u]);
         }
     };
+    // This half's LDS buffers.
+    unsigned char* const hk = lds_k + half * 2 * KTILE;
+    unsigned char* const hv = lds_v + half * 2 * VTILE;
     auto store_tile = [&](int buf, int j0, const uint4 (&kr)[LOADS], const uint4 (&vr)[LOADS]) {
+        const bool tail = j0 + kKeys > kend;  // wave-uniform: only the last tile
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {
-            const int ci = tid + u * kWaves * 64;
+            const int ci = htid + u * HT;
             const int key = ci / CPR, c = ci % CPR;
-            const uint32_t keep = 0u - (uint32_t)(j0 + key < kend);  // all ones or zero
-            const uint4 v = make_uint4(vr[u].x & keep, vr[u].y & keep, vr[u].z & keep, vr[u].w & keep);
-            *reinterpret_cast<uint4*>(lds_k + buf * KTILE + key * KROW + c * 16) = kr[u];
-            *reinterpret_cast<uint4*>(lds_v + buf * VTILE + key * VROW + c * 16) = v;
+            uint4 v = vr[u];
+            if (tail) {
+                const uint32_t keep = 0u - (uint32_t)(j0 + key < kend);  // all ones or zero
+                v = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+            }
+            st16(hk + buf * KTILE + key * KROW + c * 16, kr[u]);
+            st16(hv + buf * VTILE + key * VROW + c * 16, v);
         }
     };
 
@@ -208,11 +279,11 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
         for (int i = 0; i < MT; ++i) acc[nt][i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    // One tile of math on LDS buffer `buf` (keys j0 .. j0+63).
+    // One tile of math on this half's LDS buffer `buf` (keys j0 .. j0+63).
     auto compute_tile = [&](int j0, int buf) {
         if (j0 < wkend) {
-            const unsigned char* kt = lds_k + buf * KTILE;
-            const unsigned char* vt = lds_v + buf * VTILE;
+            const unsigned char* kt = hk + buf * KTILE;
+            const unsigned char* vt = hv + buf * VTILE;
             // S^T for keys j0 .. j0+63.  Every K fragment is read first and
             // the products follow, so the LDS reads overlap one another
             // instead of each waiting in front of its product; each fragment
@@ -222,7 +293,7 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    kf[mt][ks] = *reinterpret_cast<const uint4*>(kt + (mt * 16 + li) * KROW + (ks * 32 + kg * 8) * 2);
+                    kf[mt][ks] = ld16(kt + (mt * 16 + li) * KROW + (ks * 32 + kg * 8) * 2);
             __builtin_amdgcn_sched_barrier(0);
             floatx4 st[kNT][4];
 #pragma unroll
@@ -261,11 +332,12 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) sc[nt][mt * 4 + r] = st[nt][mt][r];
                 if (masked) {
+                    const int rel = lim[nt] - j0 - kg * 4;  // last visible key, tile-relative
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            if (j0 + mt * 16 + kg * 4 + r > lim[nt]) sc[nt][mt * 4 + r] = kNegInf;
+                            if (mt * 16 + r > rel) sc[nt][mt * 4 + r] = kNegInf;
                 }
                 float x = kNegInf;
 #pragma unroll
@@ -282,7 +354,10 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt) {
                     const float mn = mx[nt] > m[nt] + 8.0f ? mx[nt] : m[nt];
-                    const float alpha = fast_exp2(m[nt] - mn);
+                    // A row that has seen no key yet (possible in the second key
+                    // half, whose first tile can lie wholly past a row's last
+                    // visible key) has nothing to rescale: -inf - -inf is NaN.
+                    const float alpha = m[nt] == kNegInf ? 0.0f : fast_exp2(m[nt] - mn);
                     lsum[nt] *= alpha;
 #pragma unroll
                     for (int i = 0; i < MT; ++i) acc[nt][i] *= alpha;
@@ -303,7 +378,7 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
                 }
                 lsum[nt] += psum;
             }
-            // O^T += V^T P^T; each V^T fragment feeds both row tiles.
+            // O^T += V^T P^T; each V^T fragment feeds the kNT row tiles.
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 // keys 32*kk .. 32*kk+31: slots 0-3 from st[.][2kk], 4-7 from st[.][2kk+1]
@@ -321,16 +396,18 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
         }
     };
 
-    // Pipeline: LDS holds the tile being computed and the next one; DEPTH
-    // register buffers hold the tiles after that, loading from memory.  The
-    // tile loaded at step it is stored to LDS at step it+DEPTH.  The step count
-    // is rounded up to a multiple of DEPTH so the unrolled body runs whole:
-    // steps past the last tile compute nothing and store unused buffers.
+    // Pipeline, per key half h (tiles h, h+KSPLIT, h+2*KSPLIT, ...): LDS holds
+    // the tile being computed and the next one; DEPTH register buffers hold the
+    // tiles after that, loading from memory.  The tile loaded at step i is
+    // stored to LDS at step i+DEPTH.  Both halves run the same number of steps
+    // (rounded up to a multiple of DEPTH so the unrolled body runs whole); a
+    // step past the half's last tile computes nothing and stores an unused
+    // buffer.  One barrier per step serves both halves.
     if (ntiles > 0) {  // ntiles == 0 only for a sequence with no visible keys
         uint4 tile0k[LOADS], tile0v[LOADS];
-        load_tile(0, tile0k, tile0v);
+        load_tile(half, tile0k, tile0v);
 #pragma unroll
-        for (int d = 0; d < DEPTH; ++d) load_tile(d + 1, kreg[d], vreg[d]);
+        for (int d = 0; d < DEPTH; ++d) load_tile(half + KSPLIT * (d + 1), kreg[d], vreg[d]);
         // An identity DPP move makes the q registers the result of a vector
         // instruction: the tile loop then never waits on memory for them (its
         // memory waits are for the tile prefetch only).
@@ -347,27 +424,63 @@ __global__ __launch_bounds__(kWaves * 64) void chunk_kernel(const ChunkArgs a) {
                 qf[nt][ks] = as_bf16x8(v);
             }
         }
-        store_tile(0, 0, tile0k, tile0v);
+        store_tile(0, half * kKeys, tile0k, tile0v);
         __syncthreads();
-        const int nsteps = (ntiles + DEPTH - 1) / DEPTH * DEPTH;
-        for (int it0 = 0; it0 < nsteps; it0 += DEPTH) {
+        const int hsteps = (ntiles + KSPLIT - 1) / KSPLIT;
+        const int nsteps = (hsteps + DEPTH - 1) / DEPTH * DEPTH;
+        for (int i0 = 0; i0 < nsteps; i0 += DEPTH) {
 #pragma unroll
             for (int r = 0; r < DEPTH; ++r) {  // unrolled: static register buffers
-                const int it = it0 + r;
-                const int j0 = it * kKeys;
-                compute_tile(j0, it & 1);
-                store_tile((it + 1) & 1, j0 + kKeys, kreg[r], vreg[r]);
-                load_tile(it + 1 + DEPTH, kreg[r], vreg[r]);
+                const int i = i0 + r;
+                const int tile = half + KSPLIT * i;
+                compute_tile(tile * kKeys, i & 1);
+                store_tile((i + 1) & 1, (tile + KSPLIT) * kKeys, kreg[r], vreg[r]);
+                load_tile(tile + KSPLIT * (1 + DEPTH), kreg[r], vreg[r]);
                 __syncthreads();
             }
         }
     }
 
+    if constexpr (KSPLIT == 2) {
+        // Merge the two halves' softmax states (same rows, disjoint keys):
+        // the second half leaves (m, l, acc) in LDS, lane-fastest, and the
+        // first rescales both to the larger reference max.  The tile loop
+        // ended with a barrier, so the tile buffers are free.
+        float* xs = reinterpret_cast<float*>(lds_k) + rw * 64 + lane;
+        constexpr int kStride = kRowWaves * 64;
+        if (half == 1) {
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                float* x = xs + nt * (MT * 4 + 2) * kStride;
+                x[0] = m[nt];
+                x[kStride] = lsum[nt];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) x[(2 + mt * 4 + r) * kStride] = acc[nt][mt][r];
+            }
+        }
+        __syncthreads();
+        if (half == 1) return;
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            const float* x = xs + nt * (MT * 4 + 2) * kStride;
+            const float m1 = x[0];
+            const float M = fmaxf(m[nt], m1);
+            const float a0 = m[nt] == kNegInf ? 0.0f : fast_exp2(m[nt] - M);
+            const float a1 = m1 == kNegInf ? 0.0f : fast_exp2(m1 - M);
+            lsum[nt] = lsum[nt] * a0 + x[kStride] * a1;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[nt][mt][r] = acc[nt][mt][r] * a0 + x[(2 + mt * 4 + r) * kStride] * a1;
+        }
+    }
+
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
-        float l = lsum[nt];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        const float l = sum_across_row_lanes(lsum[nt]);
         if (!row_ok[nt]) continue;
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
         uint16_t* out = static_cast<uint16_t*>(a.out) + ((int64_t)(qs + trow[nt]) * Hq + g * G + hh[nt]) * D + kg * 4;
@@ -391,13 +504,20 @@ int32_t launch_chunks(const ChunkArgs& a, hipStream_t stream) {
     const int group = a.num_q_heads / a.num_kv_heads;
     if (!chunks_supported(a.dtype, a.head_dim, group)) return PA_ERR_UNSUPPORTED;
     if (a.num_seqs == 0 || a.max_query_len == 0) return PA_OK;
-    const int64_t tiles = ((int64_t)a.max_query_len * group + kRowsPerGroup - 1) / kRowsPerGroup;
+    const int64_t rows = (int64_t)a.max_query_len * group;
+    const int64_t small_tiles = (rows + kRowsSmall - 1) / kRowsSmall;
+    const bool small = small_tiles * a.num_kv_heads * a.num_seqs < kSplitBelow;
+    const int64_t tiles = small ? small_tiles : (rows + kRowsLarge - 1) / kRowsLarge;
     if (tiles > INT32_MAX || a.num_seqs > 65535) return PA_ERR_SHAPE;
-    dim3 grid((unsigned)tiles, a.num_kv_heads, a.num_seqs);
-    if (a.head_dim == 128)
-        hipLaunchKernelGGL((chunk_kernel<128, kNT, kDepth>), grid, dim3(kWaves * 64), 0, stream, a);
-    else
-        hipLaunchKernelGGL((chunk_kernel<64, kNT, kDepth>), grid, dim3(kWaves * 64), 0, stream, a);
+    const dim3 grid((unsigned)tiles, a.num_kv_heads, a.num_seqs);
+    const dim3 block(kRowWaves * (small ? 2 : 1) * 64);
+    if (a.head_dim == 128) {
+        if (small) hipLaunchKernelGGL((chunk_kernel<128, 1, kDepth, 2>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((chunk_kernel<128, 2, kDepth, 1>), grid, block, 0, stream, a);
+    } else {
+        if (small) hipLaunchKernelGGL((chunk_kernel<64, 1, kDepth, 2>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((chunk_kernel<64, 2, kDepth, 1>), grid, block, 0, stream, a);
+    }
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -53,15 +53,23 @@ __device__ __forceinline__ float group_sum(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // 16-byte global load / store.
-__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// 16-byte loads and stores go through a native 4 x u32 vector so that the
+// compiler keeps the values in registers (a struct copy can end up as a
+// memcpy through private memory).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16(const void* p) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // 16-byte load marked non-temporal: data read once (K/V streamed from HBM)
 // should not displace cached data that is reused.
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld16_stream(const void* p) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
 }
-__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+__device__ __forceinline__ void st16(void* p, uint4 v) {
+    *reinterpret_cast<u32x4*>(p) = u32x4{v.x, v.y, v.z, v.w};
+}
 
 }  // namespace pa

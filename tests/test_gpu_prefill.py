@@ -8,8 +8,8 @@ import pytest
 import torch
 
 import oracle
-from helpers import DeviceBatch, assert_close, dev, ensure_built, f64
-from workloads import mixed_prefill
+from helpers import DeviceBatch, assert_close, bits, dev, ensure_built, f64
+from workloads import f32_to_bf16_bits, mixed_prefill
 
 pytestmark = pytest.mark.gpu
 
@@ -30,6 +30,14 @@ WORKLOADS = {
                                                   n_decode=2, dec_lo=1, dec_hi=50),
     "prefill_only_p0": lambda: mixed_prefill(chunks=2, chunk_len=70, prior_hi=0, n_decode=0),
     "mixed_full": mixed_prefill,
+    # head_dim 64 (Qwen2.5-0.5B heads, G = 7): a small launch (key halves) and
+    # a large one (two row tiles per wave)
+    "mixed_d64_small": lambda: mixed_prefill(seed=10, chunks=3, chunk_len=50, prior_hi=200, n_decode=5,
+                                             dec_lo=1, dec_hi=600, num_q_heads=14, num_kv_heads=2,
+                                             head_dim=64),
+    "mixed_d64_large": lambda: mixed_prefill(seed=11, chunks=8, chunk_len=300, prior_hi=700, n_decode=16,
+                                             dec_lo=1, dec_hi=1200, num_q_heads=14, num_kv_heads=2,
+                                             head_dim=64),
     # chunks on both paths in one batch: 3, 7 and 1 rows give fewer than 16
     # (row, head) pairs per kv head at G = 2 (vector path), 40 and 64 do not
     "mixed_ragged_chunks": lambda: mixed_prefill(seed=8, chunk_lens=[3, 40, 7, 1, 64], prior_hi=300,
@@ -117,3 +125,57 @@ def test_decode_rows_match_pa_decode(pa):
                   b.max_context_len, scale=b.scale, partition_tokens=64)
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), whole[rows].view(torch.int16))
+
+
+@pytest.mark.parametrize("shape", [(3, 72, 150), (6, 200, 900)], ids=["key_halves", "one_range"])
+def test_prefill_needle_exact(pa, shape):
+    """Causal chunks with one dominant key per (sequence, kv head): q rows are
+    c * e0 and K has dim 0 zero except at the needle token (c there), c = 64,
+    so the needle's weight is exp2(~520) times any other.  Rows at or after
+    the needle get its V row exactly; an error in the row maximum (a lane
+    group of scores left out) overflows the exponentials instead.  Rows
+    before it see equal scores and get the mean of their visible V rows.
+    The small batch launches the matrix-core kernel with key halves, the
+    larger one without."""
+    chunks, chunk_len, prior_hi = shape
+    b = mixed_prefill(seed=9, chunks=chunks, chunk_len=chunk_len, prior_hi=prior_hi, n_decode=2,
+                      dec_lo=20, dec_hi=100)
+    kp, vp = oracle.kv_write(b.k_pool, b.v_pool, b.new_k, b.new_v, b.slot_mapping)
+    rng = np.random.default_rng(99)
+    c = f32_to_bf16_bits(np.array([64.0], np.float32))[0]
+    hkv, D = kp.shape[2], kp.shape[3]
+    krows, vrows = kp.reshape(-1, hkv, D), vp.reshape(-1, hkv, D)
+    needles = np.zeros((b.num_seqs, hkv), np.int64)
+    for s in range(b.num_seqs):
+        L = int(b.context_lens[s])
+        j = np.arange(L)
+        rows = b.block_tables[s, j // 16] * 16 + j % 16
+        needles[s] = rng.integers(0, L, size=hkv)
+        krows[rows, :, 0] = 0
+        krows[rows[needles[s]], np.arange(hkv), 0] = c
+        vrows[rows] = f32_to_bf16_bits((1 + rng.random((L, hkv, D))).astype(np.float32))
+    q = np.zeros_like(b.q)
+    q[:, :, 0] = c
+    ref = oracle.attention(q, b.query_start_loc, kp, vp, b.block_tables, b.context_lens, b.scale,
+                           b.dtype)
+    # some needles sit outside the first 4-key lane group of their 16 keys
+    assert ((needles % 16) >= 4).sum() >= 4
+    print(f"[needle] chunks={chunks} x {chunk_len}", flush=True)
+    out = pa.prefill_chunk(dev(q), dev(b.query_start_loc), b.num_prefill_seqs, b.max_query_len,
+                           dev(kp), dev(vp), dev(b.block_tables), dev(b.context_lens),
+                           b.max_context_len, scale=b.scale)
+    torch.cuda.synchronize()
+    ob = bits(out)
+    assert_close(f64(out), ref, b.dtype, "needle")
+    G = b.q.shape[1] // hkv
+    exact = 0
+    for s in range(b.num_seqs):
+        q0, n, L = int(b.query_start_loc[s]), int(b.query_lens[s]), int(b.context_lens[s])
+        for i in range(n):
+            for h in range(b.q.shape[1]):
+                j = needles[s, h // G]
+                if j <= L - n + i:
+                    want = vp[b.block_tables[s, j // 16], j % 16, h // G]
+                    assert np.array_equal(ob[q0 + i, h], want), (s, i, h, j)
+                    exact += 1
+    assert exact > 100
