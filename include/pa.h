@@ -163,14 +163,15 @@ int32_t pa_decode(const void* q, const void* k_pool, const void* v_pool,
  * Row i of a sequence with n rows and context length L sits at position
  * L-n+i and attends to keys 0 .. L-n+i (causal, aligned to the context end).
  * Chunks giving at least 16 (row, head) pairs per kv head run on the matrix
- * cores; the rest, and the decode rows, run on the vector path.  When both
- * kinds are present the matrix-core kernel runs on the library's auxiliary
- * stream for the device, concurrently with the vector path on `stream`: it
- * waits for the work enqueued on `stream` before the call, and work enqueued
- * on `stream` after the call waits for it (event fork/join, which HIP graph
- * capture records as well).
- * The workspace covers the vector path's processing order and split-context
- * partials.
+ * cores; the rest, and the decode rows, run on the vector path.  When
+ * matrix-core chunks and decode rows are both present, the matrix-core kernel
+ * runs on the library's auxiliary stream for the device, concurrently with the
+ * vector path on `stream`: it waits for the work enqueued on `stream` before
+ * the call, and work enqueued on `stream` after the call waits for it (event
+ * fork/join, which HIP graph capture records as well).
+ * The workspace (pa_prefill_workspace_bytes) holds the decode rows' processing
+ * order and split-context partials, then, 256-byte aligned, the prefill rows'
+ * split-context partials; the two parts never overlap.
  */
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_prefill_seqs,
                                   int32_t total_query_tokens, int32_t num_q_heads,

@@ -282,7 +282,9 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_prefill_seqs,
         return 0;
     const int64_t num_decode = num_seqs - num_prefill_seqs;
     const int64_t prefill_rows = (int64_t)total_query_tokens - num_decode;
-    size_t need = 0;
+    // [decode rows' part, 256-byte aligned][prefill rows' part]: the two
+    // vector-path launches may run at the same time on two streams.
+    size_t pre = 0, dec = 0;
     if (prefill_rows > 0) {
         // The vector path covers either every prefill row or, when the matrix
         // cores take the large chunks, a few row slots per prefill sequence;
@@ -291,15 +293,14 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_prefill_seqs,
         for (const int64_t items : {prefill_rows, slots}) {
             const int32_t part = choose_partition(items, num_kv_heads, max_context_len, partition_tokens);
             const size_t p = rows_bytes(items, num_q_heads, num_kv_heads, head_dim, max_context_len, part, false);
-            if (p > need) need = p;
+            if (p > pre) pre = p;
         }
     }
     if (num_decode > 0) {
         const int32_t part = choose_partition(num_decode, num_kv_heads, max_context_len, partition_tokens);
-        const size_t d = rows_bytes(num_decode, num_q_heads, num_kv_heads, head_dim, max_context_len, part, true);
-        if (d > need) need = d;
+        dec = rows_bytes(num_decode, num_q_heads, num_kv_heads, head_dim, max_context_len, part, true);
     }
-    return need;
+    return pre > 0 ? align256(dec) + pre : dec;
 }
 
 int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t total_query_tokens,
@@ -344,7 +345,9 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
     base.scale = scale;
     base.out = out;
 
-    // Check both vector-path launches before enqueuing anything.
+    // Check both vector-path launches before enqueuing anything.  Their
+    // workspace parts are disjoint (decode rows first), so the two launches
+    // need no ordering between them.
     RowsArgs pre = base, dec = base;
     pre.query_start_loc = query_start_loc;
     pre.seq_begin = 0;
@@ -355,8 +358,6 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
     pre.small_rows = mfma ? small_rows_for(group) : 0;
     const int64_t pre_items = mfma ? (int64_t)num_prefill_seqs * pre.small_rows : prefill_rows;
     if (pre_items > INT32_MAX) return PA_ERR_SHAPE;
-    const int32_t ppart = choose_partition(pre_items, pool.num_kv_heads, max_context_len, partition_tokens);
-    if (int32_t st = prepare_rows(pre, pre_items, ppart, workspace, workspace_bytes)) return st;
     dec.query_start_loc = nullptr;
     dec.seq_begin = num_prefill_seqs;
     dec.seq_end = num_seqs;
@@ -364,6 +365,16 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
     dec.mfma_min_pairs = 0;
     const int32_t dpart = choose_partition(num_decode, pool.num_kv_heads, max_context_len, partition_tokens);
     if (int32_t st = prepare_rows(dec, num_decode, dpart, workspace, workspace_bytes)) return st;
+    const size_t dec_bytes = align256(rows_bytes(num_decode, num_q_heads, pool.num_kv_heads,
+                                                 pool.head_dim, max_context_len, dpart, true));
+    const int32_t ppart = choose_partition(pre_items, pool.num_kv_heads, max_context_len, partition_tokens);
+    const bool pre_ws = rows_bytes(pre_items, num_q_heads, pool.num_kv_heads, pool.head_dim,
+                                   max_context_len, ppart, false) > 0;
+    if (pre_ws && workspace_bytes < dec_bytes) return PA_ERR_WORKSPACE;
+    if (int32_t st = prepare_rows(pre, pre_items, ppart,
+                                  pre_ws ? static_cast<char*>(workspace) + dec_bytes : nullptr,
+                                  pre_ws ? workspace_bytes - dec_bytes : 0))
+        return st;
 
     ChunkArgs c = {};
     if (mfma) {
@@ -400,6 +411,9 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
             return PA_ERR_LAUNCH;
         if (int32_t st = launch_chunks(c, ax->stream)) return st;
         if (hipEventRecord(ax->join, ax->stream) != hipSuccess) return PA_ERR_LAUNCH;
+        // The small chunks' rows go first on `stream`: measured on the mixed
+        // batch, the chunks finish sooner beside the decode rows when the
+        // decode rows start a few microseconds after them.
         if (int32_t st = run_rows(pre, s)) return st;
         if (int32_t st = run_rows(dec, s)) return st;
         return hipStreamWaitEvent(s, ax->join, 0) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

@@ -134,3 +134,13 @@ def test_prefill_workspace_covers_both_vector_path_layouts(pa):
     assert pa.prefill_workspace_bytes(4, 4, 4, 16, 8, 128, 2048, 0) == max(rows, slots)
     # one pass requested: no partials, and no longest-first order for chunk rows
     assert pa.prefill_workspace_bytes(4, 4, 4, 16, 8, 128, 2048, -1) == 0
+
+
+def test_prefill_workspace_parts_are_disjoint(pa):
+    """Decode rows' part first (256-byte aligned), then the prefill rows' part:
+    the two vector-path launches can run concurrently on two streams.  One
+    decode row (8 units, split into 32 parts of 64 tokens) and four one-row
+    chunks (sized as in the test above)."""
+    dec = 1 * 16 * 32 * 130 * 4
+    pre = 28 * 16 * 8 * 130 * 4
+    assert pa.prefill_workspace_bytes(5, 4, 5, 16, 8, 128, 2048, 0) == (dec + 255) // 256 * 256 + pre
