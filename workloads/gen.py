@@ -228,6 +228,27 @@ def make_batch(
     )
 
 
+def packed_qkv(b: PagedBatch, pad_cols: int = 0) -> np.ndarray:
+    """The batch's new-token q, k and v as the rows of one packed projection
+    output, [T, (Hq + 2*Hkv) * D + pad_cols]: q heads, then k heads, then v
+    heads (pad columns hold poison).  Reuses the batch's draws."""
+    T = b.q.shape[0]
+    hq, hkv, d = b.num_q_heads, b.num_kv_heads, b.head_dim
+    parts = [b.q.reshape(T, hq * d), b.new_k[:T].reshape(T, hkv * d), b.new_v[:T].reshape(T, hkv * d)]
+    if pad_cols:
+        parts.append(np.full((T, pad_cols), _poison_value(b.dtype), dtype=b.q.dtype))
+    return np.ascontiguousarray(np.concatenate(parts, axis=1))
+
+
+def norm_weights(b: PagedBatch, seed: int):
+    """Per-head RMSNorm weights for q and k, [D] each: 1 + 0.1 * N(0, 1),
+    stored like the batch (drawn from their own generator)."""
+    rng = np.random.default_rng(seed)
+    w = (1.0 + 0.1 * rng.standard_normal(size=(2, b.head_dim))).astype(np.float32)
+    w = f32_to_bf16_bits(w) if b.dtype == "bf16" else w
+    return w[0].copy(), w[1].copy()
+
+
 # ---------------------------------------------------------------------------
 # Workloads shaped like the pages' benchmarks.  Head shapes follow the model
 # each page names; the sizes keyword arguments shrink them for parity tests.
