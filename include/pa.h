@@ -1,13 +1,16 @@
 /*
  * pa.h -- C ABI of the paged-KV attention library for MI355X (gfx950).
  *
- * The library has three operations, taken from how the pages frame the
+ * The library has four operations, taken from how the pages frame the
  * problem:
  *
  *   pa_kv_write       append each step's new K/V rows into a shared block pool
  *                     at flat slots ("mini_engine", Next: fused kernels -- the
  *                     fused KV-cache write; "mini-vllm", Milestones item 7 --
  *                     GPU-side slot derivation).
+ *   pa_qkv_rope_write the same write fed straight from the packed QKV
+ *                     projection: q/k norm and rotary embedding applied, slots
+ *                     derived on the device from the block tables.
  *   pa_decode         batched grouped-query decode attention over a ragged set
  *                     of sequences, reading K/V in place through per-sequence
  *                     block tables ("09 -- Mini Inference Engine (The
@@ -106,6 +109,52 @@ int32_t pa_kv_write(const void* k, const void* v,
                     const int32_t* slot_mapping, int32_t num_tokens,
                     void* k_pool, void* v_pool, pa_pool_desc pool,
                     void* stream);
+
+/*
+ * pa_qkv_rope_write -- split the packed QKV projection, apply the rotary
+ * embedding (and optionally Qwen3's per-head RMSNorm) to q and k, store k and
+ * v in the pools at slots derived on the device, and write the rotated q.
+ * ("mini_engine", What it does: QKV packed into one GEMM, RoPE, RMSNorm; Next:
+ * fused kernels -- fused RoPE, fused QKV split and KV-cache write; "mini-vllm",
+ * Milestones item 7 -- GPU-side slot derivation.)
+ *
+ * qkv               [num_tokens, *] rows; consecutive tokens are
+ *                   qkv_token_stride ELEMENTS apart (>= (Hq + 2*Hkv) * D); a row
+ *                   holds the Hq q heads, then the Hkv k heads, then the Hkv v
+ *                   heads, each head_dim elements.
+ * query_start_loc   int32 [num_seqs + 1] as in pa_prefill_chunk (tokens of
+ *                   sequence s are qsl[s] .. qsl[s+1]-1), or NULL: one token per
+ *                   sequence, token t belongs to sequence t (num_seqs must equal
+ *                   num_tokens).
+ * context_lens      int32 [num_seqs]; lengths AFTER this step's tokens (write
+ *                   first, then attend): token i of a sequence with n tokens
+ *                   and length L is at position L - n + i.
+ * block_tables      int32 [num_seqs, max_blocks_per_seq].
+ * Slot of a token = block_tables[s][pos / 16] * 16 + pos % 16.  When the
+ * position lies outside the table or the entry outside the pool, nothing is
+ * written to the pools for that token (its q row is still written) and its
+ * slot reads -1.
+ * rope_theta        rotary base (> 0).  Rotate-half convention: dims i and
+ *                   i + D/2 of every q and k head turn by pos * theta^(-2i/D),
+ *                   computed in fp32 with precise sine and cosine.
+ * q_norm_weight, k_norm_weight
+ *                   [head_dim] each, in the pool's element type, or NULL: with a
+ *                   weight, each head is RMS-normalised (x / sqrt(mean(x^2) +
+ *                   norm_eps) * w) before the rotation.
+ * q_out             [num_tokens, Hq, D] rotated q, element type of the pool.
+ * slot_mapping_out  int32 [num_tokens] or NULL: the derived slots.
+ * Written K rows hold the rotated k rounded to the element type; V rows are the
+ * input's bits.  Nothing else in the pools changes.  qkv, its token stride in
+ * bytes and the pools must be 16-byte aligned.  num_tokens == 0 returns PA_OK
+ * without enqueuing anything.
+ */
+int32_t pa_qkv_rope_write(const void* qkv, int64_t qkv_token_stride,
+                          const int32_t* query_start_loc, int32_t num_tokens, int32_t num_seqs,
+                          const int32_t* context_lens, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, int32_t num_q_heads, float rope_theta,
+                          const void* q_norm_weight, const void* k_norm_weight, float norm_eps,
+                          void* q_out, void* k_pool, void* v_pool, pa_pool_desc pool,
+                          int32_t* slot_mapping_out, void* stream);
 
 /*
  * Split-context choice shared by pa_decode and pa_prefill_chunk:

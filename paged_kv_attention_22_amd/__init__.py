@@ -45,6 +45,8 @@ _SIGNATURES = {
     "pa_decode_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (c_i32, [c_vp, c_vp, c_vp, PoolDesc, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
                           c_f, c_vp, c_i32, c_vp, c_size, c_vp]),
+    "pa_qkv_rope_write": (c_i32, [c_vp, c_i64, c_vp, c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_f,
+                                  c_vp, c_vp, c_f, c_vp, c_vp, c_vp, PoolDesc, c_vp, c_vp]),
     "pa_prefill_workspace_bytes": (c_size, [c_i32] * 8),
     "pa_prefill_chunk": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, PoolDesc,
                                  c_vp, c_i32, c_vp, c_i32, c_i32, c_f, c_vp, c_i32, c_vp,
@@ -128,6 +130,34 @@ def kv_write(k, v, slot_mapping, k_pool, v_pool, stream=None) -> None:
                            _contig(k_pool, "k_pool"), _contig(v_pool, "v_pool"),
                            pool_desc(k_pool), _stream(stream))
     _check(st, "pa_kv_write")
+
+
+def qkv_rope_write(qkv, num_q_heads, context_lens, block_tables, k_pool, v_pool, rope_theta,
+                   query_start_loc=None, q_norm=None, k_norm=None, eps=1e-6, q_out=None,
+                   slot_mapping_out=None, stream=None):
+    """Packed projection rows qkv [T, >= (Hq + 2*Hkv) * D] -> rotated q [T, Hq, D];
+    rotated k and v stored in the pools at slots derived from the tables.
+    query_start_loc None: one token per sequence."""
+    if qkv.dim() != 2 or qkv.stride(1) != 1:
+        raise ValueError("qkv must be [T, width] with contiguous rows")
+    if qkv.dtype != k_pool.dtype:
+        raise TypeError("qkv and pools must share an element type")
+    T = qkv.shape[0]
+    S = context_lens.shape[0]
+    D = k_pool.shape[3]
+    if q_out is None:
+        q_out = torch.empty((T, num_q_heads, D), dtype=qkv.dtype, device=qkv.device)
+    qsl = 0 if query_start_loc is None else _i32(query_start_loc, "query_start_loc")
+    qn = 0 if q_norm is None else _contig(q_norm, "q_norm")
+    kn = 0 if k_norm is None else _contig(k_norm, "k_norm")
+    so = 0 if slot_mapping_out is None else _i32(slot_mapping_out, "slot_mapping_out")
+    st = lib().pa_qkv_rope_write(_dev(qkv, "qkv"), qkv.stride(0), qsl, T, S,
+                                 _i32(context_lens, "context_lens"), _i32(block_tables, "block_tables"),
+                                 block_tables.shape[1], int(num_q_heads), float(rope_theta), qn, kn,
+                                 float(eps), _contig(q_out, "q_out"), _contig(k_pool, "k_pool"),
+                                 _contig(v_pool, "v_pool"), pool_desc(k_pool), so, _stream(stream))
+    _check(st, "pa_qkv_rope_write")
+    return q_out
 
 
 def decode_partition_tokens(num_seqs, num_kv_heads, max_context_len, partition_tokens=0) -> int:

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build", "libpa")
 LIB = os.path.join(PKG, "libpa.so")
 
-SOURCES = ["kv_write.hip", "attn_rows.hip", "attn_chunks.hip", "pa_api.cpp"]
+SOURCES = ["kv_write.hip", "qkv_write.hip", "attn_rows.hip", "attn_chunks.hip", "pa_api.cpp"]
 ARCH = "gfx950"
 
 

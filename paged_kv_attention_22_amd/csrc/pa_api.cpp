@@ -1,6 +1,7 @@
 // C ABI of the library: host-side validation, path choice and launch.
 // Nothing here touches the GPU before every argument has been checked, and
 // nothing reads device memory: sizes come in as host integers.
+#include <math.h>
 #include <stdint.h>
 
 #include <mutex>
@@ -270,6 +271,53 @@ int32_t pa_decode(const void* q, const void* k_pool, const void* v_pool, pa_pool
     const int32_t part = choose_partition(num_seqs, pool.num_kv_heads, max_context_len, partition_tokens);
     if (int32_t st = prepare_rows(a, num_seqs, part, workspace, workspace_bytes)) return st;
     return run_rows(a, static_cast<hipStream_t>(stream));
+}
+
+int32_t pa_qkv_rope_write(const void* qkv, int64_t qkv_token_stride,
+                          const int32_t* query_start_loc, int32_t num_tokens, int32_t num_seqs,
+                          const int32_t* context_lens, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, int32_t num_q_heads, float rope_theta,
+                          const void* q_norm_weight, const void* k_norm_weight, float norm_eps,
+                          void* q_out, void* k_pool, void* v_pool, pa_pool_desc pool,
+                          int32_t* slot_mapping_out, void* stream) {
+    if (int32_t st = check_pool(pool)) return st;
+    if (num_tokens < 0 || num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
+        return PA_ERR_SHAPE;
+    if (query_start_loc == nullptr && num_seqs != num_tokens) return PA_ERR_SHAPE;
+    if (num_tokens > 0 && num_seqs == 0) return PA_ERR_SHAPE;
+    const int64_t width = (int64_t)(num_q_heads + 2 * pool.num_kv_heads) * pool.head_dim;
+    if (qkv_token_stride < width) return PA_ERR_SHAPE;
+    if (!(rope_theta > 0.0f) || !isfinite(rope_theta) || !(norm_eps >= 0.0f) || !isfinite(norm_eps))
+        return PA_ERR_SHAPE;
+    if (num_tokens == 0) return PA_OK;
+    if (!qkv || !context_lens || !block_tables || !q_out || !k_pool || !v_pool) return PA_ERR_NULL;
+    const int es = elem_size(pool.dtype);
+    if (!aligned16(qkv) || (qkv_token_stride * es) % 16 != 0 || !aligned16(k_pool) ||
+        !aligned16(v_pool))
+        return PA_ERR_ALIGN;
+    QkvArgs a = {};
+    a.qkv = qkv;
+    a.qkv_stride = qkv_token_stride;
+    a.query_start_loc = query_start_loc;
+    a.num_seqs = num_seqs;
+    a.num_tokens = num_tokens;
+    a.context_lens = context_lens;
+    a.block_tables = block_tables;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = pool.num_kv_heads;
+    a.head_dim = pool.head_dim;
+    a.num_blocks = pool.num_blocks;
+    a.dtype = pool.dtype;
+    a.log2_theta = log2f(rope_theta);
+    a.q_norm = q_norm_weight;
+    a.k_norm = k_norm_weight;
+    a.eps = norm_eps;
+    a.q_out = q_out;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.slots_out = slot_mapping_out;
+    return launch_qkv_write(a, static_cast<hipStream_t>(stream));
 }
 
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_prefill_seqs,

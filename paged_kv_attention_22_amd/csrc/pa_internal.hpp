@@ -70,6 +70,28 @@ struct KvWriteArgs {
 
 int32_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 
+// Fused QKV split + rotary embedding + KV write; one workgroup per token.
+struct QkvArgs {
+    const void* qkv;
+    int64_t qkv_stride;                 // ELEMENTS between consecutive tokens
+    const int32_t* query_start_loc;     // NULL: token t is sequence t
+    int32_t num_seqs, num_tokens;
+    const int32_t* context_lens;
+    const int32_t* block_tables;
+    int32_t max_blocks;
+    int32_t num_q_heads, num_kv_heads, head_dim, num_blocks, dtype;
+    float log2_theta;                   // log2 of the rotary base
+    const void* q_norm;                 // [head_dim] or NULL (no norm)
+    const void* k_norm;
+    float eps;
+    void* q_out;
+    void* k_pool;
+    void* v_pool;
+    int32_t* slots_out;                 // [num_tokens] or NULL
+};
+
+int32_t launch_qkv_write(const QkvArgs& a, hipStream_t stream);
+
 // Matrix-core causal chunk attention for prefill sequences 0..num_seqs-1 whose
 // rows give at least `min_pairs` (row, head) pairs per kv head.
 struct ChunkArgs {

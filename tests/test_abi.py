@@ -144,3 +144,29 @@ def test_prefill_workspace_parts_are_disjoint(pa):
     dec = 1 * 16 * 32 * 130 * 4
     pre = 28 * 16 * 8 * 130 * 4
     assert pa.prefill_workspace_bytes(5, 4, 5, 16, 8, 128, 2048, 0) == (dec + 255) // 256 * 256 + pre
+
+
+def test_qkv_rope_write_validation(pa):
+    L = pa.lib()
+    p = pool(hkv=2, d=64)               # width (Hq + 2*Hkv) * D = (4 + 4) * 64 = 512
+
+    def call(**kw):
+        a = dict(qkv=FAKE, stride=512, qsl=FAKE, T=6, S=2, ctx=FAKE, bt=FAKE, maxb=4, Hq=4,
+                 theta=1e6, qn=0, kn=0, eps=1e-6, qo=FAKE, kp=FAKE, vp=FAKE, pool=p, so=0)
+        a.update(kw)
+        return L.pa_qkv_rope_write(a["qkv"], a["stride"], a["qsl"], a["T"], a["S"], a["ctx"],
+                                   a["bt"], a["maxb"], a["Hq"], a["theta"], a["qn"], a["kn"],
+                                   a["eps"], a["qo"], a["kp"], a["vp"], a["pool"], a["so"], 0)
+    assert call(T=0) == 0                       # no tokens: no-op
+    assert call(qkv=0) == 1
+    assert call(qo=0) == 1
+    assert call(stride=511) == 2                # narrower than a packed row
+    assert call(stride=516) == 7                # 1032-byte token stride: not 16-byte aligned
+    assert call(qkv=FAKE + 2) == 7
+    assert call(qsl=0) == 2                     # one token per sequence needs S == T
+    assert call(T=4, S=0) == 2
+    assert call(theta=0.0) == 2
+    assert call(theta=float("inf")) == 2
+    assert call(eps=-1.0) == 2
+    assert call(pool=pool(hkv=2, d=96)) == 4
+    assert call(pool=pool(hkv=2, d=64, dtype=5)) == 3

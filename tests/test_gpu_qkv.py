@@ -1,0 +1,147 @@
+"""pa_qkv_rope_write on the GPU against the fp64 oracle (oracle/qkv.py):
+rotated q, the pool rows it writes (V bit-exact, K within the rounding of the
+element type), every other pool byte unchanged, the derived slots bit-exact,
+tokens whose table entry lies outside the pool left unwritten, and the fused
+write feeding the attention calls."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import assert_close, bits, dev, ensure_built, f64
+from workloads import (mixed_prefill, norm_weights, packed_qkv, qwen25_05b_decode, qwen3_06b_decode,
+                       tiny_f32)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    ensure_built()
+    import paged_kv_attention_22_amd as m
+    return m
+
+
+WORKLOADS = {
+    "qwen3_decode": lambda: qwen3_06b_decode(batch=24, prompt=(10, 300), gen=(0, 300)),
+    "qwen25_decode_g7": lambda: qwen25_05b_decode(batch=9, lo=1, hi=500),
+    "tiny_f32": tiny_f32,
+    "mixed": lambda: mixed_prefill(chunks=3, chunk_len=45, prior_hi=300, n_decode=7, dec_lo=1, dec_hi=900),
+    "mixed_d64": lambda: mixed_prefill(seed=12, chunks=2, chunk_len=33, prior_hi=100, n_decode=3, dec_lo=1,
+                                       dec_hi=200, num_q_heads=14, num_kv_heads=2, head_dim=64),
+}
+
+
+def as_bits(a):
+    """Stored values as raw bits (fp32 arrays viewed as uint32)."""
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+def as_values(a, dtype):
+    """Raw bits back to the stored type, for decoding to float64."""
+    return a.view(np.float32) if dtype == "f32" else a
+
+
+def tolerance(ref, pos, dtype):
+    """Bound on |GPU - fp64| for one rotated value: half a unit in the last
+    place of the stored type, plus the fp32 angle's rounding (pos * inv_freq
+    is rounded once, |error| <= pos * 2^-23 radians for inv_freq <= 1) times
+    the magnitude, plus fp32 arithmetic."""
+    mag = np.abs(ref).max(axis=-1, keepdims=True)
+    t = (np.asarray(pos, np.float64)[:, None, None] + 1) * 2.0 ** -22 * mag + 1e-5 * (mag + 1)
+    if dtype == "bf16":
+        t = t + 2.0 ** -8 * np.abs(ref)
+    return t
+
+
+def run_case(pa, b, theta, norms, pad_cols):
+    T = b.q.shape[0]
+    qsl = b.query_start_loc if b.num_prefill_seqs else None
+    x = packed_qkv(b, pad_cols=pad_cols)
+    qn, kn = norm_weights(b, 77) if norms else (None, None)
+    q_ref, kp_ref, vp_ref, slots_ref, k_rot = oracle.qkv_rope_write(
+        x, qsl, b.context_lens, b.block_tables, b.k_pool, b.v_pool, b.num_q_heads, b.num_kv_heads,
+        theta, b.dtype, q_norm=qn, k_norm=kn)
+    kp, vp = dev(b.k_pool), dev(b.v_pool)
+    so = torch.full((T,), -7, dtype=torch.int32, device="cuda")
+    q = pa.qkv_rope_write(dev(x), b.num_q_heads, dev(b.context_lens), dev(b.block_tables), kp, vp, theta,
+                          query_start_loc=None if qsl is None else dev(qsl),
+                          q_norm=None if qn is None else dev(qn), k_norm=None if kn is None else dev(kn),
+                          slot_mapping_out=so)
+    torch.cuda.synchronize()
+    return x, q, kp, vp, so, (q_ref, kp_ref, vp_ref, slots_ref, k_rot), qsl
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.parametrize("theta,norms,pad", [(1e6, True, 0), (1e4, False, 8)])
+def test_qkv_rope_write_matches_oracle(pa, name, theta, norms, pad):
+    b = WORKLOADS[name]()
+    print(f"[qkv] {name} theta={theta} norms={norms} pad={pad} T={b.q.shape[0]}", flush=True)
+    x, q, kp, vp, so, (q_ref, kp_ref, vp_ref, slots_ref, k_rot), qsl = run_case(pa, b, theta, norms, pad)
+    T, hkv, d = b.q.shape[0], b.num_kv_heads, b.head_dim
+    _, pos = oracle.token_positions(qsl, b.context_lens, T)
+    # slots: derived on the device, equal to the oracle's and to the generator's own layout
+    assert np.array_equal(so.cpu().numpy(), slots_ref.astype(np.int32))
+    assert np.array_equal(slots_ref, b.slot_mapping[:T].astype(np.int64))
+    # q
+    err = np.abs(f64(q) - q_ref)
+    assert (err <= tolerance(q_ref, pos, b.dtype)).all(), err.max()
+    # pools: written rows, then every other byte
+    krow, vrow = bits(kp).reshape(-1, hkv, d), bits(vp).reshape(-1, hkv, d)
+    kref, vref = as_bits(kp_ref).reshape(-1, hkv, d), as_bits(vp_ref).reshape(-1, hkv, d)
+    assert np.array_equal(vrow[slots_ref], vref[slots_ref])
+    kerr = np.abs(oracle.to_f64(as_values(krow[slots_ref], b.dtype), b.dtype) - k_rot)
+    assert (kerr <= tolerance(k_rot, pos, b.dtype)).all(), kerr.max()
+    mask = np.ones(krow.shape[0], bool)
+    mask[slots_ref] = False
+    assert np.array_equal(krow[mask], kref[mask])
+    assert np.array_equal(vrow[mask], vref[mask])
+
+
+def test_entries_outside_the_pool_are_not_written(pa):
+    b = mixed_prefill(seed=13, chunks=2, chunk_len=20, prior_hi=40, n_decode=4, dec_lo=1, dec_hi=60)
+    T = b.q.shape[0]
+    bt = b.block_tables.copy()
+    # the block holding the last token of sequence 1 now points past the pool
+    L1 = int(b.context_lens[1])
+    bt[1, (L1 - 1) // 16] = b.k_pool.shape[0] + 5
+    slots_ref = oracle.derive_slots(b.query_start_loc, b.context_lens, bt, T, b.k_pool.shape[0])
+    assert (slots_ref == -1).sum() >= 1
+    x = packed_qkv(b)
+    kp, vp = dev(b.k_pool), dev(b.v_pool)
+    so = torch.zeros(T, dtype=torch.int32, device="cuda")
+    q = pa.qkv_rope_write(dev(x), b.num_q_heads, dev(b.context_lens), dev(bt), kp, vp, 1e6,
+                          query_start_loc=dev(b.query_start_loc), slot_mapping_out=so)
+    torch.cuda.synchronize()
+    assert np.array_equal(so.cpu().numpy(), slots_ref.astype(np.int32))
+    q_ref, kp_ref, vp_ref, _, _ = oracle.qkv_rope_write(x, b.query_start_loc, b.context_lens, bt, b.k_pool,
+                                                         b.v_pool, b.num_q_heads, b.num_kv_heads, 1e6, b.dtype)
+    assert np.isfinite(f64(q)).all()
+    # rows the oracle leaves alone stay bit-identical (including every row of the skipped tokens)
+    hkv, d = b.num_kv_heads, b.head_dim
+    krow, vrow = bits(kp).reshape(-1, hkv, d), bits(vp).reshape(-1, hkv, d)
+    written = slots_ref[slots_ref >= 0]
+    mask = np.ones(krow.shape[0], bool)
+    mask[written] = False
+    assert np.array_equal(krow[mask], as_bits(kp_ref).reshape(-1, hkv, d)[mask])
+    assert np.array_equal(vrow, as_bits(vp_ref).reshape(-1, hkv, d))
+
+
+def test_fused_write_feeds_attention(pa):
+    """Fused write, then the attention calls on its q and pools, equals the
+    oracle's attention over the oracle's rotated q and written pools."""
+    for b in [qwen3_06b_decode(batch=16, prompt=(10, 200), gen=(0, 200)),
+              mixed_prefill(seed=14, chunks=2, chunk_len=40, prior_hi=120, n_decode=5, dec_lo=1, dec_hi=300)]:
+        x, q, kp, vp, so, (q_ref, kp_ref, vp_ref, slots_ref, _), qsl = run_case(pa, b, 1e6, True, 0)
+        q_ref_bits = oracle.to_stored(q_ref, b.dtype)
+        if qsl is None:
+            out = pa.decode(q, kp, vp, dev(b.block_tables), dev(b.context_lens), b.max_context_len,
+                            scale=b.scale)
+            ref = oracle.decode(q_ref_bits, kp_ref, vp_ref, b.block_tables, b.context_lens, b.scale, b.dtype)
+        else:
+            out = pa.prefill_chunk(q, dev(qsl), b.num_prefill_seqs, b.max_query_len, kp, vp,
+                                   dev(b.block_tables), dev(b.context_lens), b.max_context_len, scale=b.scale)
+            ref = oracle.attention(q_ref_bits, qsl, kp_ref, vp_ref, b.block_tables, b.context_lens, b.scale,
+                                   b.dtype)
+        torch.cuda.synchronize()
+        assert_close(f64(out), ref, b.dtype, f"{b.name} attention after the fused write")
