@@ -173,6 +173,69 @@ def bench_mixed(args, b, up, dev) -> dict:
     }
 
 
+def fused_write_bytes(b) -> int:
+    """Algorithmic bytes of pa_qkv_rope_write: each packed row read once, the
+    rotated q written, one K and one V row written per token, the two norm
+    weight vectors, and per token its slot out, its length and its table
+    entry."""
+    T = b.q.shape[0]
+    es = b.elem_bytes
+    hq, hkv, d = b.num_q_heads, b.num_kv_heads, b.head_dim
+    return T * ((hq + 2 * hkv) * d + hq * d + 2 * hkv * d) * es + 2 * d * es + 12 * T
+
+
+def bench_fused(args, b, up) -> dict:
+    """The fused QKV split + rotary + KV write on the workload's new tokens
+    (packed rows built from the batch's q and new K/V), alone and as the write
+    half of a decode step (fused write + pa_decode) beside the plain step
+    (pa_kv_write + pa_decode)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_attention_22_amd as pa
+    from workloads import norm_weights, packed_qkv
+    pools = [(up(b.k_pool), up(b.v_pool)) for _ in range(2)]
+    qkv = up(packed_qkv(b))
+    qn, kn = (up(w) for w in norm_weights(b, 77))
+    tables, lens = up(b.block_tables), up(b.context_lens)
+    qsl = up(b.query_start_loc) if b.num_prefill_seqs else None
+    q_out = torch.empty_like(up(b.q))
+    q, new_k, new_v, slots = up(b.q), up(b.new_k), up(b.new_v), up(b.slot_mapping)
+    out = torch.empty_like(q)
+    theta = 1e6
+
+    def fused(i):
+        kp, vp = pools[i & 1]
+        pa.qkv_rope_write(qkv, b.num_q_heads, lens, tables, kp, vp, theta, query_start_loc=qsl,
+                          q_norm=qn, k_norm=kn, q_out=q_out)
+
+    def fused_step(i):
+        kp, vp = pools[i & 1]
+        fused(i)
+        pa.decode(q_out, kp, vp, tables, lens, b.max_context_len, scale=b.scale, out=out)
+
+    def plain_step(i):
+        kp, vp = pools[i & 1]
+        pa.kv_write(new_k, new_v, slots, kp, vp)
+        pa.decode(q, kp, vp, tables, lens, b.max_context_len, scale=b.scale, out=out)
+
+    log(f"[bench] timing the fused write ({args.steps} calls)")
+    f_us = float(np.median(time_calls(fused, args.steps, args.warmup)))
+    res = {"metric": "pa_qkv_rope_write GB/s (fused QKV split + rotary + KV write)",
+           "value": round(fused_write_bytes(b) / (f_us * 1e-6) / 1e9, 1), "unit": "GB/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(f_us * 1e-3, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": b.dtype,
+           "data": "synthetic",
+           "config": {"workload": b.name, "tokens": int(b.q.shape[0]), "rope_theta": theta,
+                      "qk_norm": True, "bytes": fused_write_bytes(b)},
+           "fused_write_us": round(f_us, 2)}
+    if qsl is None:
+        res["decode_step_us"] = {
+            "fused_write_plus_decode": round(float(np.median(time_calls(fused_step, args.steps, args.warmup))), 2),
+            "kv_write_plus_decode": round(float(np.median(time_calls(plain_step, args.steps, args.warmup))), 2)}
+    return res
+
+
 def cpu_baseline(b, min_seconds: float = 10.0) -> dict:
     """The fp64 oracle on the same step (KV write + decode), one thread,
     repeated over the whole batch until at least min_seconds have passed."""
@@ -204,6 +267,9 @@ def main() -> int:
                     help="partition_tokens for pa_decode (0 = library choice, -1 = one pass)")
     ap.add_argument("--workload", default="qwen3_06b_decode",
                     help="generator preset (default: the Qwen3-0.6B batch-256 decode step)")
+    ap.add_argument("--op", default="step", choices=["step", "fused_write"],
+                    help="step: the workload's attention step (default); fused_write: "
+                         "pa_qkv_rope_write on the workload's new tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -248,6 +314,9 @@ def main() -> int:
             return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(x).to(dev)
 
+    if args.op == "fused_write":
+        print(json.dumps(bench_fused(args, b, up)), flush=True)
+        return 0
     if b.num_prefill_seqs:
         print(json.dumps(bench_mixed(args, b, up, dev)), flush=True)
         return 0

@@ -135,8 +135,9 @@ int32_t pa_kv_write(const void* k, const void* v,
  * written to the pools for that token (its q row is still written) and its
  * slot reads -1.
  * rope_theta        rotary base (> 0).  Rotate-half convention: dims i and
- *                   i + D/2 of every q and k head turn by pos * theta^(-2i/D),
- *                   computed in fp32 with precise sine and cosine.
+ *                   i + D/2 of every q and k head turn by pos * theta^(-2i/D);
+ *                   the angle is formed and reduced to within half a turn in
+ *                   fp64, its sine and cosine taken in fp32.
  * q_norm_weight, k_norm_weight
  *                   [head_dim] each, in the pool's element type, or NULL: with a
  *                   weight, each head is RMS-normalised (x / sqrt(mean(x^2) +

@@ -309,7 +309,7 @@ int32_t pa_qkv_rope_write(const void* qkv, int64_t qkv_token_stride,
     a.head_dim = pool.head_dim;
     a.num_blocks = pool.num_blocks;
     a.dtype = pool.dtype;
-    a.log2_theta = log2f(rope_theta);
+    a.log2_theta = log2((double)rope_theta);
     a.q_norm = q_norm_weight;
     a.k_norm = k_norm_weight;
     a.eps = norm_eps;

@@ -80,7 +80,7 @@ struct QkvArgs {
     const int32_t* block_tables;
     int32_t max_blocks;
     int32_t num_q_heads, num_kv_heads, head_dim, num_blocks, dtype;
-    float log2_theta;                   // log2 of the rotary base
+    double log2_theta;                  // log2 of the rotary base
     const void* q_norm;                 // [head_dim] or NULL (no norm)
     const void* k_norm;
     float eps;

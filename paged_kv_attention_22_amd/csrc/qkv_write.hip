@@ -14,8 +14,8 @@
 //     the table or the entry is outside the pool (nothing is written then);
 //   - q and k heads: optional per-head RMSNorm, then the rotate-half rotation:
 //     lane j of a head holds dims j and j + D/2 and turns them by
-//     pos * theta^(-2j/D) (fp32, precise sine and cosine); q goes to q_out, k to
-//     the pool row;
+//     pos * theta^(-2j/D) (angle formed and reduced in fp64, sine and cosine
+//     in fp32); q goes to q_out, k to the pool row;
 //   - v heads: copied unchanged, 16 bytes per lane.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
@@ -60,8 +60,37 @@ __device__ __forceinline__ int find_seq(const int32_t* qsl, int num_seqs, int t)
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void qkv_write_kernel(const QkvArgs a) {
     constexpr int HALF = D / 2;
-    constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+    constexpr int EPC = 16 / sizeof(T);   // elements per 16-byte chunk
+    constexpr int HPT = kThreads / HALF;  // rotated heads per pass
+    constexpr int KB = 8;                 // passes whose loads are in flight together
+    constexpr int VB = 2;                 // V chunks per thread loaded up front
     const int t = blockIdx.x;
+    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+    const int nh = Hq + Hkv;
+    const T* row = static_cast<const T*>(a.qkv) + (int64_t)t * a.qkv_stride;
+
+    // Everything the token's row provides is requested first: the first KB
+    // passes of rotated pairs and the first V chunks.  Thread tid always holds
+    // pair j = tid % HALF of heads tid / HALF + k * HPT (a wave covers whole
+    // heads, so the per-head norm is a reduction over HALF consecutive lanes).
+    const int j = threadIdx.x % HALF;
+    const int h0 = threadIdx.x / HALF;
+    // Every lane loads (heads past the last one re-read it, unused): loads
+    // without a branch around them are all in flight at once.
+    float x1[KB], x2[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+        const int head = min(h0 + k * HPT, nh - 1);
+        x1[k] = load_elem(row + head * D + j);
+        x2[k] = load_elem(row + head * D + j + HALF);
+    }
+    const T* vin = row + nh * D;
+    const int vchunks = Hkv * D / EPC;
+    uint4 vv[VB];
+#pragma unroll
+    for (int k = 0; k < VB; ++k) vv[k] = ld16(vin + min((int)threadIdx.x + k * kThreads, vchunks - 1) * EPC);
+
+    // Sequence, position and slot (scalar loads).
     int s, n, i;
     if (a.query_start_loc == nullptr) {
         s = t;
@@ -73,8 +102,7 @@ __global__ __launch_bounds__(kThreads) void qkv_write_kernel(const QkvArgs a) {
         n = a.query_start_loc[s + 1] - q0;
         i = t - q0;
     }
-    const int L = a.context_lens[s];
-    const int pos = L - n + i;
+    const int pos = a.context_lens[s] - n + i;
     int64_t slot = -1;
     if (pos >= 0 && pos < a.max_blocks * kBlock) {
         const int blk = a.block_tables[(int64_t)s * a.max_blocks + pos / kBlock];
@@ -82,8 +110,6 @@ __global__ __launch_bounds__(kThreads) void qkv_write_kernel(const QkvArgs a) {
     }
     if (threadIdx.x == 0 && a.slots_out != nullptr) a.slots_out[t] = (int32_t)slot;
 
-    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
-    const T* row = static_cast<const T*>(a.qkv) + (int64_t)t * a.qkv_stride;
     T* qo = static_cast<T*>(a.q_out) + (int64_t)t * Hq * D;
     const int64_t srow = slot >= 0 ? slot : 0;  // rows are only written when slot >= 0
     T* kp = static_cast<T*>(a.k_pool) + srow * Hkv * D;
@@ -91,43 +117,63 @@ __global__ __launch_bounds__(kThreads) void qkv_write_kernel(const QkvArgs a) {
     const T* qn = static_cast<const T*>(a.q_norm);
     const T* kn = static_cast<const T*>(a.k_norm);
 
-    // Rotated heads: item = head * HALF + j; a wave covers 64 / HALF whole heads,
-    // so the per-head norm is a reduction over HALF consecutive lanes.
-    const int items = (Hq + Hkv) * HALF;
-    for (int it = threadIdx.x; it - (int)(threadIdx.x & 63) < items; it += kThreads) {
-        const bool active = it < items;
-        const int head = active ? it / HALF : 0;
-        const int j = it % HALF;
-        const bool is_q = head < Hq;
-        float x1 = active ? load_elem(row + head * D + j) : 0.0f;
-        float x2 = active ? load_elem(row + head * D + j + HALF) : 0.0f;
-        const T* w = is_q ? qn : kn;
-        if (w != nullptr) {  // uniform across the head's lanes
-            const float ss = group_sum<HALF>(x1 * x1 + x2 * x2);
-            const float r = 1.0f / sqrtf(ss / D + a.eps);
-            x1 = x1 * r * load_elem(w + j);
-            x2 = x2 * r * load_elem(w + j + HALF);
+    // The rotation angle of pair j is the same for every head: one sine and
+    // cosine per thread.  The angle pos * theta^(-2j/D) is formed in fp64 and
+    // reduced to a fraction of a turn in [-1/2, 1/2] there, so the fp32 sine
+    // and cosine (the hardware ones, which take turns) see a small argument
+    // and no precision is lost to large positions.
+    const double turns = (double)pos * exp2(-(2.0 * j / D) * a.log2_theta) * 0.15915494309189535;
+    const float f = (float)(turns - rint(turns));
+    const float sn = __builtin_amdgcn_sinf(f);
+    const float cs = __builtin_amdgcn_cosf(f);
+    const T* qw = qn != nullptr ? qn : row;  // a valid address either way; unused without a norm
+    const T* kw = kn != nullptr ? kn : row;
+    const float wq1 = load_elem(qw + j), wq2 = load_elem(qw + j + HALF);
+    const float wk1 = load_elem(kw + j), wk2 = load_elem(kw + j + HALF);
+
+    for (int hb = 0; hb < nh; hb += HPT * KB) {
+        if (hb > 0) {  // later passes (many heads): load them the same way
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+                const int head = min(hb + h0 + k * HPT, nh - 1);
+                x1[k] = load_elem(row + head * D + j);
+                x2[k] = load_elem(row + head * D + j + HALF);
+            }
         }
-        const float inv_freq = exp2f(-(2.0f * j / D) * a.log2_theta);
-        float sn, cs;
-        sincosf((float)pos * inv_freq, &sn, &cs);
-        const float o1 = x1 * cs - x2 * sn;
-        const float o2 = x2 * cs + x1 * sn;
-        if (!active) continue;
-        if (is_q) {
-            store_elem(qo + head * D + j, o1);
-            store_elem(qo + head * D + j + HALF, o2);
-        } else if (slot >= 0) {
-            const int kh = head - Hq;
-            store_elem(kp + kh * D + j, o1);
-            store_elem(kp + kh * D + j + HALF, o2);
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int head = hb + h0 + k * HPT;  // the same for the HALF lanes of a head
+            if (head >= nh) continue;
+            const bool is_q = head < Hq;
+            float y1 = x1[k], y2 = x2[k];
+            if (is_q ? qn != nullptr : kn != nullptr) {
+                const float ss = group_sum<HALF>(y1 * y1 + y2 * y2);
+                const float r = 1.0f / sqrtf(ss / D + a.eps);
+                y1 *= r * (is_q ? wq1 : wk1);
+                y2 *= r * (is_q ? wq2 : wk2);
+            }
+            const float o1 = y1 * cs - y2 * sn;
+            const float o2 = y2 * cs + y1 * sn;
+            if (is_q) {
+                store_elem(qo + head * D + j, o1);
+                store_elem(qo + head * D + j + HALF, o2);
+            } else if (slot >= 0) {
+                const int kh = head - Hq;
+                store_elem(kp + kh * D + j, o1);
+                store_elem(kp + kh * D + j + HALF, o2);
+            }
         }
     }
 
     // V heads: bits copied unchanged.
     if (slot >= 0) {
-        const T* vin = row + (Hq + Hkv) * D;
-        for (int c = threadIdx.x; c < Hkv * D / EPC; c += kThreads) st16(vp + c * EPC, ld16(vin + c * EPC));
+#pragma unroll
+        for (int k = 0; k < VB; ++k) {
+            const int c = threadIdx.x + k * kThreads;
+            if (c < vchunks) st16(vp + c * EPC, vv[k]);
+        }
+        for (int c = threadIdx.x + VB * kThreads; c < vchunks; c += kThreads)
+            st16(vp + c * EPC, ld16(vin + c * EPC));
     }
 }
 
