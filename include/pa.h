@@ -69,7 +69,8 @@ typedef enum {
     PA_ERR_UNSUPPORTED = 4, /* valid but not built: block size, head_dim, group */
     PA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
     PA_ERR_LAUNCH = 6,      /* the HIP runtime rejected a launch */
-    PA_ERR_ALIGN = 7        /* a pointer or stride breaks 16-byte alignment */
+    PA_ERR_ALIGN = 7,       /* a pointer or stride breaks 16-byte alignment */
+    PA_ERR_CAPACITY = 8     /* block manager: not enough free blocks (nothing changed) */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
@@ -237,6 +238,66 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc,
                          int32_t num_q_heads, float scale, void* out,
                          int32_t partition_tokens,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Host-side block manager (no GPU involved): the block pool's free list, the
+ * per-sequence block tables that the attention calls read, and the prefix
+ * cache.  ("09 -- Mini Inference Engine (The Capstone)": the engine diagram's
+ * KV cache manager -- block pool with free list, prefix hash -> block ids,
+ * block tables per sequence; Week 4 -- a block is allocated when a sequence's
+ * last block fills and every block returns on completion; Week 5 -- rolling
+ * hash(previous block hash, block tokens) per full block, a global hash ->
+ * block map, shared prompt blocks, reference counts, a block freed only at
+ * count zero.)
+ *
+ * A manager owns num_blocks physical block ids of block_size tokens each
+ * (block_size 16 for the attention calls).  All calls are host calls and
+ * thread-safe (one lock per manager); each either succeeds or changes
+ * nothing.  Sequence ids are the caller's.
+ *
+ * pa_bm_add_sequence   a new sequence with its prompt.  With prefix caching,
+ *                      the prompt's leading full blocks whose exact token prefix
+ *                      is already cached (and computed) are shared instead of
+ *                      allocated; *num_cached_tokens (a multiple of block_size)
+ *                      tells how many prompt tokens need no recomputation.  If
+ *                      every prompt token would be cached, the last block is
+ *                      allocated privately and recomputed.  Blocks for the rest
+ *                      of the prompt come from the free list (least recently
+ *                      freed first).  PA_ERR_CAPACITY when they do not fit.
+ * pa_bm_append         adds tokens (generated ones) to a sequence, allocating a
+ *                      block whenever the last one fills; slots_out (or NULL)
+ *                      receives each new token's flat slot, block*block_size +
+ *                      offset, the pa_kv_write slot convention.
+ * pa_bm_mark_computed  the caller has written the K/V of the sequence's first
+ *                      num_computed_tokens tokens: full blocks among them enter
+ *                      the prefix cache (unless the same prefix is cached
+ *                      already).
+ * pa_bm_free_sequence  every block of the sequence loses one reference; a block
+ *                      at zero returns to the free list (last block first) and,
+ *                      if cached, stays findable until it is taken again.
+ * pa_bm_block_table    copies the sequence's block table (capacity entries at
+ *                      most) and its block and token counts.
+ * pa_bm_num_free_blocks blocks that can be allocated now (-1 for a NULL manager).
+ * pa_bm_stats          prompt blocks found in the cache / looked up, and the
+ *                      number of cache entries.
+ * pa_bm_block_refcount references to one block (-1 for a bad id).
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size, int32_t prefix_caching);
+void pa_bm_destroy(pa_block_manager* m);
+int32_t pa_bm_add_sequence(pa_block_manager* m, int64_t seq_id, const int32_t* tokens,
+                           int32_t num_tokens, int32_t* num_cached_tokens);
+int32_t pa_bm_append(pa_block_manager* m, int64_t seq_id, const int32_t* tokens,
+                     int32_t num_tokens, int32_t* slots_out);
+int32_t pa_bm_mark_computed(pa_block_manager* m, int64_t seq_id, int32_t num_computed_tokens);
+int32_t pa_bm_free_sequence(pa_block_manager* m, int64_t seq_id);
+int32_t pa_bm_block_table(pa_block_manager* m, int64_t seq_id, int32_t* table_out,
+                          int32_t capacity, int32_t* num_blocks_out, int32_t* num_tokens_out);
+int32_t pa_bm_num_free_blocks(pa_block_manager* m);
+int32_t pa_bm_stats(pa_block_manager* m, int64_t* hit_blocks, int64_t* queried_blocks,
+                    int32_t* cached_blocks);
+int32_t pa_bm_block_refcount(pa_block_manager* m, int32_t block_id);
 
 #ifdef __cplusplus
 }

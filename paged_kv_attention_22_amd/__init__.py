@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 BLOCK_SIZE = 16
 
 PA_OK, PA_F32, PA_BF16 = 0, 0, 1
+PA_ERR_SHAPE, PA_ERR_CAPACITY = 2, 8
 
 c_i32, c_i64, c_size, c_vp, c_f = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
                                   ctypes.c_void_p, ctypes.c_float)
@@ -48,6 +49,16 @@ _SIGNATURES = {
     "pa_qkv_rope_write": (c_i32, [c_vp, c_i64, c_vp, c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_f,
                                   c_vp, c_vp, c_f, c_vp, c_vp, c_vp, PoolDesc, c_vp, c_vp]),
     "pa_prefill_workspace_bytes": (c_size, [c_i32] * 8),
+    "pa_bm_create": (c_vp, [c_i32, c_i32, c_i32]),
+    "pa_bm_destroy": (None, [c_vp]),
+    "pa_bm_add_sequence": (c_i32, [c_vp, c_i64, c_vp, c_i32, c_vp]),
+    "pa_bm_append": (c_i32, [c_vp, c_i64, c_vp, c_i32, c_vp]),
+    "pa_bm_mark_computed": (c_i32, [c_vp, c_i64, c_i32]),
+    "pa_bm_free_sequence": (c_i32, [c_vp, c_i64]),
+    "pa_bm_block_table": (c_i32, [c_vp, c_i64, c_vp, c_i32, c_vp, c_vp]),
+    "pa_bm_num_free_blocks": (c_i32, [c_vp]),
+    "pa_bm_stats": (c_i32, [c_vp, c_vp, c_vp, c_vp]),
+    "pa_bm_block_refcount": (c_i32, [c_vp, c_i32]),
     "pa_prefill_chunk": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, PoolDesc,
                                  c_vp, c_i32, c_vp, c_i32, c_i32, c_f, c_vp, c_i32, c_vp,
                                  c_size, c_vp]),
@@ -229,3 +240,77 @@ def prefill_chunk(q, query_start_loc, num_prefill_seqs, max_query_len, k_pool, v
                                 int(partition_tokens), wp, wb, _stream(stream))
     _check(st, "pa_prefill_chunk")
     return out
+
+
+class BlockManager:
+    """Host-side block pool, block tables and prefix cache (pa_bm_* calls).
+
+    Token ids and slots travel as int32 numpy arrays; nothing here touches the
+    GPU.  The tables it hands out are what pa_decode / pa_prefill_chunk and
+    pa_qkv_rope_write read (after a copy to the device)."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16, prefix_caching: bool = True):
+        self._h = lib().pa_bm_create(int(num_blocks), int(block_size), int(bool(prefix_caching)))
+        if not self._h:
+            raise PAError(PA_ERR_SHAPE, "pa_bm_create")
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def close(self) -> None:
+        if self._h:
+            lib().pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _arr(tokens):
+        import numpy as np
+        a = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        return a, a.ctypes.data if a.size else 0
+
+    def add_sequence(self, seq_id: int, prompt) -> int:
+        """Register a sequence and its prompt; returns the prompt tokens found in the cache."""
+        a, p = self._arr(prompt)
+        cached = ctypes.c_int32(0)
+        _check(lib().pa_bm_add_sequence(self._h, int(seq_id), p, a.size, ctypes.byref(cached)),
+               "pa_bm_add_sequence")
+        return cached.value
+
+    def append(self, seq_id: int, tokens):
+        """Add tokens; returns their flat slots (int32 numpy array)."""
+        import numpy as np
+        a, p = self._arr(tokens)
+        slots = np.zeros(a.size, np.int32)
+        _check(lib().pa_bm_append(self._h, int(seq_id), p, a.size, slots.ctypes.data if a.size else 0),
+               "pa_bm_append")
+        return slots
+
+    def mark_computed(self, seq_id: int, num_tokens: int) -> None:
+        _check(lib().pa_bm_mark_computed(self._h, int(seq_id), int(num_tokens)), "pa_bm_mark_computed")
+
+    def free(self, seq_id: int) -> None:
+        _check(lib().pa_bm_free_sequence(self._h, int(seq_id)), "pa_bm_free_sequence")
+
+    def block_table(self, seq_id: int):
+        """(block ids as an int32 numpy array, number of tokens)."""
+        import numpy as np
+        nb, nt = ctypes.c_int32(0), ctypes.c_int32(0)
+        out = np.zeros(self.num_blocks, np.int32)
+        _check(lib().pa_bm_block_table(self._h, int(seq_id), out.ctypes.data, out.size,
+                                       ctypes.byref(nb), ctypes.byref(nt)), "pa_bm_block_table")
+        return out[:nb.value].copy(), nt.value
+
+    def num_free_blocks(self) -> int:
+        return lib().pa_bm_num_free_blocks(self._h)
+
+    def refcount(self, block_id: int) -> int:
+        return lib().pa_bm_block_refcount(self._h, int(block_id))
+
+    def stats(self) -> dict:
+        h, q, c = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int32(0)
+        _check(lib().pa_bm_stats(self._h, ctypes.byref(h), ctypes.byref(q), ctypes.byref(c)), "pa_bm_stats")
+        return {"hit_blocks": h.value, "queried_blocks": q.value, "cached_blocks": c.value}

@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build", "libpa")
 LIB = os.path.join(PKG, "libpa.so")
 
-SOURCES = ["kv_write.hip", "qkv_write.hip", "attn_rows.hip", "attn_chunks.hip", "pa_api.cpp"]
+SOURCES = ["kv_write.hip", "qkv_write.hip", "attn_rows.hip", "attn_chunks.hip", "pa_api.cpp",
+           "block_manager.cpp"]
 ARCH = "gfx950"
 
 

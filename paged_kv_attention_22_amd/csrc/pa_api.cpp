@@ -183,6 +183,7 @@ const char* pa_status_str(int32_t status) {
         case PA_ERR_WORKSPACE: return "workspace missing or too small";
         case PA_ERR_LAUNCH: return "kernel launch failed";
         case PA_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+        case PA_ERR_CAPACITY: return "not enough free blocks";
         default: return "unknown status";
     }
 }

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(pa):
 
 
 def test_status_strings(pa):
-    for code in range(8):
+    for code in range(9):
         assert pa.status_str(code) and pa.status_str(code) != "unknown status"
     assert pa.status_str(99) == "unknown status"
 
