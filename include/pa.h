@@ -43,8 +43,8 @@
  *     context_lens   int32 [num_seqs]; tokens attended, including the ones
  *                    written in this step (write first, then attend)
  * - Query head h attends with kv head h / (num_q_heads / num_kv_heads).
- * - q, out and the pools share one element type: bf16 (accumulation in fp32,
- *   output rounded to nearest even) or fp32.
+ * - q, out and the pools share one element type: bf16 or fp16 (accumulation in
+ *   fp32, output rounded to nearest even) or fp32.
  * - Device-side data is trusted for results but not for memory safety: slots
  *   outside [0, num_blocks*16) are skipped, block ids are clamped into
  *   [0, num_blocks), context lengths are clamped into [0, max_context_len] and
@@ -73,7 +73,7 @@ typedef enum {
     PA_ERR_CAPACITY = 8     /* block manager: not enough free blocks (nothing changed) */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
 
 /* Shape of one layer's K pool (the V pool has the same shape).
  * block_size must be 16; head_dim 64 or 128; dtype a pa_dtype. */

@@ -92,9 +92,11 @@ def derive_slots(query_start_loc, context_lens, block_tables, num_tokens, num_bl
 
 
 def to_stored(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Round float64 values to the stored element type: fp32 (nearest even),
-    or bf16 bit patterns (fp32 first, then the upper 16 bits with nearest-even
-    rounding of the lower 16)."""
+    """Round float64 values to the stored element type: fp32 or fp16 (nearest
+    even), or bf16 bit patterns (fp32 first, then the upper 16 bits with
+    nearest-even rounding of the lower 16)."""
+    if dtype == "f16":
+        return np.asarray(x, np.float64).astype(np.float16)   # nearest even
     f = np.asarray(x, np.float64).astype(np.float32)
     if dtype == "f32":
         return f

@@ -45,10 +45,12 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     """Exact decode of stored values to float64.
 
     bf16 arrives as uint16 bit patterns: placing them in the top half of an
-    fp32 word gives the same number exactly."""
+    fp32 word gives the same number exactly.  fp16 and fp32 widen exactly."""
     if dtype == "bf16":
         bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return bits.view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return np.asarray(a, dtype=np.float16).astype(np.float64)
     if dtype == "f32":
         return np.asarray(a, dtype=np.float32).astype(np.float64)
     if dtype == "f64":

@@ -21,7 +21,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 BLOCK_SIZE = 16
 
-PA_OK, PA_F32, PA_BF16 = 0, 0, 1
+PA_OK, PA_F32, PA_BF16, PA_F16 = 0, 0, 1, 2
 PA_ERR_SHAPE, PA_ERR_CAPACITY = 2, 8
 
 c_i32, c_i64, c_size, c_vp, c_f = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
@@ -95,9 +95,11 @@ def _check(status: int, what: str) -> None:
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return PA_BF16
+    if t.dtype == torch.float16:
+        return PA_F16
     if t.dtype == torch.float32:
         return PA_F32
-    raise TypeError(f"unsupported element type {t.dtype} (bf16 or fp32)")
+    raise TypeError(f"unsupported element type {t.dtype} (bf16, fp16 or fp32)")
 
 
 def _dev(t: torch.Tensor, name: str) -> int:

@@ -1,4 +1,4 @@
-// Matrix-core causal attention for prefill chunks (bf16, gfx950 MFMA).
+// Matrix-core causal attention for prefill chunks (bf16 or fp16, gfx950 MFMA).
 //
 // A chunk of n new query tokens of a sequence with context length L holds
 // rows (token t, head hh) of the kv head's GQA group, n*G rows in all; row
@@ -36,12 +36,32 @@
 namespace pa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+// Per 16-bit element type (uint16_t: bf16 bits, _Float16: fp16): the 8-wide
+// operand vector, the 16x16x32 product, and two probabilities packed with
+// the conversion instruction (nearest even).
+template <typename T>
+struct Mma;
+template <>
+struct Mma<uint16_t> {
+    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ floatx4 mfma(v8 a, v8 b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Mma<_Float16> {
+    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ floatx4 mfma(v8 a, v8 b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
@@ -64,11 +84,7 @@ constexpr int kSplitBelow = 256;
 constexpr int kRowsSmall = 16 * 1 * kRowWaves;
 constexpr int kRowsLarge = 16 * 2 * kRowWaves;
 
-__device__ __forceinline__ floatx4 mfma(bf16x8 a, bf16x8 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ uint2 ld_tr(const unsigned char* p) {
     const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p));
@@ -120,8 +136,11 @@ __device__ __forceinline__ uint4 ld16_at(const unsigned char* base, uint32_t off
     return make_uint4(x.x, x.y, x.z, x.w);
 }
 
-template <int D, int NT, int DEPTH, int KSPLIT>
+template <typename T, int D, int NT, int DEPTH, int KSPLIT>
 __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const ChunkArgs a) {
+    using V8 = typename Mma<T>::v8;
+    using V2 = typename Mma<T>::v2;
+    auto as_v8 = [](uint4 v) { return __builtin_bit_cast(V8, v); };
     constexpr int kNT = NT;
     constexpr int kRowsPerWave = 16 * NT;
     constexpr int kRowsPerGroup = kRowsPerWave * kRowWaves;
@@ -190,11 +209,11 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
     const const_i32* bt = (const const_i32*)(a.block_tables + (int64_t)s * a.max_blocks);
 
     const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
-    const uint16_t* q = static_cast<const uint16_t*>(a.q);
+    const T* q = static_cast<const T*>(a.q);
     // q rows: every lane loads (rows past the chunk read its last row and are
     // zeroed after), so the loads are issued together and waited for once.
     uint4 qraw[kNT][KS];
-    bf16x8 qf[kNT][KS];
+    V8 qf[kNT][KS];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
         const int R = min(wrow0 + nt * 16 + li, rows - 1);
@@ -305,7 +324,7 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                    for (int nt = 0; nt < kNT; ++nt) st[nt][mt] = mfma(as_bf16x8(kf[mt][ks]), qf[nt][ks], st[nt][mt]);
+                    for (int nt = 0; nt < kNT; ++nt) st[nt][mt] = Mma<T>::mfma(as_v8(kf[mt][ks]), qf[nt][ks], st[nt][mt]);
             // The V^T fragments of the second product do not depend on the
             // probabilities: reading them now overlaps the reads with the
             // softmax.
@@ -374,7 +393,7 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
                     const float p0 = fast_exp2(fmaf(sc[nt][2 * i], sl2, nmref));
                     const float p1 = fast_exp2(fmaf(sc[nt][2 * i + 1], sl2, nmref));
                     psum += p0 + p1;
-                    pk[nt][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){p0, p1}, bf16x2v));
+                    pk[nt][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){p0, p1}, V2));
                 }
                 lsum[nt] += psum;
             }
@@ -382,15 +401,15 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 // keys 32*kk .. 32*kk+31: slots 0-3 from st[.][2kk], 4-7 from st[.][2kk+1]
-                bf16x8 pb[kNT];
+                V8 pb[kNT];
 #pragma unroll
                 for (int nt = 0; nt < kNT; ++nt)
-                    pb[nt] = as_bf16x8(make_uint4(pk[nt][4 * kk], pk[nt][4 * kk + 1], pk[nt][4 * kk + 2], pk[nt][4 * kk + 3]));
+                    pb[nt] = as_v8(make_uint4(pk[nt][4 * kk], pk[nt][4 * kk + 1], pk[nt][4 * kk + 2], pk[nt][4 * kk + 3]));
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    const bf16x8 va = as_bf16x8(make_uint4(vlo[kk][mt].x, vlo[kk][mt].y, vhi[kk][mt].x, vhi[kk][mt].y));
+                    const V8 va = as_v8(make_uint4(vlo[kk][mt].x, vlo[kk][mt].y, vhi[kk][mt].x, vhi[kk][mt].y));
 #pragma unroll
-                    for (int nt = 0; nt < kNT; ++nt) acc[nt][mt] = mfma(va, pb[nt], acc[nt][mt]);
+                    for (int nt = 0; nt < kNT; ++nt) acc[nt][mt] = Mma<T>::mfma(va, pb[nt], acc[nt][mt]);
                 }
             }
         }
@@ -421,7 +440,7 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
                 v.y = __builtin_amdgcn_update_dpp(0u, v.y & keep, 0xE4, 0xf, 0xf, false);
                 v.z = __builtin_amdgcn_update_dpp(0u, v.z & keep, 0xE4, 0xf, 0xf, false);
                 v.w = __builtin_amdgcn_update_dpp(0u, v.w & keep, 0xE4, 0xf, 0xf, false);
-                qf[nt][ks] = as_bf16x8(v);
+                qf[nt][ks] = as_v8(v);
             }
         }
         store_tile(0, half * kKeys, tile0k, tile0v);
@@ -483,20 +502,31 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
         const float l = sum_across_row_lanes(lsum[nt]);
         if (!row_ok[nt]) continue;
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        uint16_t* out = static_cast<uint16_t*>(a.out) + ((int64_t)(qs + trow[nt]) * Hq + g * G + hh[nt]) * D + kg * 4;
+        T* out = static_cast<T*>(a.out) + ((int64_t)(qs + trow[nt]) * Hq + g * G + hh[nt]) * D + kg * 4;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const uint2 o = make_uint2(pack_bf16x2(acc[nt][mt][0] * inv, acc[nt][mt][1] * inv),
-                                       pack_bf16x2(acc[nt][mt][2] * inv, acc[nt][mt][3] * inv));
+            const uint2 o = make_uint2(pack16<T>(acc[nt][mt][0] * inv, acc[nt][mt][1] * inv),
+                                       pack16<T>(acc[nt][mt][2] * inv, acc[nt][mt][3] * inv));
             *reinterpret_cast<uint2*>(out + mt * 16) = o;
         }
+    }
+}
+
+template <typename T>
+void launch_typed(const ChunkArgs& a, bool small, dim3 grid, dim3 block, hipStream_t stream) {
+    if (a.head_dim == 128) {
+        if (small) hipLaunchKernelGGL((chunk_kernel<T, 128, 1, kDepth, 2>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((chunk_kernel<T, 128, 2, kDepth, 1>), grid, block, 0, stream, a);
+    } else {
+        if (small) hipLaunchKernelGGL((chunk_kernel<T, 64, 1, kDepth, 2>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((chunk_kernel<T, 64, 2, kDepth, 1>), grid, block, 0, stream, a);
     }
 }
 
 }  // namespace
 
 bool chunks_supported(int32_t dtype, int32_t head_dim, int32_t group) {
-    return dtype == PA_BF16 && (head_dim == 64 || head_dim == 128) && group >= 1 &&
+    return (dtype == PA_BF16 || dtype == PA_F16) && (head_dim == 64 || head_dim == 128) && group >= 1 &&
            group <= kMaxGroup;
 }
 
@@ -511,13 +541,8 @@ int32_t launch_chunks(const ChunkArgs& a, hipStream_t stream) {
     if (tiles > INT32_MAX || a.num_seqs > 65535) return PA_ERR_SHAPE;
     const dim3 grid((unsigned)tiles, a.num_kv_heads, a.num_seqs);
     const dim3 block(kRowWaves * (small ? 2 : 1) * 64);
-    if (a.head_dim == 128) {
-        if (small) hipLaunchKernelGGL((chunk_kernel<128, 1, kDepth, 2>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((chunk_kernel<128, 2, kDepth, 1>), grid, block, 0, stream, a);
-    } else {
-        if (small) hipLaunchKernelGGL((chunk_kernel<64, 1, kDepth, 2>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((chunk_kernel<64, 2, kDepth, 1>), grid, block, 0, stream, a);
-    }
+    if (a.dtype == PA_BF16) launch_typed<uint16_t>(a, small, grid, block, stream);
+    else launch_typed<_Float16>(a, small, grid, block, stream);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

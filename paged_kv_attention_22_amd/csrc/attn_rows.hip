@@ -37,9 +37,23 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
-__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
+// The 16x16x32 matrix-core product for each 16-bit element type.
+template <typename T>
+struct Mma;
+template <>
+struct Mma<uint16_t> {
+    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+    static __device__ __forceinline__ floatx4 mfma(v8 a, v8 b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Mma<_Float16> {
+    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+    static __device__ __forceinline__ floatx4 mfma(v8 a, v8 b, floatx4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
 
 // 16-lane transposing LDS read: lane i of each group of 16 receives element
 // i%4 of the 8-byte words addressed by lanes i/4 + 4k, k = 0..3.
@@ -54,17 +68,21 @@ struct Elem<uint16_t> {
     static constexpr int kPerChunk = 8;  // bf16 bit patterns
 };
 template <>
+struct Elem<_Float16> {
+    static constexpr int kPerChunk = 8;
+};
+template <>
 struct Elem<float> {
     static constexpr int kPerChunk = 4;
 };
 
 template <typename T>
 __device__ __forceinline__ float chunk_dot(const uint4& q, const uint4& k) {
-    if constexpr (std::is_same_v<T, uint16_t>) {
-        float s = dot2_bf16(q.x, k.x, 0.0f);
-        s = dot2_bf16(q.y, k.y, s);
-        s = dot2_bf16(q.z, k.z, s);
-        return dot2_bf16(q.w, k.w, s);
+    if constexpr (kIs16<T>) {
+        float s = dot16<T>(q.x, k.x, 0.0f);
+        s = dot16<T>(q.y, k.y, s);
+        s = dot16<T>(q.z, k.z, s);
+        return dot16<T>(q.w, k.w, s);
     } else {
         float s = __uint_as_float(q.x) * __uint_as_float(k.x);
         s = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), s);
@@ -75,11 +93,11 @@ __device__ __forceinline__ float chunk_dot(const uint4& q, const uint4& k) {
 
 template <typename T>
 __device__ __forceinline__ void unpack(const uint4& c, float* v) {
-    if constexpr (std::is_same_v<T, uint16_t>) {
-        v[0] = bf_lo(c.x); v[1] = bf_hi(c.x);
-        v[2] = bf_lo(c.y); v[3] = bf_hi(c.y);
-        v[4] = bf_lo(c.z); v[5] = bf_hi(c.z);
-        v[6] = bf_lo(c.w); v[7] = bf_hi(c.w);
+    if constexpr (kIs16<T>) {
+        v[0] = lo16<T>(c.x); v[1] = hi16<T>(c.x);
+        v[2] = lo16<T>(c.y); v[3] = hi16<T>(c.y);
+        v[4] = lo16<T>(c.z); v[5] = hi16<T>(c.z);
+        v[6] = lo16<T>(c.w); v[7] = hi16<T>(c.w);
     } else {
         v[0] = __uint_as_float(c.x); v[1] = __uint_as_float(c.y);
         v[2] = __uint_as_float(c.z); v[3] = __uint_as_float(c.w);
@@ -89,9 +107,9 @@ __device__ __forceinline__ void unpack(const uint4& c, float* v) {
 // Store E fp32 values (already normalised) as one 16-byte chunk of T.
 template <typename T>
 __device__ __forceinline__ void store_chunk(T* dst, const float* o) {
-    if constexpr (std::is_same_v<T, uint16_t>) {
-        st16(dst, make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
-                             pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])));
+    if constexpr (kIs16<T>) {
+        st16(dst, make_uint4(pack16<T>(o[0], o[1]), pack16<T>(o[2], o[3]),
+                             pack16<T>(o[4], o[5]), pack16<T>(o[6], o[7])));
     } else {
         st16(dst, make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]),
                              __float_as_uint(o[2]), __float_as_uint(o[3])));
@@ -424,8 +442,9 @@ __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
 //                    ds_read_b64_tr_b16 from the wave's own row-major V tile in
 //                    LDS (written with 16-byte stores; no barrier needed, the
 //                    tile is private to the wave).
-template <int D, int G>
+template <typename T, int D, int G>
 __global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a) {
+    using V8 = typename Mma<T>::v8;
     constexpr int KS = D / 32;                // 32-dim slices (first product)
     constexpr int MT = D / 16;                // 16-dim output tiles (second product)
     constexpr int CPR = D / 8;                // 16-byte chunks per token row
@@ -453,13 +472,13 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a
 
     const int Lraw = a.context_lens[it.seq];
     const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
-    bf16x8 qf[KS];
+    V8 qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         uint4 v = make_uint4(0, 0, 0, 0);
         if (li < G)
-            v = ld16(static_cast<const uint16_t*>(a.q) + ((int64_t)it.row * Hq + g * G + li) * D + ks * 32 + kg * 8);
-        qf[ks] = __builtin_bit_cast(bf16x8, v);
+            v = ld16(static_cast<const T*>(a.q) + ((int64_t)it.row * Hq + g * G + li) * D + ks * 32 + kg * 8);
+        qf[ks] = __builtin_bit_cast(V8, v);
     }
     // Block ids: lane i holds the id of block (b0 + 2*(wave + (kbase + i/2)*kWaves) + i%2).
     const int32_t* bt = a.block_tables + (int64_t)it.seq * a.max_blocks;
@@ -493,8 +512,8 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a
     };
 
     const int64_t tok_stride = (int64_t)Hkv * D;
-    const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool) + (int64_t)g * D;
-    const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool) + (int64_t)g * D;
+    const T* kpool = static_cast<const T*>(a.k_pool) + (int64_t)g * D;
+    const T* vpool = static_cast<const T*>(a.v_pool) + (int64_t)g * D;
     unsigned char* vt = s_v + wave * VT;
     const float sl2 = a.scale * kLog2e;
 
@@ -536,7 +555,7 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a
         for (int mt = 0; mt < 2; ++mt) {
             floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) c = mfma16(__builtin_bit_cast(bf16x8, kf[mt][ks]), qf[ks], c);
+            for (int ks = 0; ks < KS; ++ks) c = Mma<T>::mfma(__builtin_bit_cast(V8, kf[mt][ks]), qf[ks], c);
             st[mt] = c;
         }
         float sc[8];
@@ -563,19 +582,20 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a
         uint32_t pk[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const __bf16 lo = static_cast<__bf16>(fast_exp2(sc[2 * i] - mref));
-            const __bf16 hi = static_cast<__bf16>(fast_exp2(sc[2 * i + 1] - mref));
-            lsum += static_cast<float>(lo) + static_cast<float>(hi);
-            pk[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+            // the sum takes the probabilities as rounded for the product
+            const uint32_t lo = to16<T>(fast_exp2(sc[2 * i] - mref));
+            const uint32_t hi = to16<T>(fast_exp2(sc[2 * i + 1] - mref));
+            lsum += lo16<T>(lo) + lo16<T>(hi);
+            pk[i] = lo | (hi << 16);
         }
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+        const V8 pb = __builtin_bit_cast(V8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
         __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's V tile is in LDS
         const unsigned char* v0 = vt + (4 * kg + ((lane >> 2) & 3)) * VROW + (lane & 3) * 8;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const uint2 lo = ld_tr16(v0 + mt * 32);
             const uint2 hi = ld_tr16(v0 + 16 * VROW + mt * 32);
-            acc[mt] = mfma16(__builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, acc[mt]);
+            acc[mt] = Mma<T>::mfma(__builtin_bit_cast(V8, make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, acc[mt]);
         }
     };
 
@@ -610,7 +630,7 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a
         }
     }
     __syncthreads();
-    combine_waves<uint16_t, D, G>(a, it, z, g, part, final_out, s_acc, s_m, s_l);
+    combine_waves<T, D, G>(a, it, z, g, part, final_out, s_acc, s_m, s_l);
 }
 
 // Log-sum-exp merge of the partitions of one (row, q head):
@@ -671,8 +691,8 @@ __global__ __launch_bounds__(64) void merge_kernel(const RowsArgs a, int group) 
     o0 *= inv;
     o1 *= inv;
     T* dst = static_cast<T*>(a.out) + ((int64_t)it.row * Hq + hq) * D + d;
-    if constexpr (std::is_same_v<T, uint16_t>) {
-        *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(o0, o1);
+    if constexpr (kIs16<T>) {
+        *reinterpret_cast<uint32_t*>(dst) = pack16<T>(o0, o1);
     } else {
         *reinterpret_cast<float2*>(dst) = make_float2(o0, o1);
     }
@@ -748,8 +768,8 @@ int32_t launch_typed(const RowsArgs& a, hipStream_t stream) {
     const bool split = a.part_tokens > 0;
     const int64_t units = (int64_t)a.num_items * a.num_kv_heads * (split ? a.nparts : 1);
     if (units > INT32_MAX) return PA_ERR_SHAPE;
-    if constexpr (std::is_same_v<T, uint16_t> && G >= kMfmaMinGroup)
-        hipLaunchKernelGGL((mfma_rows_kernel<D, G>), dim3((unsigned)units), dim3(kWaves * 64), 0, stream, a);
+    if constexpr (kIs16<T> && G >= kMfmaMinGroup)
+        hipLaunchKernelGGL((mfma_rows_kernel<T, D, G>), dim3((unsigned)units), dim3(kWaves * 64), 0, stream, a);
     else
         hipLaunchKernelGGL((rows_kernel<T, D, G>), dim3((unsigned)units), dim3(kWaves * 64), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
@@ -794,6 +814,9 @@ int32_t launch_rows(const RowsArgs& a, hipStream_t stream) {
     if (a.dtype == PA_BF16) {
         if (a.head_dim == 64) return launch_group<uint16_t, 64>(a, group, stream);
         if (a.head_dim == 128) return launch_group<uint16_t, 128>(a, group, stream);
+    } else if (a.dtype == PA_F16) {
+        if (a.head_dim == 64) return launch_group<_Float16, 64>(a, group, stream);
+        if (a.head_dim == 128) return launch_group<_Float16, 128>(a, group, stream);
     } else if (a.dtype == PA_F32) {
         if (a.head_dim == 64) return launch_group<float, 64>(a, group, stream);
         if (a.head_dim == 128) return launch_group<float, 128>(a, group, stream);

@@ -50,7 +50,7 @@ AuxStream* aux_for(hipStream_t s) {
 }
 
 int elem_size(int32_t dtype) {
-    if (dtype == PA_BF16) return 2;
+    if (dtype == PA_BF16 || dtype == PA_F16) return 2;
     if (dtype == PA_F32) return 4;
     return 0;
 }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pa {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -23,10 +25,49 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return bf16_rne(lo) | (bf16_rne(hi) << 16);
 }
 
+// fp16 halves of a 32-bit word -> fp32 (exact), and fp32 -> fp16 bits with the
+// conversion instruction's round-to-nearest-even.
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float h_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)w); }
+__device__ __forceinline__ float h_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+__device__ __forceinline__ uint32_t f16_rne(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) { return f16_rne(lo) | (f16_rne(hi) << 16); }
+
+// 2-wide fp16 dot product accumulated into fp32 (v_dot2_f32_f16).
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b), c, false);
+}
+
 // 2-wide bf16 dot product accumulated into fp32 (v_dot2c_f32_bf16).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
                                            __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// 16-bit element types: uint16_t carries bf16 bit patterns, _Float16 carries
+// fp16.  These pick the conversions and the dot product per type.
+template <typename T>
+inline constexpr bool kIs16 = std::is_same_v<T, uint16_t> || std::is_same_v<T, _Float16>;
+template <typename T>
+__device__ __forceinline__ float lo16(uint32_t w) {
+    if constexpr (std::is_same_v<T, uint16_t>) return bf_lo(w); else return h_lo(w);
+}
+template <typename T>
+__device__ __forceinline__ float hi16(uint32_t w) {
+    if constexpr (std::is_same_v<T, uint16_t>) return bf_hi(w); else return h_hi(w);
+}
+template <typename T>
+__device__ __forceinline__ uint32_t to16(float f) {  // rounded bits (conversion instruction, nearest even)
+    if constexpr (std::is_same_v<T, uint16_t>) return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+    else return f16_rne(f);
+}
+template <typename T>
+__device__ __forceinline__ uint32_t pack16(float lo, float hi) {
+    if constexpr (std::is_same_v<T, uint16_t>) return pack_bf16x2(lo, hi); else return pack_f16x2(lo, hi);
+}
+template <typename T>
+__device__ __forceinline__ float dot16(uint32_t a, uint32_t b, float c) {
+    if constexpr (std::is_same_v<T, uint16_t>) return dot2_bf16(a, b, c); else return dot2_f16(a, b, c);
 }
 
 template <int CTRL>

@@ -25,16 +25,17 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// T: uint16_t (bf16 bits), _Float16 or float.
 template <typename T>
 __device__ __forceinline__ float load_elem(const T* p) {
     if constexpr (std::is_same_v<T, uint16_t>) return bf_lo(*p);
-    else return *p;
+    else return (float)*p;
 }
 
 template <typename T>
 __device__ __forceinline__ void store_elem(T* p, float x) {
     if constexpr (std::is_same_v<T, uint16_t>) *p = (uint16_t)bf16_rne(x);
-    else *p = x;
+    else *p = (T)x;
 }
 
 // Last s in [0, num_seqs) with qsl[s] <= t (qsl is non-decreasing, qsl[0] = 0).
@@ -185,6 +186,9 @@ int32_t launch_qkv_write(const QkvArgs& a, hipStream_t stream) {
     if (a.dtype == PA_BF16) {
         if (a.head_dim == 128) hipLaunchKernelGGL((qkv_write_kernel<uint16_t, 128>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((qkv_write_kernel<uint16_t, 64>), grid, block, 0, stream, a);
+    } else if (a.dtype == PA_F16) {
+        if (a.head_dim == 128) hipLaunchKernelGGL((qkv_write_kernel<_Float16, 128>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((qkv_write_kernel<_Float16, 64>), grid, block, 0, stream, a);
     } else {
         if (a.head_dim == 128) hipLaunchKernelGGL((qkv_write_kernel<float, 128>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((qkv_write_kernel<float, 64>), grid, block, 0, stream, a);

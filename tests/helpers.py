@@ -34,7 +34,7 @@ def dev(x: np.ndarray, device="cuda") -> torch.Tensor:
 def bits(t: torch.Tensor) -> np.ndarray:
     """Raw bit patterns of a device tensor as numpy (uint16 / uint32)."""
     t = t.detach().contiguous().cpu()
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.float32:
         return t.view(torch.int32).numpy().view(np.uint32)

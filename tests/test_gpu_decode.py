@@ -41,6 +41,11 @@ WORKLOADS = {
     "g5_d128_f32": lambda: make_batch(63, name="g5_d128_f32", dtype="f32", num_q_heads=10,
                                       num_kv_heads=2, head_dim=128,
                                       draw_lens=lambda rng: rng.integers(1, 300, size=6)),
+    # fp16 pools: the vector path (G = 2) and the matrix-core path (G = 7, G = 4)
+    "qwen3_f16": lambda: qwen3_06b_decode(batch=40, prompt=(1, 600), gen=(0, 400), dtype="f16"),
+    "qwen25_f16": lambda: qwen25_05b_decode(batch=17, lo=1, hi=900, dtype="f16"),
+    "g4_d128_f16": lambda: make_batch(64, name="g4_d128_f16", dtype="f16", num_q_heads=16, num_kv_heads=4,
+                                      head_dim=128, draw_lens=lambda rng: rng.integers(1, 700, size=21)),
 }
 
 _cache = {}

@@ -24,6 +24,8 @@ CASES = {
     "qwen3_full": qwen3_06b_decode,
     "mixed_full": mixed_prefill,
     "long_small": lambda: long_context(batch=4, ctx=1000, shared_blocks=20),
+    "qwen3_f16": lambda: qwen3_06b_decode(batch=30, prompt=(1, 300), gen=(0, 100), dtype="f16"),
+    "mixed_f16": lambda: mixed_prefill(chunks=2, chunk_len=50, prior_hi=100, n_decode=6, dtype="f16"),
 }
 
 

@@ -38,6 +38,11 @@ WORKLOADS = {
     "mixed_d64_large": lambda: mixed_prefill(seed=11, chunks=8, chunk_len=300, prior_hi=700, n_decode=16,
                                              dec_lo=1, dec_hi=1200, num_q_heads=14, num_kv_heads=2,
                                              head_dim=64),
+    # fp16 pools in both launch shapes of the chunk kernel
+    "mixed_f16_small": lambda: mixed_prefill(seed=15, chunks=3, chunk_len=60, prior_hi=250, n_decode=6,
+                                             dec_lo=1, dec_hi=500, dtype="f16"),
+    "mixed_f16_large": lambda: mixed_prefill(seed=16, chunks=4, chunk_len=300, prior_hi=600, n_decode=10,
+                                             dec_lo=1, dec_hi=900, dtype="f16"),
     # chunks on both paths in one batch: 3, 7 and 1 rows give fewer than 16
     # (row, head) pairs per kv head at G = 2 (vector path), 40 and 64 do not
     "mixed_ragged_chunks": lambda: mixed_prefill(seed=8, chunk_lens=[3, 40, 7, 1, 64], prior_hi=300,

@@ -29,17 +29,22 @@ WORKLOADS = {
     "mixed": lambda: mixed_prefill(chunks=3, chunk_len=45, prior_hi=300, n_decode=7, dec_lo=1, dec_hi=900),
     "mixed_d64": lambda: mixed_prefill(seed=12, chunks=2, chunk_len=33, prior_hi=100, n_decode=3, dec_lo=1,
                                        dec_hi=200, num_q_heads=14, num_kv_heads=2, head_dim=64),
+    "qwen3_f16": lambda: qwen3_06b_decode(batch=20, prompt=(10, 300), gen=(0, 300), dtype="f16"),
 }
 
 
 def as_bits(a):
-    """Stored values as raw bits (fp32 arrays viewed as uint32)."""
-    return a.view(np.uint32) if a.dtype == np.float32 else a
+    """Stored values as raw bits (fp32 arrays viewed as uint32, fp16 as uint16)."""
+    if a.dtype == np.float32:
+        return a.view(np.uint32)
+    return a.view(np.uint16) if a.dtype == np.float16 else a
 
 
 def as_values(a, dtype):
     """Raw bits back to the stored type, for decoding to float64."""
-    return a.view(np.float32) if dtype == "f32" else a
+    if dtype == "f32":
+        return a.view(np.float32)
+    return a.view(np.float16) if dtype == "f16" else a
 
 
 def tolerance(ref, pos, dtype):
@@ -51,6 +56,8 @@ def tolerance(ref, pos, dtype):
     t = (np.asarray(pos, np.float64)[:, None, None] + 1) * 2.0 ** -22 * mag + 1e-5 * (mag + 1)
     if dtype == "bf16":
         t = t + 2.0 ** -8 * np.abs(ref)
+    elif dtype == "f16":
+        t = t + 2.0 ** -11 * np.abs(ref) + 2.0 ** -25    # half a unit (and subnormal spacing)
     return t
 
 

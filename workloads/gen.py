@@ -40,6 +40,7 @@ import numpy as np
 
 BLOCK = 16
 BF16_NAN = np.uint16(0x7FC0)
+F16_NAN = np.uint16(0x7E00).view(np.float16)
 F32_NAN_BITS = np.uint32(0x7FC00000)
 
 
@@ -58,7 +59,7 @@ class PagedBatch:
 
     name: str
     seed: int
-    dtype: str                    # "bf16" or "f32"
+    dtype: str                    # "bf16" (uint16 bit patterns), "f16" or "f32"
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
@@ -105,7 +106,7 @@ class PagedBatch:
 
     @property
     def elem_bytes(self) -> int:
-        return 2 if self.dtype == "bf16" else 4
+        return 4 if self.dtype == "f32" else 2
 
     def used_block_ids(self) -> np.ndarray:
         """Physical ids referenced by some sequence within its length."""
@@ -115,11 +116,15 @@ class PagedBatch:
 
 def _values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
     x = rng.standard_normal(size=shape, dtype=np.float32)
-    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    return x.astype(np.float16) if dtype == "f16" else x    # fp32 -> fp16 rounds to nearest even
 
 
 def _poison_value(dtype: str):
-    return BF16_NAN if dtype == "bf16" else F32_NAN_BITS.view(np.float32)
+    if dtype == "bf16":
+        return BF16_NAN
+    return F16_NAN if dtype == "f16" else F32_NAN_BITS.view(np.float32)
 
 
 def make_batch(
@@ -150,7 +155,7 @@ def make_batch(
     same physical blocks (read-only aliasing, as a prefix-cache hit produces).
     ``pad_slots``: extra new tokens with slot -1 appended to the write.
     """
-    assert dtype in ("bf16", "f32")
+    assert dtype in ("bf16", "f16", "f32")
     rng = np.random.default_rng(seed)
     lens = np.asarray(draw_lens(rng), dtype=np.int64)
     S = int(lens.shape[0])
@@ -245,7 +250,7 @@ def norm_weights(b: PagedBatch, seed: int):
     stored like the batch (drawn from their own generator)."""
     rng = np.random.default_rng(seed)
     w = (1.0 + 0.1 * rng.standard_normal(size=(2, b.head_dim))).astype(np.float32)
-    w = f32_to_bf16_bits(w) if b.dtype == "bf16" else w
+    w = f32_to_bf16_bits(w) if b.dtype == "bf16" else (w.astype(np.float16) if b.dtype == "f16" else w)
     return w[0].copy(), w[1].copy()
 
 
@@ -264,18 +269,19 @@ def tiny_f32(seed: int = 1) -> PagedBatch:
         recipe="lens {5,17,33,64}; pool 32 blocks; N(0,1) fp32")
 
 
-def qwen25_05b_decode(seed: int = 2, batch: int = 32, lo: int = 128, hi: int = 1024) -> PagedBatch:
+def qwen25_05b_decode(seed: int = 2, batch: int = 32, lo: int = 128, hi: int = 1024,
+                      dtype: str = "bf16") -> PagedBatch:
     """Qwen2.5-0.5B-shaped decode step: 14 q / 2 kv heads, dim 64, bf16,
     lengths uniform in [lo, hi]; pool 1.2x the blocks in use."""
     return make_batch(
-        seed, name="qwen25_05b_decode", dtype="bf16", num_q_heads=14,
+        seed, name="qwen25_05b_decode", dtype=dtype, num_q_heads=14,
         num_kv_heads=2, head_dim=64,
         draw_lens=lambda rng: rng.integers(lo, hi + 1, size=batch),
         recipe=f"B={batch}, L~U[{lo},{hi}], pool 1.2x, N(0,1)->bf16")
 
 
 def qwen3_06b_decode(seed: int = 3, batch: int = 256, prompt=(100, 1024),
-                     gen=(0, 1024), cap: int = 2048) -> PagedBatch:
+                     gen=(0, 1024), cap: int = 2048, dtype: str = "bf16") -> PagedBatch:
     """Qwen3-0.6B-shaped decode step: 16 q / 8 kv heads, dim 128, bf16,
     length = prompt U[100,1024] + generated U[0,1024], capped at 2048; pool
     1.2x the blocks in use with permuted ids."""
@@ -284,7 +290,7 @@ def qwen3_06b_decode(seed: int = 3, batch: int = 256, prompt=(100, 1024),
         g = rng.integers(gen[0], gen[1] + 1, size=batch)
         return np.minimum(p + g, cap)
     return make_batch(
-        seed, name="qwen3_06b_decode", dtype="bf16", num_q_heads=16,
+        seed, name="qwen3_06b_decode", dtype=dtype, num_q_heads=16,
         num_kv_heads=8, head_dim=128, draw_lens=lens,
         recipe=f"B={batch}, L=min(U{list(prompt)}+U{list(gen)},{cap}), pool 1.2x, N(0,1)->bf16")
 
@@ -293,7 +299,7 @@ def mixed_prefill(seed: int = 4, chunks: int = 4, chunk_len: int = 512,
                   prior_hi: int = 1536, n_decode: int = 192,
                   dec_lo: int = 256, dec_hi: int = 2048, num_q_heads: int = 16,
                   num_kv_heads: int = 8, head_dim: int = 128,
-                  chunk_lens=None) -> PagedBatch:
+                  chunk_lens=None, dtype: str = "bf16") -> PagedBatch:
     """Mixed chunked-prefill batch, by default the Qwen3-0.6B head shape (16 / 8 / 128, bf16):
     ``chunks`` prefill chunks of ``chunk_len`` new tokens (or the lengths listed
     in ``chunk_lens``) after a cached prior context U[0, prior_hi], followed by
@@ -313,7 +319,7 @@ def mixed_prefill(seed: int = 4, chunks: int = 4, chunk_len: int = 512,
     def qlens(rng, L):
         return np.concatenate([new_tokens, np.ones(n_decode, np.int64)])
     return make_batch(
-        seed, name="mixed_prefill", dtype="bf16", num_q_heads=num_q_heads,
+        seed, name="mixed_prefill", dtype=dtype, num_q_heads=num_q_heads,
         num_kv_heads=num_kv_heads, head_dim=head_dim, draw_lens=lens, draw_query_lens=qlens,
         num_prefill_seqs=chunks,
         recipe=(f"{chunks} chunks x {[int(x) for x in new_tokens] if chunk_lens is not None else chunk_len} "
