@@ -33,7 +33,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .ref import BLOCK_SIZE, to_f64
+from .ref import BLOCK_SIZE, to_f64  # noqa: F401  (BLOCK_SIZE: the default block size)
 
 
 def rms_norm(x: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
@@ -74,20 +74,21 @@ def token_positions(query_start_loc, context_lens, num_tokens):
     return seq, pos
 
 
-def derive_slots(query_start_loc, context_lens, block_tables, num_tokens, num_blocks):
-    """Flat pool slot of every token: table[seq][pos // 16] * 16 + pos % 16.
-    A position outside the table, or a table entry outside the pool, gives -1
-    (nothing is written for that token)."""
+def derive_slots(query_start_loc, context_lens, block_tables, num_tokens, num_blocks,
+                 block_size=BLOCK_SIZE):
+    """Flat pool slot of every token: table[seq][pos // B] * B + pos % B for
+    B-token blocks.  A position outside the table, or a table entry outside
+    the pool, gives -1 (nothing is written for that token)."""
     seq, pos = token_positions(query_start_loc, context_lens, num_tokens)
     slots = np.full(num_tokens, -1, np.int64)
     width = block_tables.shape[1]
     for t in range(num_tokens):
         p = int(pos[t])
-        if p < 0 or p >= width * BLOCK_SIZE:
+        if p < 0 or p >= width * block_size:
             continue
-        blk = int(block_tables[seq[t], p // BLOCK_SIZE])
+        blk = int(block_tables[seq[t], p // block_size])
         if 0 <= blk < num_blocks:
-            slots[t] = blk * BLOCK_SIZE + p % BLOCK_SIZE
+            slots[t] = blk * block_size + p % block_size
     return slots
 
 
@@ -133,7 +134,7 @@ def qkv_rope_write(qkv, query_start_loc, context_lens, block_tables, k_pool, v_p
     _, pos = token_positions(query_start_loc, context_lens, T)
     q_out = rope(q, pos, theta)
     k_rot = rope(k, pos, theta)
-    slots = derive_slots(query_start_loc, context_lens, block_tables, T, k_pool.shape[0])
+    slots = derive_slots(query_start_loc, context_lens, block_tables, T, k_pool.shape[0], k_pool.shape[1])
     kp, vp = k_pool.copy(), v_pool.copy()
     krow, vrow = kp.reshape(-1, hkv, d), vp.reshape(-1, hkv, d)
     k_store = to_stored(k_rot, dtype)

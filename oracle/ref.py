@@ -61,23 +61,27 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
 def kv_write(k_pool, v_pool, new_k, new_v, slot_mapping):
     """Return copies of the pools with each new token's K/V rows stored.
 
-    Token t goes to block slot // 16, offset slot % 16; slot < 0 is skipped.
-    Bits are copied unchanged (no arithmetic)."""
+    Token t goes to block slot // B, offset slot % B for a pool of B-token
+    blocks (B = 16 unless the pool says otherwise); slot < 0 is skipped.  Bits
+    are copied unchanged (no arithmetic)."""
     k_out = np.array(k_pool, copy=True)
     v_out = np.array(v_pool, copy=True)
+    bsz = k_pool.shape[1]
     for t, slot in enumerate(np.asarray(slot_mapping).tolist()):
         if slot < 0:
             continue
-        block, offset = divmod(slot, BLOCK_SIZE)
+        block, offset = divmod(slot, bsz)
         k_out[block, offset] = new_k[t]
         v_out[block, offset] = new_v[t]
     return k_out, v_out
 
 
 def gather(pool, table_row, n_tokens):
-    """Logical token j of a sequence lives at pool[table_row[j // 16], j % 16]."""
-    phys = [int(table_row[j // BLOCK_SIZE]) for j in range(n_tokens)]
-    offs = [j % BLOCK_SIZE for j in range(n_tokens)]
+    """Logical token j of a sequence lives at pool[table_row[j // B], j % B],
+    B the pool's block size (16 by default)."""
+    bsz = pool.shape[1]
+    phys = [int(table_row[j // bsz]) for j in range(n_tokens)]
+    offs = [j % bsz for j in range(n_tokens)]
     return pool[phys, offs] if n_tokens else pool[:0, 0]
 
 

@@ -21,22 +21,22 @@ B = 16  # block size
 
 
 # ----------------------------------------------------------------- helpers
-def scatter_dense(dense_list, num_blocks, rng, hkv, d, fill=np.nan):
+def scatter_dense(dense_list, num_blocks, rng, hkv, d, fill=np.nan, bs=B):
     """Independent pool builder: places each sequence's logical K (or V) rows
-    [L, Hkv, D] into a fresh pool under a random physical-id permutation.
-    Returns (pool, tables)."""
+    [L, Hkv, D] into a fresh pool of bs-token blocks under a random
+    physical-id permutation.  Returns (pool, tables)."""
     perm = rng.permutation(num_blocks)
-    pool = np.full((num_blocks * B, hkv, d), fill)
-    maxb = max(1, max(-(-x.shape[0] // B) for x in dense_list))
+    pool = np.full((num_blocks * bs, hkv, d), fill)
+    maxb = max(1, max(-(-x.shape[0] // bs) for x in dense_list))
     tables = np.full((len(dense_list), maxb), perm[-1], np.int64)
     cur = 0
     for s, x in enumerate(dense_list):
-        nb = -(-x.shape[0] // B)
+        nb = -(-x.shape[0] // bs)
         tables[s, :nb] = perm[cur:cur + nb]
         cur += nb
-        flat = np.repeat(tables[s, :nb], B)[: x.shape[0]] * B + np.tile(np.arange(B), nb)[: x.shape[0]]
+        flat = np.repeat(tables[s, :nb], bs)[: x.shape[0]] * bs + np.tile(np.arange(bs), nb)[: x.shape[0]]
         pool[flat] = x
-    return pool.reshape(num_blocks, B, hkv, d), tables
+    return pool.reshape(num_blocks, bs, hkv, d), tables
 
 
 def sdpa_f64(q, K, V, scale, mask=None):
@@ -96,6 +96,35 @@ def pin_dense_vs_sdpa_decode(ref):
         for s, L in enumerate(lens):
             want = sdpa_f64(q[s:s + 1], Ks[s], Vs[s], scale)[0]
             np.testing.assert_allclose(out[s], want, rtol=0, atol=1e-12)
+
+
+def pin_other_block_sizes(ref):
+    """Pools of 8- and 32-token blocks (the pages leave the block size
+    tunable): paged decode and prefill still equal dense attention."""
+    rng = np.random.default_rng(13)
+    hq, hkv, d = 4, 2, 16
+    for bs in (8, 32):
+        lens = [1, 7, 8, 9, 31, 32, 33, 65]
+        Ks = [rng.standard_normal((L, hkv, d)) for L in lens]
+        Vs = [rng.standard_normal((L, hkv, d)) for L in lens]
+        q = rng.standard_normal((len(lens), hq, d))
+        nb = sum(-(-L // bs) for L in lens) + 2
+        kp, tab = scatter_dense(Ks, nb, np.random.default_rng(9), hkv, d, bs=bs)
+        vp, _ = scatter_dense(Vs, nb, np.random.default_rng(9), hkv, d, bs=bs)
+        scale = 1 / math.sqrt(d)
+        out = ref.decode(q, kp, vp, tab, np.array(lens), scale, "f64")
+        for s, L in enumerate(lens):
+            np.testing.assert_allclose(out[s], sdpa_f64(q[s:s + 1], Ks[s], Vs[s], scale)[0], rtol=0, atol=1e-12)
+        # a 5-row chunk at the end of each context
+        n = 5
+        rows = [rng.standard_normal((min(n, L), hq, d)) for L in lens]
+        qsl = np.concatenate([[0], np.cumsum([r.shape[0] for r in rows])])
+        out = ref.attention(np.concatenate(rows), qsl, kp, vp, tab, np.array(lens), scale, "f64")
+        for s, L in enumerate(lens):
+            m = rows[s].shape[0]
+            mask = np.arange(L)[None, :] <= (L - m + np.arange(m))[:, None]
+            np.testing.assert_allclose(out[qsl[s]:qsl[s + 1]], sdpa_f64(rows[s], Ks[s], Vs[s], scale, mask),
+                                       rtol=0, atol=1e-12)
 
 
 def pin_dense_vs_sdpa_prefill(ref):
@@ -270,7 +299,7 @@ def pin_kv_write_roundtrip(ref):
     assert np.array_equal(g[0], nk[6]) and np.array_equal(g[17], nk[1])
 
 
-ALL_PINS = [pin_golden, pin_dense_vs_sdpa_decode, pin_dense_vs_sdpa_prefill,
+ALL_PINS = [pin_golden, pin_dense_vs_sdpa_decode, pin_other_block_sizes, pin_dense_vs_sdpa_prefill,
             pin_permutation, pin_single_token, pin_uniform_keys,
             pin_two_token_sigmoid, pin_brute_force, pin_gqa_repeat,
             pin_prefill_reductions, pin_kv_write_roundtrip]
@@ -287,6 +316,12 @@ def test_bf16_decode_matches_torch():
     bits = bits[(bits & 0x7F80) != 0x7F80]             # finite values only
     want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
     assert np.array_equal(ORACLE.to_f64(bits, "bf16"), want)
+
+
+def test_f16_decode_matches_torch():
+    vals = np.random.default_rng(2).standard_normal(4096).astype(np.float16)
+    want = torch.from_numpy(vals).double().numpy()
+    assert np.array_equal(ORACLE.to_f64(vals, "f16"), want)
 
 
 def test_oracle_finite_on_poisoned_batches():
@@ -309,11 +344,11 @@ MUTANTS = {
     "score_sign": ("scores = (keys @ q) * scale", "scores = -(keys @ q) * scale"),
     "no_normalise": ("weights = weights / weights.sum()", "weights = weights"),
     "wrong_operand": ("return weights @ values", "return weights @ keys"),
-    "gather_offset": ("offs = [j % BLOCK_SIZE", "offs = [(j + 1) % BLOCK_SIZE"),
-    "gather_block": ("int(table_row[j // BLOCK_SIZE])", "int(table_row[(j // BLOCK_SIZE) % 1])"),
+    "gather_offset": ("offs = [j % bsz", "offs = [(j + 1) % bsz"),
+    "gather_block": ("int(table_row[j // bsz])", "int(table_row[(j // bsz) % 1])"),
     "write_skips_slot0": ("if slot < 0:", "if slot <= 0:"),
-    "write_transposed": ("block, offset = divmod(slot, BLOCK_SIZE)",
-                         "offset, block = divmod(slot, BLOCK_SIZE)"),
+    "write_transposed": ("block, offset = divmod(slot, bsz)",
+                         "offset, block = divmod(slot, bsz)"),
     "write_k_into_v": ("v_out[block, offset] = new_v[t]", "v_out[block, offset] = new_k[t]"),
 }
 

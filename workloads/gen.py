@@ -110,7 +110,8 @@ class PagedBatch:
 
     def used_block_ids(self) -> np.ndarray:
         """Physical ids referenced by some sequence within its length."""
-        ids = [self.block_tables[s, : -(-int(L) // BLOCK)] for s, L in enumerate(self.context_lens)]
+        bs = self.k_pool.shape[1]
+        ids = [self.block_tables[s, : -(-int(L) // bs)] for s, L in enumerate(self.context_lens)]
         return np.unique(np.concatenate(ids)) if ids else np.zeros(0, np.int32)
 
 
@@ -143,6 +144,7 @@ def make_batch(
     num_prefill_seqs: int = 0,
     extra_table_cols: int = 0,
     pad_slots: int = 0,
+    block_size: int = BLOCK,
     recipe: str = "",
 ) -> PagedBatch:
     """Draw one batch.
@@ -154,7 +156,9 @@ def make_batch(
     ``shared_prefix_blocks``: logical blocks 0..n-1 of every sequence map to the
     same physical blocks (read-only aliasing, as a prefix-cache hit produces).
     ``pad_slots``: extra new tokens with slot -1 appended to the write.
+    ``block_size``: tokens per pool block (16, the pages' choice, by default).
     """
+    bs = block_size
     assert dtype in ("bf16", "f16", "f32")
     rng = np.random.default_rng(seed)
     lens = np.asarray(draw_lens(rng), dtype=np.int64)
@@ -162,7 +166,7 @@ def make_batch(
     qlens = (np.ones(S, np.int64) if draw_query_lens is None
              else np.asarray(draw_query_lens(rng, lens), np.int64))
     assert np.all(qlens >= 0) and np.all(qlens <= lens)
-    nblk = -(-lens // BLOCK)                      # blocks each sequence occupies
+    nblk = -(-lens // bs)                      # blocks each sequence occupies
     assert np.all(nblk >= shared_prefix_blocks)
     private = nblk - shared_prefix_blocks
     used = int(shared_prefix_blocks + private.sum())
@@ -193,7 +197,7 @@ def make_batch(
 
     # (3)-(6) values.
     q = _values(rng, (T, num_q_heads, head_dim), dtype)
-    pool_shape = (pool_blocks, BLOCK, num_kv_heads, head_dim)
+    pool_shape = (pool_blocks, bs, num_kv_heads, head_dim)
     k_pool = _values(rng, pool_shape, dtype)
     v_pool = _values(rng, pool_shape, dtype)
     new_k = _values(rng, (T + pad_slots, num_kv_heads, head_dim), dtype)
@@ -202,8 +206,8 @@ def make_batch(
     # Poison: unused blocks, slots past each length, and the slots this step's
     # KV write must fill.  Build the flat slot of every new token.
     poison = _poison_value(dtype)
-    k_rows = k_pool.reshape(pool_blocks * BLOCK, num_kv_heads, head_dim)
-    v_rows = v_pool.reshape(pool_blocks * BLOCK, num_kv_heads, head_dim)
+    k_rows = k_pool.reshape(pool_blocks * bs, num_kv_heads, head_dim)
+    v_rows = v_pool.reshape(pool_blocks * bs, num_kv_heads, head_dim)
     if unused_ids.size:
         k_pool[unused_ids] = poison
         v_pool[unused_ids] = poison
@@ -212,12 +216,12 @@ def make_batch(
         L, n = int(lens[s]), int(qlens[s])
         if L == 0:
             continue
-        last = int(tables[s, (L - 1) // BLOCK])
-        tail = (L - 1) % BLOCK + 1
+        last = int(tables[s, (L - 1) // bs])
+        tail = (L - 1) % bs + 1
         k_pool[last, tail:] = poison
         v_pool[last, tail:] = poison
         pos = np.arange(L - n, L)
-        rows = tables[s, pos // BLOCK] * BLOCK + pos % BLOCK
+        rows = tables[s, pos // bs] * bs + pos % bs
         slots[qsl[s]:qsl[s] + n] = rows
         k_rows[rows] = poison
         v_rows[rows] = poison
@@ -270,18 +274,19 @@ def tiny_f32(seed: int = 1) -> PagedBatch:
 
 
 def qwen25_05b_decode(seed: int = 2, batch: int = 32, lo: int = 128, hi: int = 1024,
-                      dtype: str = "bf16") -> PagedBatch:
+                      dtype: str = "bf16", block_size: int = BLOCK) -> PagedBatch:
     """Qwen2.5-0.5B-shaped decode step: 14 q / 2 kv heads, dim 64, bf16,
     lengths uniform in [lo, hi]; pool 1.2x the blocks in use."""
     return make_batch(
-        seed, name="qwen25_05b_decode", dtype=dtype, num_q_heads=14,
+        seed, name="qwen25_05b_decode", dtype=dtype, block_size=block_size, num_q_heads=14,
         num_kv_heads=2, head_dim=64,
         draw_lens=lambda rng: rng.integers(lo, hi + 1, size=batch),
         recipe=f"B={batch}, L~U[{lo},{hi}], pool 1.2x, N(0,1)->bf16")
 
 
 def qwen3_06b_decode(seed: int = 3, batch: int = 256, prompt=(100, 1024),
-                     gen=(0, 1024), cap: int = 2048, dtype: str = "bf16") -> PagedBatch:
+                     gen=(0, 1024), cap: int = 2048, dtype: str = "bf16",
+                     block_size: int = BLOCK) -> PagedBatch:
     """Qwen3-0.6B-shaped decode step: 16 q / 8 kv heads, dim 128, bf16,
     length = prompt U[100,1024] + generated U[0,1024], capped at 2048; pool
     1.2x the blocks in use with permuted ids."""
@@ -290,7 +295,7 @@ def qwen3_06b_decode(seed: int = 3, batch: int = 256, prompt=(100, 1024),
         g = rng.integers(gen[0], gen[1] + 1, size=batch)
         return np.minimum(p + g, cap)
     return make_batch(
-        seed, name="qwen3_06b_decode", dtype=dtype, num_q_heads=16,
+        seed, name="qwen3_06b_decode", dtype=dtype, block_size=block_size, num_q_heads=16,
         num_kv_heads=8, head_dim=128, draw_lens=lens,
         recipe=f"B={batch}, L=min(U{list(prompt)}+U{list(gen)},{cap}), pool 1.2x, N(0,1)->bf16")
 
@@ -299,7 +304,7 @@ def mixed_prefill(seed: int = 4, chunks: int = 4, chunk_len: int = 512,
                   prior_hi: int = 1536, n_decode: int = 192,
                   dec_lo: int = 256, dec_hi: int = 2048, num_q_heads: int = 16,
                   num_kv_heads: int = 8, head_dim: int = 128,
-                  chunk_lens=None, dtype: str = "bf16") -> PagedBatch:
+                  chunk_lens=None, dtype: str = "bf16", block_size: int = BLOCK) -> PagedBatch:
     """Mixed chunked-prefill batch, by default the Qwen3-0.6B head shape (16 / 8 / 128, bf16):
     ``chunks`` prefill chunks of ``chunk_len`` new tokens (or the lengths listed
     in ``chunk_lens``) after a cached prior context U[0, prior_hi], followed by
@@ -319,7 +324,7 @@ def mixed_prefill(seed: int = 4, chunks: int = 4, chunk_len: int = 512,
     def qlens(rng, L):
         return np.concatenate([new_tokens, np.ones(n_decode, np.int64)])
     return make_batch(
-        seed, name="mixed_prefill", dtype=dtype, num_q_heads=num_q_heads,
+        seed, name="mixed_prefill", dtype=dtype, block_size=block_size, num_q_heads=num_q_heads,
         num_kv_heads=num_kv_heads, head_dim=head_dim, draw_lens=lens, draw_query_lens=qlens,
         num_prefill_seqs=chunks,
         recipe=(f"{chunks} chunks x {[int(x) for x in new_tokens] if chunk_lens is not None else chunk_len} "
