@@ -43,15 +43,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(partition: int):
+def measured_traffic(partition: int, block_size: int, workload: str):
     """HBM bytes per decode launch from committed rocprofv3 counter runs, when
-    they were taken on the kernel sources and partition in use now."""
+    they were taken on the kernel sources, workload, block size and partition
+    in use now."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("partition_tokens") != partition:
+    if (t.get("kernel_source_hash") != kernel_source_hash() or t.get("partition_tokens") != partition
+            or t.get("block_size", 16) != block_size or not str(t.get("workload", "")).startswith(workload)):
         return None
     return t.get("hbm_bytes_per_decode")
 
@@ -60,11 +62,12 @@ def unique_context_tokens(b) -> int:
     """Distinct pool slots the batch reads: a physical block shared by several
     tables (a common prefix) counts once."""
     import numpy as np
+    bs = b.k_pool.shape[1]
     used = {}
     for s, L in enumerate(b.context_lens.tolist()):
-        nb = -(-L // 16)
+        nb = -(-L // bs)
         for j, blk in enumerate(b.block_tables[s, :nb].tolist()):
-            used[blk] = max(used.get(blk, 0), min(16, L - 16 * j))
+            used[blk] = max(used.get(blk, 0), min(bs, L - bs * j))
     return int(np.sum(list(used.values()))) if used else 0
 
 
@@ -75,7 +78,8 @@ def decode_bytes(b) -> int:
     es = b.elem_bytes
     kv = unique_context_tokens(b) * 2 * b.num_kv_heads * b.head_dim * es
     qo = 2 * b.num_seqs * b.num_q_heads * b.head_dim * es
-    tables = 4 * int(sum(-(-int(L) // 16) for L in b.context_lens))
+    bs = b.k_pool.shape[1]
+    tables = 4 * int(sum(-(-int(L) // bs) for L in b.context_lens))
     return kv + qo + tables + 4 * b.num_seqs
 
 
@@ -270,6 +274,8 @@ def main() -> int:
     ap.add_argument("--op", default="step", choices=["step", "fused_write"],
                     help="step: the workload's attention step (default); fused_write: "
                          "pa_qkv_rope_write on the workload's new tokens")
+    ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
+                    help="tokens per pool block (16 is the pages' choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -302,7 +308,7 @@ def main() -> int:
         pa_build.build()
 
     log(f"[bench] generating {args.workload}")
-    b = PRESETS[args.workload]()
+    b = PRESETS[args.workload](**({} if args.block_size == 16 else {"block_size": args.block_size}))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
@@ -363,7 +369,7 @@ def main() -> int:
     value = (dbytes + wbytes) / (ms_per_step * 1e-3) / 1e9
     dec_mean_s = float(np.mean(dec_ms)) * 1e-3
     achieved = dbytes / dec_mean_s / 1e9
-    traffic = measured_traffic(part)
+    traffic = measured_traffic(part, int(b.k_pool.shape[1]), b.name)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -380,7 +386,7 @@ def main() -> int:
         "config": {
             "workload": b.name, "recipe": b.recipe, "seed": b.seed, "num_seqs": b.num_seqs,
             "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads,
-            "head_dim": b.head_dim, "block_size": 16, "num_blocks": b.num_blocks,
+            "head_dim": b.head_dim, "block_size": int(b.k_pool.shape[1]), "num_blocks": b.num_blocks,
             "mean_context": round(float(b.context_lens.mean()), 2),
             "max_context": b.max_context_len, "partition_tokens": part,
             "step": "pa_kv_write (one new token per sequence) + pa_decode",

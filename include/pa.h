@@ -36,19 +36,19 @@
  *   never reads device memory from the host, so all sizes the launch needs come
  *   in as host integers.
  * - Layouts are row-major and contiguous unless a stride says otherwise:
- *     pools          [num_blocks, 16, num_kv_heads, head_dim]
+ *     pools          [num_blocks, B, num_kv_heads, head_dim], B = block_size
  *     q, out         [rows, num_q_heads, head_dim]
  *     block_tables   int32 [num_seqs, max_blocks_per_seq]; entry i is the
- *                    physical block holding logical tokens 16i .. 16i+15
+ *                    physical block holding logical tokens B*i .. B*i+B-1
  *     context_lens   int32 [num_seqs]; tokens attended, including the ones
  *                    written in this step (write first, then attend)
  * - Query head h attends with kv head h / (num_q_heads / num_kv_heads).
  * - q, out and the pools share one element type: bf16 or fp16 (accumulation in
  *   fp32, output rounded to nearest even) or fp32.
  * - Device-side data is trusted for results but not for memory safety: slots
- *   outside [0, num_blocks*16) are skipped, block ids are clamped into
+ *   outside [0, num_blocks*B) are skipped, block ids are clamped into
  *   [0, num_blocks), context lengths are clamped into [0, max_context_len] and
- *   to max_blocks_per_seq*16.  Such inputs give unspecified values, never an
+ *   to max_blocks_per_seq*B.  Such inputs give unspecified values, never an
  *   out-of-bounds access.
  */
 #ifndef PA_H
@@ -76,7 +76,9 @@ typedef enum {
 typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
 
 /* Shape of one layer's K pool (the V pool has the same shape).
- * block_size must be 16; head_dim 64 or 128; dtype a pa_dtype. */
+ * block_size 8, 16 or 32 tokens (16 is the pages' choice; the others serve a
+ * block-size sweep, and a 16-token chunk then spans two blocks of 8 or half
+ * a block of 32); head_dim 64 or 128; dtype a pa_dtype. */
 typedef struct {
     int32_t num_blocks;
     int32_t block_size;
@@ -95,9 +97,9 @@ const char* pa_status_str(int32_t status);
  *                 tokens are k_token_stride / v_token_stride ELEMENTS apart
  *                 (so views into a packed QKV projection work); within a token
  *                 the [num_kv_heads, head_dim] row is contiguous.
- * slot_mapping    int32 [num_tokens]; token t goes to block slot/16, offset
- *                 slot%16, i.e. row `slot` of the pool seen as
- *                 [num_blocks*16, num_kv_heads*head_dim].  slot < 0 marks a
+ * slot_mapping    int32 [num_tokens]; token t goes to block slot/B, offset
+ *                 slot%B, i.e. row `slot` of the pool seen as
+ *                 [num_blocks*B, num_kv_heads*head_dim].  slot < 0 marks a
  *                 padding token: nothing is written for it.  Slots must be
  *                 distinct within one call (otherwise which row wins is
  *                 unspecified).
@@ -131,7 +133,7 @@ int32_t pa_kv_write(const void* k, const void* v,
  *                   first, then attend): token i of a sequence with n tokens
  *                   and length L is at position L - n + i.
  * block_tables      int32 [num_seqs, max_blocks_per_seq].
- * Slot of a token = block_tables[s][pos / 16] * 16 + pos % 16.  When the
+ * Slot of a token = block_tables[s][pos / B] * B + pos % B.  When the
  * position lies outside the table or the entry outside the pool, nothing is
  * written to the pools for that token (its q row is still written) and its
  * slot reads -1.
@@ -183,9 +185,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * pa_decode -- one query row per sequence.
  *
  * q, out          [num_seqs, num_q_heads, head_dim]
- * k_pool, v_pool  [num_blocks, 16, num_kv_heads, head_dim] (read only)
+ * k_pool, v_pool  [num_blocks, B, num_kv_heads, head_dim] (read only)
  * block_tables    int32 [num_seqs, max_blocks_per_seq]; entries past
- *                 ceil(context_len/16) are never read
+ *                 ceil(context_len/B) are never read
  * context_lens    int32 [num_seqs]; 0 gives an all-zero output row
  * max_context_len host-side upper bound of context_lens
  * scale           multiplies q.k before the softmax (normally 1/sqrt(head_dim))
@@ -251,7 +253,7 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc,
  * count zero.)
  *
  * A manager owns num_blocks physical block ids of block_size tokens each
- * (block_size 16 for the attention calls).  All calls are host calls and
+ * (8, 16 or 32 for the attention calls).  All calls are host calls and
  * thread-safe (one lock per manager); each either succeeds or changes
  * nothing.  Sequence ids are the caller's.
  *

@@ -158,7 +158,8 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
     constexpr int KTILE = kKeys * KROW;
     constexpr int VTILE = kKeys * VROW;
     constexpr int KEYS_PER_WAVE_LOAD = 64 / CPR;  // keys one wave covers per load slot
-    static_assert(LOADS >= 1 && kBlock % KEYS_PER_WAVE_LOAD == 0, "tile loader");
+    // a wave's keys of one load slot lie inside one pool block (8 tokens or more)
+    static_assert(LOADS >= 1 && 8 % KEYS_PER_WAVE_LOAD == 0, "tile loader");
     // Two buffers per key half; the halves' states are merged through lds_k.
     static_assert(KSPLIT == 1 || (kRowWaves * 64 * NT * (MT * 4 + 2) * 4 <= KSPLIT * 2 * KTILE), "merge space");
     __shared__ __align__(16) unsigned char lds_k[KSPLIT * 2 * KTILE];
@@ -172,7 +173,8 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
     if (rows < a.min_pairs) return;  // the vector path handles this sequence
     const int row0 = blockIdx.x * kRowsPerGroup;
     if (row0 >= rows) return;
-    const int cap = min(a.max_context_len, a.max_blocks * kBlock);
+    const int bsh = a.block_shift;  // pool blocks of 1 << bsh tokens
+    const int cap = (int)min((int64_t)a.max_context_len, (int64_t)a.max_blocks << bsh);
     const int L = min(max(a.context_lens[s], 0), cap);
     const int prior = L - n;  // keys before the chunk
 
@@ -238,17 +240,19 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
     // included), are stored as zeros so that a zero probability times them
     // stays zero.
     uint4 kreg[DEPTH][LOADS], vreg[DEPTH][LOADS];
-    // A tile starts on a block boundary, so each chunk's row inside its block,
-    // and with it the chunk's byte offset inside the block, is the same for
-    // every tile: only the (wave-uniform) block base changes, and the loads
-    // take it as a scalar base plus this per-lane offset.
-    const int64_t blk_bytes = (int64_t)kBlock * tok_stride * 2;
+    // A tile starts on a block boundary (tiles of kKeys keys, blocks of at
+    // most 32), so each chunk's row inside its block, and with it the chunk's
+    // byte offset inside the block, is the same for every tile: only the
+    // (wave-uniform) block base changes, and the loads take it as a scalar
+    // base plus this per-lane offset.
+    static_assert(kKeys % 32 == 0, "tiles start on block boundaries");
+    const int64_t blk_bytes = ((int64_t)tok_stride * 2) << bsh;
     uint32_t lane_off[LOADS];
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
         const int ci = htid + u * HT;
         const int key = ci / CPR, c = ci % CPR;
-        lane_off[u] = (uint32_t)(((key % kBlock) * tok_stride + g * D + c * 8) * 2);
+        lane_off[u] = (uint32_t)(((key & ((1 << bsh) - 1)) * tok_stride + g * D + c * 8) * 2);
     }
     const unsigned char* kbase = static_cast<const unsigned char*>(a.k_pool);
     const unsigned char* vbase = static_cast<const unsigned char*>(a.v_pool);
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {  // scalar loads first, one wait for all
             const int key0 = (rw * 64 + u * HT) / CPR;  // wave-uniform
-            const int bi = min((j0 + key0) / kBlock, a.max_blocks - 1);
+            const int bi = min((j0 + key0) >> bsh, a.max_blocks - 1);
             blk[u] = min(max(bt[bi], 0), a.num_blocks - 1);
         }
 #pragma unroll

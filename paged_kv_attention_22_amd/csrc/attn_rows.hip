@@ -164,7 +164,7 @@ __device__ __forceinline__ Item locate(const RowsArgs& a, int z, int group) {
 
 // Keys visible to the row: 0 .. L-n+i, with L clamped to what the table holds.
 __device__ __forceinline__ int visible_len(const RowsArgs& a, const Item& it, int L) {
-    const int cap = min(a.max_context_len, a.max_blocks * kBlock);
+    const int cap = (int)min((int64_t)a.max_context_len, (int64_t)a.max_blocks << a.block_shift);
     L = min(max(L, 0), cap);
     return min(max(L - it.n + it.i + 1, 0), L);
 }
@@ -235,8 +235,9 @@ __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
     constexpr int EL = V * E;                 // elements per lane per token
     constexpr int R = D / EL;                 // lanes per token row
     constexpr int TPW = 64 / R;               // token rows per wave
-    constexpr int NT = kBlock / TPW;          // tokens of one block per lane
+    constexpr int NT = kBlock / TPW;          // tokens of one chunk per lane
     static_assert(TPW >= 1 && NT >= 1 && R >= 4, "lane layout");
+    static_assert(8 % TPW == 0, "each lane's rows split evenly between a chunk's two halves");
     constexpr float kLazy = 8.0f;             // log2 headroom before rescaling
 
     const int lane = threadIdx.x & 63;
@@ -263,12 +264,18 @@ __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int u = 0; u < V; ++u) qv[h][u] = ld16(qp + h * D + u * R * E);
-    // Block ids: lane i holds the id of block k = kbase + i (one load per 64).
+    // Block ids: lane i holds the table entry behind this wave's chunk
+    // kbase + i (one load per 64 chunks): the block holding the chunk (blocks
+    // of 16 or 32), or the first of its two blocks with the second in ids_hi
+    // (blocks of 8).
     const int32_t* bt = a.block_tables + (int64_t)it.seq * a.max_blocks;
-    int ids = 0;
+    const int bsh = a.block_shift;
+    const ChunkMap cm = chunk_map(bsh);
+    int ids = 0, ids_hi = 0;
     auto fetch_ids = [&](int kbase) {
         const int jj = first + (kbase + lane) * kWaves;
-        ids = jj < a.max_blocks ? bt[jj] : 0;
+        ids = bt[min((jj << cm.mul) >> cm.shr, a.max_blocks - 1)];
+        ids_hi = bt[min(((jj << cm.mul) + cm.mul) >> cm.shr, a.max_blocks - 1)];
     };
     fetch_ids(0);
 
@@ -296,10 +303,15 @@ __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
     const int nk = b1 > first ? (b1 - first + kWaves - 1) / kWaves : 0;
     const int nfull = len / kBlock;
     const int nkf = nfull > first ? min(nk, (nfull - first + kWaves - 1) / kWaves) : 0;
-    auto block_of = [&](int k) -> int {
+    // First pool rows of chunk k's tokens 0-7 (lo) and 8-15 (hi); ids are
+    // clamped into the pool.
+    auto rows_of = [&](int k, int64_t& lo, int64_t& hi) {
         if ((k & 63) == 0 && k != 0) fetch_ids(k);
-        const int blk = __builtin_amdgcn_readlane(ids, k & 63);
-        return min(max(blk, 0), a.num_blocks - 1);
+        const int bl = min(max(__builtin_amdgcn_readlane(ids, k & 63), 0), a.num_blocks - 1);
+        const int bh = min(max(__builtin_amdgcn_readlane(ids_hi, k & 63), 0), a.num_blocks - 1);
+        const int off = ((first + k * kWaves) << 4) & cm.in_block;
+        lo = ((int64_t)bl << bsh) + off;
+        hi = ((int64_t)bh << bsh) + off + cm.hi_off;
     };
 
     const int64_t tok_stride = (int64_t)Hkv * D;  // elements between tokens
@@ -308,12 +320,16 @@ __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
     const float sl2 = a.scale * kLog2e;
 
     auto load = [&](uint4 (&kk)[NT][V], uint4 (&vv)[NT][V], int k) {
-        const int64_t off = (int64_t)block_of(k) * kBlock * tok_stride;
+        int64_t lo, hi;
+        rows_of(k, lo, hi);
+        // element offsets of the chunk's rows 0 and 8 (wave-uniform)
+        const int64_t o_lo = lo * tok_stride, o_hi = (hi - 8) * tok_stride;
 #pragma unroll
         for (int i = 0; i < NT; ++i)
 #pragma unroll
             for (int u = 0; u < V; ++u) {
-                const int64_t o = off + (int64_t)(i * TPW) * tok_stride + u * R * E;
+                // this lane's row rg + i*TPW of the chunk is in its first half iff i*TPW < 8
+                const int64_t o = (i * TPW < 8 ? o_lo : o_hi) + (i * TPW) * tok_stride + u * R * E;
                 kk[i][u] = ld16_stream(kbase + o);
                 vv[i][u] = ld16_stream(vbase + o);
             }
@@ -480,12 +496,17 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a
             v = ld16(static_cast<const T*>(a.q) + ((int64_t)it.row * Hq + g * G + li) * D + ks * 32 + kg * 8);
         qf[ks] = __builtin_bit_cast(V8, v);
     }
-    // Block ids: lane i holds the id of block (b0 + 2*(wave + (kbase + i/2)*kWaves) + i%2).
+    // Block ids: lane i holds the table entry behind chunk
+    // b0 + 2*(wave + (kbase + i/2)*kWaves) + i%2 (as in rows_kernel: blocks of
+    // 8 keep the chunk's second block in ids_hi).
     const int32_t* bt = a.block_tables + (int64_t)it.seq * a.max_blocks;
-    int ids = 0;
+    const int bsh = a.block_shift;
+    const ChunkMap cm = chunk_map(bsh);
+    int ids = 0, ids_hi = 0;
     auto fetch_ids = [&](int kbase) {
         const int jj = b0 + 2 * (wave + (kbase + (lane >> 1)) * kWaves) + (lane & 1);
-        ids = jj < a.max_blocks ? bt[jj] : 0;
+        ids = bt[min((jj << cm.mul) >> cm.shr, a.max_blocks - 1)];
+        ids_hi = bt[min(((jj << cm.mul) + cm.mul) >> cm.shr, a.max_blocks - 1)];
     };
     fetch_ids(0);
 
@@ -505,15 +526,24 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a
     const int nk = b1 > first ? (b1 - first + 2 * kWaves - 1) / (2 * kWaves) : 0;
     const int full_end = min(b1, len / kBlock);  // blocks below this are full
     const int nkf = full_end >= first + 2 ? min(nk, (full_end - first - 2) / (2 * kWaves) + 1) : 0;
-    auto block_of = [&](int k, int half) -> int {
+    // First pool rows of the step's chunk `half`, tokens 0-7 (lo) and 8-15 (hi).
+    auto rows_of = [&](int k, int half, int64_t& lo, int64_t& hi) {
         if ((k & 31) == 0 && k != 0 && half == 0) fetch_ids(k);
-        const int blk = __builtin_amdgcn_readlane(ids, ((k & 31) << 1) | half);
-        return min(max(blk, 0), a.num_blocks - 1);
+        const int ln = ((k & 31) << 1) | half;
+        const int bl = min(max(__builtin_amdgcn_readlane(ids, ln), 0), a.num_blocks - 1);
+        const int bh = min(max(__builtin_amdgcn_readlane(ids_hi, ln), 0), a.num_blocks - 1);
+        const int off = ((first + 2 * kWaves * k + half) << 4) & cm.in_block;
+        lo = ((int64_t)bl << bsh) + off;
+        hi = ((int64_t)bh << bsh) + off + cm.hi_off;
     };
 
     const int64_t tok_stride = (int64_t)Hkv * D;
     const T* kpool = static_cast<const T*>(a.k_pool) + (int64_t)g * D;
     const T* vpool = static_cast<const T*>(a.v_pool) + (int64_t)g * D;
+    constexpr int TPS = 64 / CPR;  // V rows one 64-lane slice covers
+    static_assert(8 % TPS == 0, "a V slice stays inside half a chunk");
+    const int k_lane = li * (int)tok_stride + kg * 8;                             // K row li, column
+    const int v_lane = (lane / CPR) * (int)tok_stride + (lane % CPR) * 8;          // V row, column
     unsigned char* vt = s_v + wave * VT;
     const float sl2 = a.scale * kLog2e;
 
@@ -524,20 +554,32 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a
 
     auto load = [&](uint4 (&kf)[2][KS], uint4 (&vr)[VL], int k) {
         const int jb = first + 2 * kWaves * k;
-        const int blk0 = block_of(k, 0);
-        const int blk1 = jb + 1 < b1 ? block_of(k, 1) : blk0;
+        int64_t lo0, hi0, lo1, hi1;
+        rows_of(k, 0, lo0, hi0);
+        if (jb + 1 < b1) {
+            rows_of(k, 1, lo1, hi1);
+        } else {
+            lo1 = lo0;
+            hi1 = hi0;
+        }
+        // Wave-uniform element offsets of rows 0 and 8 of both chunks; the
+        // lanes add their own (loop-invariant) row and column offsets.
+        const int64_t o_lo0 = lo0 * tok_stride, o_hi0 = (hi0 - 8) * tok_stride;
+        const int64_t o_lo1 = lo1 * tok_stride, o_hi1 = (hi1 - 8) * tok_stride;
+        // K: lane row li of chunk mt lies in the chunk's first half iff li < 8
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-            const int blk = mt ? blk1 : blk0;
+            const T* kp = kpool + (mt ? (li < 8 ? o_lo1 : o_hi1) : (li < 8 ? o_lo0 : o_hi0));
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                kf[mt][ks] = ld16_stream(kpool + ((int64_t)blk * kBlock + li) * tok_stride + ks * 32 + kg * 8);
+            for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = ld16_stream(kp + k_lane + ks * 32);
         }
+        // V: slice u covers step tokens u*TPS .. u*TPS+TPS-1, all in one half
+        // of one chunk (known at compile time)
 #pragma unroll
         for (int u = 0; u < VL; ++u) {
-            const int c = lane + 64 * u, tk = c / CPR, piece = c % CPR;
-            const int blk = tk < 16 ? blk0 : blk1;
-            vr[u] = ld16_stream(vpool + ((int64_t)blk * kBlock + (tk & 15)) * tok_stride + piece * 8);
+            const int t0 = u * TPS;
+            const int64_t o = (t0 >> 4) ? ((t0 & 15) < 8 ? o_lo1 : o_hi1) : ((t0 & 15) < 8 ? o_lo0 : o_hi0);
+            vr[u] = ld16_stream(vpool + o + (int64_t)(t0 & 15) * tok_stride + v_lane);
         }
     };
     auto compute = [&](const uint4 (&kf)[2][KS], const uint4 (&vr)[VL], int k, bool masked) {

@@ -57,14 +57,24 @@ int elem_size(int32_t dtype) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// log2 of a supported pool block size (8, 16 or 32 tokens), else -1.
+int32_t block_shift_of(int32_t block_size) {
+    switch (block_size) {
+        case 8: return 3;
+        case 16: return 4;
+        case 32: return 5;
+        default: return -1;
+    }
+}
+
 int32_t check_pool(const pa_pool_desc& p) {
     if (elem_size(p.dtype) == 0) return PA_ERR_DTYPE;
     if (p.num_blocks <= 0 || p.num_kv_heads <= 0 || p.head_dim <= 0 || p.block_size <= 0)
         return PA_ERR_SHAPE;
-    if (p.block_size != kBlock) return PA_ERR_UNSUPPORTED;
+    if (block_shift_of(p.block_size) < 0) return PA_ERR_UNSUPPORTED;
     if (p.head_dim != 64 && p.head_dim != 128) return PA_ERR_UNSUPPORTED;
     if (p.num_kv_heads > 65535) return PA_ERR_SHAPE;
-    if ((int64_t)p.num_blocks * kBlock > INT32_MAX) return PA_ERR_SHAPE;  // slots are int32
+    if ((int64_t)p.num_blocks * p.block_size > INT32_MAX) return PA_ERR_SHAPE;  // slots are int32
     return PA_OK;
 }
 
@@ -212,7 +222,7 @@ int32_t pa_kv_write(const void* k, const void* v, int64_t k_token_stride, int64_
     a.num_tokens = num_tokens;
     a.k_pool = k_pool;
     a.v_pool = v_pool;
-    a.pool_rows = (int64_t)pool.num_blocks * kBlock;
+    a.pool_rows = (int64_t)pool.num_blocks * pool.block_size;
     a.row_bytes = (int32_t)(row_elems * es);
     return launch_kv_write(a, static_cast<hipStream_t>(stream));
 }
@@ -241,7 +251,7 @@ int32_t pa_decode(const void* q, const void* k_pool, const void* v_pool, pa_pool
     if (int32_t st = check_pool(pool)) return st;
     if (int32_t st = check_heads(num_q_heads, pool.num_kv_heads)) return st;
     if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
-        (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlock)
+        (int64_t)max_context_len > (int64_t)max_blocks_per_seq * pool.block_size)
         return PA_ERR_SHAPE;
     if (int32_t st = check_partition(partition_tokens)) return st;
     if (num_seqs == 0) return PA_OK;
@@ -265,6 +275,7 @@ int32_t pa_decode(const void* q, const void* k_pool, const void* v_pool, pa_pool
     a.num_kv_heads = pool.num_kv_heads;
     a.head_dim = pool.head_dim;
     a.num_blocks = pool.num_blocks;
+    a.block_shift = block_shift_of(pool.block_size);
     a.dtype = pool.dtype;
     a.max_context_len = max_context_len;
     a.scale = scale;
@@ -309,6 +320,7 @@ int32_t pa_qkv_rope_write(const void* qkv, int64_t qkv_token_stride,
     a.num_kv_heads = pool.num_kv_heads;
     a.head_dim = pool.head_dim;
     a.num_blocks = pool.num_blocks;
+    a.block_shift = block_shift_of(pool.block_size);
     a.dtype = pool.dtype;
     a.log2_theta = log2((double)rope_theta);
     a.q_norm = q_norm_weight;
@@ -363,7 +375,7 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
     if (int32_t st = check_heads(num_q_heads, pool.num_kv_heads)) return st;
     if (num_seqs < 0 || num_prefill_seqs < 0 || num_prefill_seqs > num_seqs ||
         total_query_tokens < 0 || max_query_len < 0 || max_blocks_per_seq <= 0 ||
-        max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlock ||
+        max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * pool.block_size ||
         max_query_len > max_context_len)
         return PA_ERR_SHAPE;
     const int64_t num_decode = num_seqs - num_prefill_seqs;
@@ -389,6 +401,7 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
     base.num_kv_heads = pool.num_kv_heads;
     base.head_dim = pool.head_dim;
     base.num_blocks = pool.num_blocks;
+    base.block_shift = block_shift_of(pool.block_size);
     base.dtype = pool.dtype;
     base.max_context_len = max_context_len;
     base.scale = scale;
@@ -441,6 +454,7 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
         c.num_kv_heads = pool.num_kv_heads;
         c.head_dim = pool.head_dim;
         c.num_blocks = pool.num_blocks;
+        c.block_shift = block_shift_of(pool.block_size);
         c.dtype = pool.dtype;
         c.total_rows = total_query_tokens;
         c.scale = scale;

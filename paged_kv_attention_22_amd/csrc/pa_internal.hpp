@@ -9,7 +9,22 @@
 
 namespace pa {
 
-constexpr int kBlock = 16;   // tokens per KV block (fixed; the pages' default)
+// The attention kernels work in chunks of 16 tokens (the pages' block size).
+// A pool block holds 8, 16 or 32 tokens (block_shift 3, 4 or 5): a 16-token
+// chunk lies inside one block of 16 or 32, and spans two blocks of 8.
+constexpr int kBlock = 16;
+
+// Where a 16-token chunk c lives, for pools of 1 << shift tokens per block:
+// its table entries are lo = (c << mul) >> shr and hi = ((c << mul) + mul) >> shr
+// (blocks of 8: entries 2c and 2c+1; of 16: c; of 32: c/2), its tokens 0-7
+// start at row (c*16 & in_block) of entry lo, and its tokens 8-15 at row
+// (c*16 & in_block) + hi_off of entry hi.
+struct ChunkMap {
+    int mul, shr, in_block, hi_off;
+};
+__host__ __device__ inline ChunkMap chunk_map(int shift) {
+    return shift == 3 ? ChunkMap{1, 0, 0, 0} : ChunkMap{0, shift - 4, (1 << shift) - 1, 8};
+}
 constexpr int kMaxGroup = 8; // largest GQA group built
 
 // One launch of the vector-path attention over a set of query rows ("items").
@@ -47,6 +62,7 @@ struct RowsArgs {
     int32_t part_tokens;  // <= 0: one pass, else a multiple of 16
     int32_t nparts;       // partitions per item when split
     float* ws;            // split partials: acc [items,Hq,nparts,D], m, l [items,Hq,nparts]
+    int32_t block_shift;  // log2 of the pool's block size
 };
 
 int32_t launch_rows(const RowsArgs& a, hipStream_t stream);
@@ -88,6 +104,7 @@ struct QkvArgs {
     void* k_pool;
     void* v_pool;
     int32_t* slots_out;                 // [num_tokens] or NULL
+    int32_t block_shift;                // log2 of the pool's block size
 };
 
 int32_t launch_qkv_write(const QkvArgs& a, hipStream_t stream);
@@ -110,6 +127,7 @@ struct ChunkArgs {
     float scale;
     void* out;
     int32_t min_pairs;
+    int32_t block_shift;  // log2 of the pool's block size
 };
 
 // Returns PA_ERR_UNSUPPORTED when no matrix-core kernel exists for the shape

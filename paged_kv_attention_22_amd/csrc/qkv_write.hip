@@ -105,9 +105,10 @@ __global__ __launch_bounds__(kThreads) void qkv_write_kernel(const QkvArgs a) {
     }
     const int pos = a.context_lens[s] - n + i;
     int64_t slot = -1;
-    if (pos >= 0 && pos < a.max_blocks * kBlock) {
-        const int blk = a.block_tables[(int64_t)s * a.max_blocks + pos / kBlock];
-        if (blk >= 0 && blk < a.num_blocks) slot = (int64_t)blk * kBlock + pos % kBlock;
+    const int bsh = a.block_shift;  // pool blocks of 1 << bsh tokens
+    if (pos >= 0 && (int64_t)pos < ((int64_t)a.max_blocks << bsh)) {
+        const int blk = a.block_tables[(int64_t)s * a.max_blocks + (pos >> bsh)];
+        if (blk >= 0 && blk < a.num_blocks) slot = ((int64_t)blk << bsh) + (pos & ((1 << bsh) - 1));
     }
     if (threadIdx.x == 0 && a.slots_out != nullptr) a.slots_out[t] = (int32_t)slot;
 

@@ -61,7 +61,11 @@ def decode(pa, **kw):
 def test_decode_validation(pa):
     assert decode(pa, q=0) == 1                       # NULL
     assert decode(pa, out=0) == 1
-    assert decode(pa, pool=pool(bs=32)) == 4           # block size must be 16
+    for bs in (4, 12, 64):
+        assert decode(pa, pool=pool(bs=bs)) == 4       # block sizes 8, 16, 32 only
+    assert decode(pa, pool=pool(bs=8), maxL=33) == 2   # > max_blocks * 8
+    assert decode(pa, pool=pool(bs=32), maxL=129) == 2  # > max_blocks * 32
+    assert decode(pa, pool=pool(nb=1 << 26, bs=32)) == 2  # slots past int32
     assert decode(pa, pool=pool(d=96)) == 4            # head_dim 64/128 only
     assert decode(pa, pool=pool(dtype=7)) == 3         # unknown dtype
     assert decode(pa, pool=pool(nb=0)) == 2
@@ -83,7 +87,9 @@ def test_kv_write_validation(pa):
     assert L.pa_kv_write(0, FAKE, 64, 64, FAKE, 4, FAKE, FAKE, p, 0) == 1
     assert L.pa_kv_write(FAKE, FAKE, 32, 64, FAKE, 4, FAKE, FAKE, p, 0) == 2   # stride < row
     assert L.pa_kv_write(FAKE, FAKE, 68, 64, FAKE, 4, FAKE, FAKE, p, 0) == 7   # unaligned stride
-    assert L.pa_kv_write(FAKE, FAKE, 64, 64, FAKE, 4, FAKE, FAKE, pool(bs=8), 0) == 4
+    assert L.pa_kv_write(FAKE, FAKE, 64, 64, FAKE, 4, FAKE, FAKE, pool(bs=64), 0) == 4
+    assert L.pa_kv_write(FAKE, FAKE, 64, 64, FAKE, 0, FAKE, FAKE, pool(bs=8), 0) == 0
+    assert L.pa_kv_write(FAKE, FAKE, 64, 64, FAKE, 0, FAKE, FAKE, pool(bs=32), 0) == 0
 
 
 def test_prefill_validation(pa):
@@ -102,6 +108,8 @@ def test_prefill_validation(pa):
     assert call(T=1) == 2               # fewer rows than decode seqs
     assert call(npre=0, T=5) == 2       # rows beyond the decode rows but no prefill seq
     assert call(maxq=65) == 2           # a chunk longer than any context
+    assert call(pool=pool(bs=8)) == 2   # max_context_len 64 > 4 blocks of 8
+    assert call(pool=pool(bs=24)) == 4
     assert call(T=0, S=0, npre=0) == 0    # empty batch: no-op
 
 
@@ -169,4 +177,6 @@ def test_qkv_rope_write_validation(pa):
     assert call(theta=float("inf")) == 2
     assert call(eps=-1.0) == 2
     assert call(pool=pool(hkv=2, d=96)) == 4
+    assert call(pool=pool(hkv=2, d=64, bs=64)) == 4
+    assert call(T=0, pool=pool(hkv=2, d=64, bs=8)) == 0
     assert call(pool=pool(hkv=2, d=64, dtype=5)) == 3

@@ -333,15 +333,16 @@ def mixed_prefill(seed: int = 4, chunks: int = 4, chunk_len: int = 512,
 
 
 def long_context(seed: int = 5, batch: int = 64, ctx: int = 8192,
-                 shared_blocks: int = 256) -> PagedBatch:
+                 shared_blocks: int = 256, block_size: int = BLOCK) -> PagedBatch:
     """Qwen2.5-7B-shaped long-context decode: 28 q / 4 kv heads, dim 128,
     bf16, every sequence at ``ctx`` tokens, whose first ``shared_blocks``
-    logical blocks are the same physical blocks for all sequences; the pool
-    holds exactly the blocks in use."""
+    logical blocks (of 16 tokens: the shared prefix is 16 * shared_blocks
+    tokens at any block size) are the same physical blocks for all
+    sequences; the pool holds exactly the blocks in use."""
     return make_batch(
         seed, name="long_context", dtype="bf16", num_q_heads=28, num_kv_heads=4,
-        head_dim=128, draw_lens=lambda rng: np.full(batch, ctx),
-        pool_factor=1.0, shared_prefix_blocks=shared_blocks,
+        head_dim=128, draw_lens=lambda rng: np.full(batch, ctx), block_size=block_size,
+        pool_factor=1.0, shared_prefix_blocks=shared_blocks * BLOCK // block_size,
         recipe=f"B={batch}, L={ctx}, shared prefix {shared_blocks} blocks, N(0,1)->bf16")
 
 
