@@ -118,20 +118,100 @@ __device__ __forceinline__ void store_chunk(T* dst, const float* o) {
 
 struct Item {
     int seq;
+    int item;  // index of the item (its partial-state slots)
     int row;
     int n;     // query rows of the sequence
     int i;     // this row's index among them
     bool skip; // left to the matrix-core kernel
 };
 
+// Inclusive sum over the kWaves*64 threads of a workgroup of one value per
+// thread.  `tmp` holds one int per wave; the caller synchronises before
+// reusing it.
+__device__ __forceinline__ int block_inclusive_sum(int v, int* tmp) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(v, o);
+        if (lane >= o) v += y;
+    }
+    if (lane == 63) tmp[w] = v;
+    __syncthreads();
+    int before = 0;
+    for (int i = 0; i < w; ++i) before += tmp[i];
+    return v + before;
+}
+
+// Longest-first order computed by every workgroup itself: the decode items
+// sorted by descending bucket min(L, max_context_len) >> rank_shift (kRank
+// buckets), equal buckets in index order.  Returns the item handled z-th.
+// The order is a function of the lengths alone, so all workgroups of a launch
+// agree on it; each pays one pass over the lengths (kRankKeep per thread, in
+// registers), a histogram in LDS and two workgroup-wide sums, instead of a
+// separate sorting launch ahead of the attention kernel.  Called by every
+// thread of the workgroup.
+constexpr int kRankBuckets = kWaves * 64;  // one bucket per thread
+constexpr int kRankKeep = 8;               // items per thread
+__device__ __forceinline__ int rank_select(const RowsArgs& a, int z) {
+    __shared__ int hist[kRankBuckets];
+    __shared__ int tmp[kWaves];
+    __shared__ int pick[2];
+    const int t = threadIdx.x;
+    const int n = a.num_items;
+    const int32_t* lens = a.context_lens + a.seq_begin;
+    // thread t owns items t*kRankKeep .. t*kRankKeep+kRankKeep-1: index order
+    // within a bucket follows thread order, then j
+    int pos[kRankKeep];  // position of the item's bucket, longest first; -1: no item
+#pragma unroll
+    for (int j = 0; j < kRankKeep; ++j) {
+        const int i = t * kRankKeep + j;
+        const int L = i < n ? lens[i] : 0;
+        const int key = min(min(max(L, 0), a.max_context_len) >> a.rank_shift, kRankBuckets - 1);
+        pos[j] = i < n ? kRankBuckets - 1 - key : -1;
+    }
+    hist[t] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kRankKeep; ++j)
+        if (pos[j] >= 0) atomicAdd(&hist[pos[j]], 1);
+    __syncthreads();
+    const int c = hist[t];
+    const int incl = block_inclusive_sum(c, tmp);
+    if (incl - c <= z && z < incl) {  // bucket t holds rank z
+        pick[0] = t;
+        pick[1] = z - (incl - c);
+    }
+    __syncthreads();
+    const int pb = pick[0], r = pick[1];
+    int m = 0;
+#pragma unroll
+    for (int j = 0; j < kRankKeep; ++j) m += pos[j] == pb;
+    const int incl2 = block_inclusive_sum(m, tmp);  // (every thread has read pick)
+    if (incl2 - m <= r && r < incl2) {              // the r-th item of bucket pb is here
+        int k = r - (incl2 - m);
+#pragma unroll
+        for (int j = 0; j < kRankKeep; ++j) {
+            if (pos[j] == pb) {
+                if (k == 0) pick[0] = t * kRankKeep + j;
+                --k;
+            }
+        }
+    }
+    __syncthreads();
+    return pick[0];
+}
+
 // Which sequence and q/out row grid index z stands for.  Decode items read
-// nothing but the optional processing order; the context length is loaded
-// separately so that its latency overlaps the first q and block-id loads.
+// nothing but the processing order (in-kernel ranking or an order array); the
+// context length is loaded separately so that its latency overlaps the first
+// q and block-id loads.
 __device__ __forceinline__ Item locate(const RowsArgs& a, int z, int group) {
     Item it;
     it.skip = false;
+    it.item = z;
     if (a.query_start_loc == nullptr) {
-        const int zz = a.order != nullptr ? a.order[z] : z;
+        const int zz = a.rank_shift >= 0 ? rank_select(a, z) : (a.order != nullptr ? a.order[z] : z);
+        it.item = zz;
         it.seq = a.seq_begin + zz;
         it.row = a.row_begin + zz;
         it.n = 1;
@@ -214,7 +294,7 @@ __device__ __forceinline__ void combine_waves(const RowsArgs& a, const Item& it,
             for (int e = 0; e < E; ++e) o[e] *= inv;
             store_chunk<T>(static_cast<T*>(a.out) + ((int64_t)it.row * Hq + hq) * D + cc * E, o);
         } else {
-            const int64_t slot = ((int64_t)z * Hq + hq) * a.nparts + part;
+            const int64_t slot = ((int64_t)it.item * Hq + hq) * a.nparts + part;
             float* wa = a.ws + slot * D + cc * E;
 #pragma unroll
             for (int e = 0; e < E; e += 4) st16(wa + e, make_uint4(__float_as_uint(o[e]), __float_as_uint(o[e + 1]),
@@ -679,7 +759,8 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a
 // out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
 // Rows whose context fits one partition were written by rows_kernel.  The
 // first eight partials are loaded before any reduction so that the loads
-// overlap instead of forming a chain.
+// overlap instead of forming a chain.  Partials are indexed by item, so the
+// merge runs in index order (its arguments carry no processing order).
 template <typename T, int D>
 __global__ __launch_bounds__(64) void merge_kernel(const RowsArgs a, int group) {
     constexpr int kPre = 8;
@@ -816,8 +897,11 @@ int32_t launch_typed(const RowsArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((rows_kernel<T, D, G>), dim3((unsigned)units), dim3(kWaves * 64), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
     if (split) {
+        RowsArgs m = a;  // index order
+        m.order = nullptr;
+        m.rank_shift = -1;
         hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.num_items, a.num_q_heads), dim3(64), 0,
-                           stream, a, G);
+                           stream, m, G);
         if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
     }
     return PA_OK;

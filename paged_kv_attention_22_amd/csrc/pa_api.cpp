@@ -121,9 +121,10 @@ int32_t small_rows_for(int32_t group) { return group >= 1 ? (kMfmaMinPairs - 1) 
 
 // Longest-first processing order for decode rows: with a ragged batch the
 // workgroups of the longest sequences start first and the short ones fill the
-// end, instead of a long sequence starting last and running alone.  Worth its
-// extra (one-workgroup) launch once the batch spans several waves of
-// workgroups.
+// end, instead of a long sequence starting last and running alone.  Used once
+// the batch spans several waves of workgroups.  Up to kRankMaxItems rows the
+// attention kernels derive the order themselves; larger batches get it from a
+// one-workgroup sorting launch (launch_plan) ahead of the attention kernel.
 bool use_plan(int64_t items, int32_t num_kv_heads, int32_t max_context_len, int32_t part) {
     const int64_t units = items * num_kv_heads * (part > 0 ? ceil_div(max_context_len, part) : 1);
     return items >= 16 && units >= 1024;
@@ -137,7 +138,8 @@ size_t rows_bytes(int64_t items, int32_t num_q_heads, int32_t num_kv_heads, int3
                   int32_t max_context_len, int32_t part, bool decode_rows) {
     if (items <= 0) return 0;
     size_t n = 0;
-    if (decode_rows && use_plan(items, num_kv_heads, max_context_len, part)) n += plan_bytes(items);
+    if (decode_rows && use_plan(items, num_kv_heads, max_context_len, part) && items > kRankMaxItems)
+        n += plan_bytes(items);  // order array of launch_plan
     return n + split_bytes(items, num_q_heads, head_dim, max_context_len, part);
 }
 
@@ -163,8 +165,12 @@ int32_t prepare_rows(RowsArgs& a, int64_t items, int32_t part, void* workspace,
         if (!aligned16(workspace)) return PA_ERR_ALIGN;
     }
     char* w = static_cast<char*>(workspace);
-    a.order = plan ? reinterpret_cast<int32_t*>(w) : nullptr;
-    a.ws = part > 0 ? reinterpret_cast<float*>(w + (plan ? plan_bytes(items) : 0)) : nullptr;
+    // Up to kRankMaxItems decode rows the attention kernels rank themselves;
+    // beyond that launch_plan writes the order into the workspace.
+    const bool order_array = plan && items > kRankMaxItems;
+    a.rank_shift = plan && !order_array ? rank_shift_for(a.max_context_len) : -1;
+    a.order = order_array ? reinterpret_cast<int32_t*>(w) : nullptr;
+    a.ws = part > 0 ? reinterpret_cast<float*>(w + (order_array ? plan_bytes(items) : 0)) : nullptr;
     return PA_OK;
 }
 

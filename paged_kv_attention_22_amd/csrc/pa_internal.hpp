@@ -45,6 +45,11 @@ struct RowsArgs {
     // Without query_start_loc: optional processing order, item order[z] is
     // handled z-th (longest first, written by launch_plan); NULL = index order.
     const int32_t* order;
+    // Without query_start_loc and order: rank_shift >= 0 makes each
+    // workgroup derive the longest-first order itself from the lengths
+    // (buckets min(L, max_context_len) >> rank_shift, at most kRankMaxItems
+    // items); -1: no ranking.
+    int32_t rank_shift;
     // With query_start_loc: items whose sequence gives at least this many
     // (row, head) pairs per kv head are left to the matrix-core kernel
     // (0 = handle every item here).
@@ -66,6 +71,16 @@ struct RowsArgs {
 };
 
 int32_t launch_rows(const RowsArgs& a, hipStream_t stream);
+
+// Most decode items the attention kernels rank themselves (256 threads x 8);
+// larger batches get their order from launch_plan.
+constexpr int32_t kRankMaxItems = 2048;
+// Bucket shift for in-kernel ranking: max_context_len >> shift < 256.
+inline int32_t rank_shift_for(int32_t max_context_len) {
+    int32_t shift = 0;
+    while ((max_context_len >> shift) >= 256) ++shift;
+    return shift;
+}
 
 // Counting sort of sequences seq_begin .. seq_begin+n-1 by context length,
 // longest first, into order[0..n) (indices relative to seq_begin).

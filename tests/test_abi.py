@@ -124,10 +124,14 @@ def test_partition_choice_and_workspace(pa):
     # many (row, kv head) units: one pass, longest first
     assert pa.decode_partition_tokens(256, 8, 2048, 0) == -1
     # workspace = the longest-first order (items int32, 256-byte aligned) when
-    # the batch is large, then items * Hq * nparts * (D + 2) fp32 partials
+    # the batch is larger than the kernels rank themselves (2048 rows), then
+    # items * Hq * nparts * (D + 2) fp32 partials
     n = -(-2048 // 256)
-    assert pa.decode_workspace_bytes(256, 16, 8, 128, 2048, 256) == 1024 + 256 * 16 * n * 130 * 4
-    assert pa.decode_workspace_bytes(256, 16, 8, 128, 2048, -1) == 1024
+    assert pa.decode_workspace_bytes(256, 16, 8, 128, 2048, 256) == 256 * 16 * n * 130 * 4
+    assert pa.decode_workspace_bytes(256, 16, 8, 128, 2048, -1) == 0
+    assert pa.decode_workspace_bytes(2048, 16, 8, 128, 2048, -1) == 0
+    assert pa.decode_workspace_bytes(2049, 16, 8, 128, 2048, -1) == 2049 * 4 + 252
+    assert pa.decode_workspace_bytes(3000, 4, 2, 64, 60, 64) == 12032 + 3000 * 4 * 1 * 66 * 4  # order: 12,000 bytes, 256-aligned
     assert pa.decode_workspace_bytes(4, 2, 1, 64, 64, -1) == 0     # small batch: nothing
 
 
