@@ -240,6 +240,83 @@ def bench_fused(args, b, up) -> dict:
     return res
 
 
+def bench_shared_prefix(args, b, up) -> dict:
+    """A decode step on a batch whose sequences share a prompt prefix (one
+    group, the generator's shared blocks): KV write + pa_decode_shared_prefix,
+    beside KV write + pa_decode on the same inputs.  Both attention calls are
+    timed with HIP events; the rate counts the shared blocks once."""
+    import numpy as np
+    import torch
+
+    import paged_kv_attention_22_amd as pa
+    if b.shared_prefix_tokens <= 0:
+        raise SystemExit("bench.py: --op shared_prefix needs a workload with a shared prefix (long_context)")
+    pools = [(up(b.k_pool), up(b.v_pool)) for _ in range(2)]
+    q, new_k, new_v, slots = up(b.q), up(b.new_k), up(b.new_v), up(b.slot_mapping)
+    tables, lens = up(b.block_tables), up(b.context_lens)
+    S, P = b.num_seqs, b.shared_prefix_tokens
+    gs = torch.tensor([0, S], dtype=torch.int32, device=q.device)
+    pl = torch.tensor([P], dtype=torch.int32, device=q.device)
+    out = torch.empty_like(q)
+    need = pa.decode_shared_prefix_workspace_bytes(S, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                                   b.max_context_len, 1, S, P, args.partition)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dws = torch.empty(max(pa.decode_workspace_bytes(S, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                                    b.max_context_len, args.partition), 1),
+                      dtype=torch.uint8, device=q.device)
+
+    def shared(i):
+        kp, vp = pools[i & 1]
+        pa.decode_shared_prefix(q, kp, vp, tables, lens, b.max_context_len, gs, pl, S, P, scale=b.scale,
+                                out=out, partition_tokens=args.partition, workspace=ws)
+
+    def plain(i):
+        kp, vp = pools[i & 1]
+        pa.decode(q, kp, vp, tables, lens, b.max_context_len, scale=b.scale, out=out,
+                  partition_tokens=args.partition, workspace=dws)
+
+    def step(i):
+        kp, vp = pools[i & 1]
+        pa.kv_write(new_k, new_v, slots, kp, vp)
+        shared(i)
+
+    log(f"[bench] timing pa_decode_shared_prefix and pa_decode ({args.steps} calls each)")
+    s_us = time_calls(shared, args.steps, args.warmup)
+    p_us = time_calls(plain, args.steps, args.warmup)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    dbytes, wbytes = decode_bytes(b), kv_write_bytes(b)
+    mean_s = float(np.mean(s_us)) * 1e-6
+    achieved = dbytes / mean_s / 1e9
+    return {
+        "metric": "pa_decode_shared_prefix HBM GB/s on unique K/V bytes (shared prefix read once)",
+        "value": round((dbytes + wbytes) / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": b.dtype,
+        "data": "synthetic",
+        "config": {"workload": b.name, "recipe": b.recipe, "seed": b.seed, "num_seqs": S,
+                   "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
+                   "block_size": int(b.k_pool.shape[1]), "shared_prefix_tokens": P,
+                   "max_context": b.max_context_len,
+                   "step": "pa_kv_write + pa_decode_shared_prefix (one group of every sequence)"},
+        "shared_prefix_us": {"mean": round(mean_s * 1e6, 2), "median": round(float(np.median(s_us)), 2),
+                             "p10": round(float(np.percentile(s_us, 10)), 2),
+                             "p90": round(float(np.percentile(s_us, 90)), 2)},
+        "pa_decode_us": {"mean": round(float(np.mean(p_us)), 2), "median": round(float(np.median(p_us)), 2)},
+        "roofline": {"kernel": "pa_decode_shared_prefix call: prefix chunk kernel + decode kernel + merge",
+                     "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": dbytes},
+        "cpu_baseline": None,
+    }
+
+
 def cpu_baseline(b, min_seconds: float = 10.0) -> dict:
     """The fp64 oracle on the same step (KV write + decode), one thread,
     repeated over the whole batch until at least min_seconds have passed."""
@@ -271,9 +348,10 @@ def main() -> int:
                     help="partition_tokens for pa_decode (0 = library choice, -1 = one pass)")
     ap.add_argument("--workload", default="qwen3_06b_decode",
                     help="generator preset (default: the Qwen3-0.6B batch-256 decode step)")
-    ap.add_argument("--op", default="step", choices=["step", "fused_write"],
+    ap.add_argument("--op", default="step", choices=["step", "fused_write", "shared_prefix"],
                     help="step: the workload's attention step (default); fused_write: "
-                         "pa_qkv_rope_write on the workload's new tokens")
+                         "pa_qkv_rope_write on the workload's new tokens; shared_prefix: "
+                         "pa_decode_shared_prefix on a workload whose sequences share a prefix")
     ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
                     help="tokens per pool block (16 is the pages' choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -322,6 +400,9 @@ def main() -> int:
 
     if args.op == "fused_write":
         print(json.dumps(bench_fused(args, b, up)), flush=True)
+        return 0
+    if args.op == "shared_prefix":
+        print(json.dumps(bench_shared_prefix(args, b, up)), flush=True)
         return 0
     if b.num_prefill_seqs:
         print(json.dumps(bench_mixed(args, b, up, dev)), flush=True)

@@ -28,7 +28,8 @@
  *   as `workspace`, sized by the matching *_workspace_bytes.  The only state it
  *   keeps is one auxiliary stream and two events per device, created by the
  *   first pa_prefill_chunk call that mixes matrix-core chunks with decode rows
- *   and kept for the life of the process (see pa_prefill_chunk).
+ *   (or the first pa_decode_shared_prefix call with a prefix) and kept for the
+ *   life of the process (see pa_prefill_chunk).
  * - Every call validates its host arguments first.  On failure it returns a
  *   non-zero pa_status, enqueues nothing and leaves every output untouched.
  * - On success the work is enqueued on `stream` (a hipStream_t; NULL means the
@@ -170,10 +171,12 @@ int32_t pa_qkv_rope_write(const void* qkv, int64_t qkv_token_stride,
  *                          kernel (log-sum-exp), which needs the workspace.
  *
  * pa_decode_partition_tokens returns the partition size the library uses for
- * these arguments (-1 = one pass).  pa_decode_workspace_bytes returns the
- * workspace pa_decode needs for the same arguments: the longest-first
- * processing order (num_seqs int32, 256-byte aligned) when the batch is large
- * enough to use one, then the split partials; 0 when neither is used.
+ * these arguments (-1 = one pass): one pass with at least 256 (sequence, kv
+ * head) units, else partitions that bring the launch to about 256 workgroups.
+ * pa_decode_workspace_bytes returns the workspace pa_decode needs for the same
+ * arguments: the longest-first processing order (num_seqs int32, 256-byte
+ * aligned) when the batch has more than 2048 sequences and uses one, then the
+ * split partials; 0 when neither is used.
  */
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                    int32_t max_context_len, int32_t partition_tokens);
@@ -201,6 +204,59 @@ int32_t pa_decode(const void* q, const void* k_pool, const void* v_pool,
                   int32_t max_context_len, int32_t num_q_heads, float scale,
                   void* out, int32_t partition_tokens,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_shared_prefix -- pa_decode for groups of sequences that share a
+ * prompt prefix (the blocks a prefix-cache hit points several block tables
+ * at: Capstone page, Week 5 -- Prefix caching; its acceptance criteria run
+ * many sequences at 8k context).  The result equals pa_decode's (within
+ * rounding: the sums are ordered differently), but each group's prefix is
+ * read from memory once for all its members instead of once per member.
+ *
+ * Arguments as pa_decode, plus:
+ * group_start     int32 device [num_groups + 1]: group g is sequences
+ *                 group_start[g] .. group_start[g+1]-1; group_start[0] = 0,
+ *                 nondecreasing, group_start[num_groups] = num_seqs (every
+ *                 sequence in one group; a group may hold one sequence)
+ * prefix_lens     int32 device [num_groups]: tokens of group g's shared
+ *                 prefix, taken in whole 16-token chunks (rounded down) and
+ *                 clamped to max_prefix_len; every member's first
+ *                 ceil(prefix/B) table entries must equal the group's first
+ *                 member's, and every member's context_len must be at least
+ *                 the prefix (0 = no shared prefix)
+ * max_group_size  host upper bound of the group sizes (1..num_seqs)
+ * max_prefix_len  host upper bound of prefix_lens (0..max_context_len)
+ * partition_tokens as pa_decode, for the keys after the prefix (which are
+ *                 always stored as partial states: -1 means one partition)
+ * workspace       pa_decode_shared_prefix_workspace_bytes(...) bytes,
+ *                 16-byte aligned (never zero)
+ *
+ * Work: the prefix of each group is attended on the matrix cores, the group's
+ * members as rows of one block that sees all of the prefix (split into key
+ * parts over workgroups), on the library's auxiliary stream (forked from and
+ * joined back into `stream`); the rest of each context runs on the decode path
+ * on `stream`; a log-sum-exp merge on `stream` combines the partial states.
+ * Supported: bf16 or fp16 pools (the matrix cores), group size 1..8.
+ * Preconditions on the group arrays are not checked beyond memory safety:
+ * rows of groups larger than max_group_size, or groups that overlap, give
+ * unspecified values.
+ */
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t max_context_len, int32_t num_groups,
+                                               int32_t max_group_size, int32_t max_prefix_len,
+                                               int32_t partition_tokens);
+
+int32_t pa_decode_shared_prefix(const void* q, const void* k_pool, const void* v_pool,
+                                pa_pool_desc pool,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs,
+                                int32_t max_context_len,
+                                const int32_t* group_start, const int32_t* prefix_lens,
+                                int32_t num_groups, int32_t max_group_size,
+                                int32_t max_prefix_len, int32_t num_q_heads, float scale,
+                                void* out, int32_t partition_tokens,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pa_prefill_chunk -- causal attention for a packed mixed batch.

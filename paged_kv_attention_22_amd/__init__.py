@@ -46,6 +46,10 @@ _SIGNATURES = {
     "pa_decode_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (c_i32, [c_vp, c_vp, c_vp, PoolDesc, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
                           c_f, c_vp, c_i32, c_vp, c_size, c_vp]),
+    "pa_decode_shared_prefix_workspace_bytes": (c_size, [c_i32] * 9),
+    "pa_decode_shared_prefix": (c_i32, [c_vp, c_vp, c_vp, PoolDesc, c_vp, c_i32, c_vp, c_i32, c_i32,
+                                        c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_f, c_vp, c_i32,
+                                        c_vp, c_size, c_vp]),
     "pa_qkv_rope_write": (c_i32, [c_vp, c_i64, c_vp, c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_f,
                                   c_vp, c_vp, c_f, c_vp, c_vp, c_vp, PoolDesc, c_vp, c_vp]),
     "pa_prefill_workspace_bytes": (c_size, [c_i32] * 8),
@@ -216,6 +220,42 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale
                          int(max_context_len), Hq, float(scale), _contig(out, "out"),
                          int(partition_tokens), wp, wb, _stream(stream))
     _check(st, "pa_decode")
+    return out
+
+
+def decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                         num_groups, max_group_size, max_prefix_len,
+                                         partition_tokens=0) -> int:
+    return lib().pa_decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                         max_context_len, num_groups, max_group_size,
+                                                         max_prefix_len, partition_tokens)
+
+
+def decode_shared_prefix(q, k_pool, v_pool, block_tables, context_lens, max_context_len, group_start,
+                         prefix_lens, max_group_size, max_prefix_len, scale=None, out=None,
+                         partition_tokens=0, workspace=None, stream=None):
+    """Decode attention for groups of sequences sharing a prompt prefix:
+    group g is sequences group_start[g] .. group_start[g+1]-1 (int32 device
+    tensor [G+1]) sharing their first prefix_lens[g] tokens (int32 device
+    [G]).  Same result as decode() within rounding."""
+    S, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    hkv = k_pool.shape[2]
+    ng = group_start.shape[0] - 1
+    need = decode_shared_prefix_workspace_bytes(S, Hq, hkv, D, max_context_len, ng, max_group_size,
+                                                max_prefix_len, partition_tokens)
+    wp, wb = _workspace(need, workspace, q.device)
+    st = lib().pa_decode_shared_prefix(_contig(q, "q"), _contig(k_pool, "k_pool"), _contig(v_pool, "v_pool"),
+                                       pool_desc(k_pool), _i32(block_tables, "block_tables"),
+                                       block_tables.shape[1], _i32(context_lens, "context_lens"), S,
+                                       int(max_context_len), _i32(group_start, "group_start"),
+                                       _i32(prefix_lens, "prefix_lens"), ng, int(max_group_size),
+                                       int(max_prefix_len), Hq, float(scale), _contig(out, "out"),
+                                       int(partition_tokens), wp, wb, _stream(stream))
+    _check(st, "pa_decode_shared_prefix")
     return out
 
 

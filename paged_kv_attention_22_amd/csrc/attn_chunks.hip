@@ -30,6 +30,13 @@
 // Two LDS buffers per key half: the next tile is written while the current
 // one is read, one barrier per tile; the tile after that is already loading
 // from memory.
+//
+// The same kernel attends a prefix shared by a group of decode sequences: the
+// group's members are the "chunk" rows (one token each), every row sees all
+// of the prefix (no causal limit), the keys come through the group's first
+// member's table, the keys are split into parts over workgroups, and each
+// part leaves its softmax state (m, l, unnormalised acc) as a partial for the
+// log-sum-exp merge instead of writing the output.
 #include "pa_device.hpp"
 #include "pa_internal.hpp"
 
@@ -166,17 +173,22 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
     __shared__ __align__(16) unsigned char lds_v[KSPLIT * 2 * VTILE];
 
     const int s = blockIdx.z, g = blockIdx.y;
+    const int nkp = max(a.key_parts, 1);
+    const int kp = blockIdx.x % nkp;  // key part (0 unless keys are split)
     const int G = a.num_q_heads / a.num_kv_heads;
     const int qs = a.query_start_loc[s];
     const int n = a.query_start_loc[s + 1] - qs;
     const int rows = n * G;
     if (rows < a.min_pairs) return;  // the vector path handles this sequence
-    const int row0 = blockIdx.x * kRowsPerGroup;
+    const int row0 = blockIdx.x / nkp * kRowsPerGroup;
     if (row0 >= rows) return;
     const int bsh = a.block_shift;  // pool blocks of 1 << bsh tokens
     const int cap = (int)min((int64_t)a.max_context_len, (int64_t)a.max_blocks << bsh);
-    const int L = min(max(a.context_lens[s], 0), cap);
-    const int prior = L - n;  // keys before the chunk
+    const bool causal = a.causal != 0;
+    // without a causal limit (a shared prefix) the keys are taken in whole
+    // 16-token chunks: the decode kernels take the rest from that chunk on
+    const int L = min(max(a.context_lens[s], 0), cap) & (causal ? ~0 : ~15);
+    const int prior = causal ? L - n : L;  // keys before the chunk (all L without a causal limit)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform branches below
@@ -194,21 +206,31 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
         row_ok[nt] = R < rows;
         trow[nt] = R / G;
         hh[nt] = R - trow[nt] * G;
-        lim[nt] = prior + trow[nt];  // last visible key of the row
+        lim[nt] = causal ? prior + trow[nt] : L - 1;  // last visible key of the row
     }
 
-    // Keys this workgroup / this wave needs.
+    // Keys this workgroup / this wave needs: 0 .. kend-1 in all, of which this
+    // workgroup's key part takes kb .. ke-1 (whole tiles: parts are multiples
+    // of the tile).
     const int last_row = min(row0 + kRowsPerGroup, rows) - 1;
-    const int kend = min(prior + last_row / G + 1, L);
-    const int ntiles = kend > 0 ? (kend + kKeys - 1) / kKeys : 0;
-    const int wkend = wrow0 < rows ? min(prior + (min(wrow0 + kRowsPerWave, rows) - 1) / G + 1, L) : 0;
-    const int wlim_min = prior + wrow0 / G;  // smallest last-visible key among the wave's rows
+    const int kend = causal ? min(prior + last_row / G + 1, L) : L;
+    const int kb = nkp > 1 ? kp * a.key_part_tokens : 0;
+    const int ke = nkp > 1 ? min(kb + a.key_part_tokens, kend) : kend;
+    const int tbase = kb / kKeys;
+    const int ntiles = ke > kb ? (ke - kb + kKeys - 1) / kKeys : 0;
+    if (a.partials != nullptr && ntiles == 0) return;  // no keys in this part: the merge skips it
+    const int wkend = wrow0 < rows
+                          ? min(causal ? min(prior + (min(wrow0 + kRowsPerWave, rows) - 1) / G + 1, L) : L, ke)
+                          : 0;
+    // smallest last-visible key among the wave's rows
+    const int wlim_min = causal ? prior + wrow0 / G : L - 1;
 
     // The block table is read-only for the whole kernel: reading it through
     // the constant address space makes the (wave-uniform) id loads scalar, so
     // they do not queue behind the K/V loads.
     typedef __attribute__((address_space(4))) const int32_t const_i32;
-    const const_i32* bt = (const const_i32*)(a.block_tables + (int64_t)s * a.max_blocks);
+    const int trow_of_table = a.table_row_qsl ? qs : s;  // a group's keys: its first member's table
+    const const_i32* bt = (const const_i32*)(a.block_tables + (int64_t)trow_of_table * a.max_blocks);
 
     const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
     const T* q = static_cast<const T*>(a.q);
@@ -257,7 +279,7 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
     const unsigned char* kbase = static_cast<const unsigned char*>(a.k_pool);
     const unsigned char* vbase = static_cast<const unsigned char*>(a.v_pool);
     auto load_tile = [&](int tile, uint4 (&kr)[LOADS], uint4 (&vr)[LOADS]) {
-        const int j0 = min(tile, ntiles - 1) * kKeys;
+        const int j0 = (tbase + min(tile, ntiles - 1)) * kKeys;
         int blk[LOADS];
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {  // scalar loads first, one wait for all
@@ -447,7 +469,7 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
                 qf[nt][ks] = as_v8(v);
             }
         }
-        store_tile(0, half * kKeys, tile0k, tile0v);
+        store_tile(0, (tbase + half) * kKeys, tile0k, tile0v);
         __syncthreads();
         const int hsteps = (ntiles + KSPLIT - 1) / KSPLIT;
         const int nsteps = (hsteps + DEPTH - 1) / DEPTH * DEPTH;
@@ -456,8 +478,8 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
             for (int r = 0; r < DEPTH; ++r) {  // unrolled: static register buffers
                 const int i = i0 + r;
                 const int tile = half + KSPLIT * i;
-                compute_tile(tile * kKeys, i & 1);
-                store_tile((i + 1) & 1, (tile + KSPLIT) * kKeys, kreg[r], vreg[r]);
+                compute_tile((tbase + tile) * kKeys, i & 1);
+                store_tile((i + 1) & 1, (tbase + tile + KSPLIT) * kKeys, kreg[r], vreg[r]);
                 load_tile(tile + KSPLIT * (1 + DEPTH), kreg[r], vreg[r]);
                 __syncthreads();
             }
@@ -498,9 +520,32 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     acc[nt][mt][r] = acc[nt][mt][r] * a0 + x[(2 + mt * 4 + r) * kStride] * a1;
+            m[nt] = M;  // the reference of the merged state (a partial carries it)
         }
     }
 
+    if (a.partials != nullptr) {
+        // Partial state of the key part: unnormalised acc, the reference max
+        // m (log2 units) and the sum l, in the layout the merge reads.
+        const int64_t nslots = (int64_t)a.num_items * Hq * a.part_slots;
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            const float l = sum_across_row_lanes(lsum[nt]);
+            const int item = qs + trow[nt];
+            if (!row_ok[nt] || item < 0 || item >= a.num_items) continue;
+            const int64_t slot = ((int64_t)item * Hq + g * G + hh[nt]) * a.part_slots + kp;
+            float* pa = a.partials + slot * D + kg * 4;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                st16(pa + mt * 16, make_uint4(__float_as_uint(acc[nt][mt][0]), __float_as_uint(acc[nt][mt][1]),
+                                              __float_as_uint(acc[nt][mt][2]), __float_as_uint(acc[nt][mt][3])));
+            if (kg == 0) {
+                a.partials[nslots * D + slot] = m[nt];
+                a.partials[nslots * D + nslots + slot] = l;
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
         const float l = sum_across_row_lanes(lsum[nt]);
@@ -539,9 +584,10 @@ int32_t launch_chunks(const ChunkArgs& a, hipStream_t stream) {
     if (!chunks_supported(a.dtype, a.head_dim, group)) return PA_ERR_UNSUPPORTED;
     if (a.num_seqs == 0 || a.max_query_len == 0) return PA_OK;
     const int64_t rows = (int64_t)a.max_query_len * group;
-    const int64_t small_tiles = (rows + kRowsSmall - 1) / kRowsSmall;
-    const bool small = small_tiles * a.num_kv_heads * a.num_seqs < kSplitBelow;
-    const int64_t tiles = small ? small_tiles : (rows + kRowsLarge - 1) / kRowsLarge;
+    const int64_t kparts = a.key_parts > 1 ? a.key_parts : 1;
+    const int64_t small_tiles = (rows + kRowsSmall - 1) / kRowsSmall * kparts;
+    const bool small = !a.prefer_large && small_tiles * a.num_kv_heads * a.num_seqs < kSplitBelow;
+    const int64_t tiles = small ? small_tiles : (rows + kRowsLarge - 1) / kRowsLarge * kparts;
     if (tiles > INT32_MAX || a.num_seqs > 65535) return PA_ERR_SHAPE;
     const dim3 grid((unsigned)tiles, a.num_kv_heads, a.num_seqs);
     const dim3 block(kRowWaves * (small ? 2 : 1) * 64);

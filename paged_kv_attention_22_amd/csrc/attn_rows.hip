@@ -242,6 +242,18 @@ __device__ __forceinline__ Item locate(const RowsArgs& a, int z, int group) {
     return it;
 }
 
+// Shared-prefix mode: 16-token chunks of the prefix of sequence seq's group
+// (the last group g with group_start[g] <= seq), which the chunk kernel has
+// attended; the decode kernels start after them.
+__device__ __forceinline__ int prefix_chunks(const RowsArgs& a, int seq) {
+    int lo = 0, hi = a.num_groups - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a.group_start[mid] <= seq) lo = mid; else hi = mid - 1;
+    }
+    return min(max(a.prefix_lens[lo], 0), a.prefix_cap) >> 4;
+}
+
 // Keys visible to the row: 0 .. L-n+i, with L clamped to what the table holds.
 __device__ __forceinline__ int visible_len(const RowsArgs& a, const Item& it, int L) {
     const int cap = (int)min((int64_t)a.max_context_len, (int64_t)a.max_blocks << a.block_shift);
@@ -254,7 +266,7 @@ __device__ __forceinline__ int visible_len(const RowsArgs& a, const Item& it, in
 // the pool (each head a 2*D-byte slice of every row) at about the same time.
 __device__ __forceinline__ void unit_of(const RowsArgs& a, int& z, int& g, int& part) {
     const int id = blockIdx.x;
-    const int nparts = a.part_tokens > 0 ? a.nparts : 1;
+    const int nparts = a.part_tokens > 0 ? a.nparts - a.prefix_slots : 1;  // partitions launched
     g = id % a.num_kv_heads;
     const int rest = id / a.num_kv_heads;
     part = rest % nparts;
@@ -331,7 +343,9 @@ __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
     if (it.skip) return;
     const bool split = a.part_tokens > 0;
     const int pb = split ? a.part_tokens / kBlock : 0;
-    const int b0 = split ? part * pb : 0;
+    // shared-prefix mode: the chunks after the group's prefix, always split
+    const bool cascade = a.group_start != nullptr;
+    const int b0 = (cascade ? prefix_chunks(a, it.seq) : 0) + (split ? part * pb : 0);
     const int first = b0 + wave;  // this wave's blocks: first + k*kWaves
 
     // Issue the length, q and first block-id loads together.
@@ -365,8 +379,9 @@ __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
     bool final_out = true;
     if (split) {
         b1 = min(nblk, b0 + pb);
-        if (b0 >= b1 && !(part == 0 && nblk == 0)) return;  // the merge ignores missing partitions
-        final_out = nblk <= pb;  // a single partition writes the output itself
+        // the merge ignores missing partitions
+        if (b0 >= b1 && (cascade || !(part == 0 && nblk == 0))) return;
+        final_out = !cascade && nblk <= pb;  // a single partition writes the output itself
     }
 
     float m[G], l[G], acc[G][EL];
@@ -520,7 +535,7 @@ __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
         }
     }
     __syncthreads();
-    combine_waves<T, D, G>(a, it, z, g, part, final_out, s_acc, s_m, s_l);
+    combine_waves<T, D, G>(a, it, z, g, a.prefix_slots + part, final_out, s_acc, s_m, s_l);
 }
 
 // Decode rows on the matrix cores, for large GQA groups (bf16).  Same work
@@ -564,7 +579,9 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a
     if (it.skip) return;
     const bool split = a.part_tokens > 0;
     const int pb = split ? a.part_tokens / kBlock : 0;
-    const int b0 = split ? part * pb : 0;
+    // shared-prefix mode: the chunks after the group's prefix, always split
+    const bool cascade = a.group_start != nullptr;
+    const int b0 = (cascade ? prefix_chunks(a, it.seq) : 0) + (split ? part * pb : 0);
 
     const int Lraw = a.context_lens[it.seq];
     const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
@@ -596,8 +613,8 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a
     bool final_out = true;
     if (split) {
         b1 = min(nblk, b0 + pb);
-        if (b0 >= b1 && !(part == 0 && nblk == 0)) return;
-        final_out = nblk <= pb;
+        if (b0 >= b1 && (cascade || !(part == 0 && nblk == 0))) return;
+        final_out = !cascade && nblk <= pb;
     }
     // Steps of this wave: pair k covers blocks jb = b0 + 2*(wave + k*kWaves)
     // and jb + 1; the steps with both blocks full come first, then at most one
@@ -752,7 +769,7 @@ __global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a
         }
     }
     __syncthreads();
-    combine_waves<T, D, G>(a, it, z, g, part, final_out, s_acc, s_m, s_l);
+    combine_waves<T, D, G>(a, it, z, g, a.prefix_slots + part, final_out, s_acc, s_m, s_l);
 }
 
 // Log-sum-exp merge of the partitions of one (row, q head):
@@ -770,8 +787,18 @@ __global__ __launch_bounds__(64) void merge_kernel(const RowsArgs a, int group) 
     const int len = visible_len(a, it, a.context_lens[it.seq]);
     const int pb = a.part_tokens / kBlock;
     const int nblk = (len + kBlock - 1) / kBlock;
-    const int np = (nblk + pb - 1) / pb;
-    if (np <= 1) return;
+    // Partials: npre of the shared prefix (slots 0..npre-1, shared-prefix mode
+    // only), then nsuf of the rest (slots prefix_slots..).
+    int npre = 0, c0 = 0;
+    if (a.group_start != nullptr) {
+        const int pch = prefix_chunks(a, it.seq);
+        npre = (pch * kBlock + a.prefix_part_tokens - 1) / a.prefix_part_tokens;
+        c0 = min(pch, nblk);
+    }
+    const int nsuf = (nblk - c0 + pb - 1) / pb;
+    const int np = npre + nsuf;
+    if (a.group_start == nullptr && np <= 1) return;  // written by the attention kernel
+    auto slot_of = [&](int p) { return p < npre ? p : a.prefix_slots + p - npre; };
     const int Hq = a.num_q_heads;
     const int lane = threadIdx.x;
     const int64_t slot0 = ((int64_t)z * Hq + hq) * a.nparts;
@@ -784,15 +811,15 @@ __global__ __launch_bounds__(64) void merge_kernel(const RowsArgs a, int group) 
     float2 v[kPre];
 #pragma unroll
     for (int u = 0; u < kPre; ++u)
-        v[u] = u < np ? *reinterpret_cast<const float2*>(acc + (int64_t)u * D + d) : make_float2(0.0f, 0.0f);
+        v[u] = u < np ? *reinterpret_cast<const float2*>(acc + (int64_t)slot_of(u) * D + d) : make_float2(0.0f, 0.0f);
     float M = kNegInf;
-    for (int p = lane; p < np; p += 64) M = fmaxf(M, ms[p]);
+    for (int p = lane; p < np; p += 64) M = fmaxf(M, ms[slot_of(p)]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     const float mref = (M == kNegInf) ? 0.0f : M;
     float den = 0.0f, wl = 0.0f;
-    for (int p = lane; p < np; p += 64) den = fmaf(ls[p], fast_exp2(ms[p] - mref), den);
-    if (lane < np) wl = fast_exp2(ms[lane] - mref);  // weight of partial `lane`
+    for (int p = lane; p < np; p += 64) den = fmaf(ls[slot_of(p)], fast_exp2(ms[slot_of(p)] - mref), den);
+    if (lane < np) wl = fast_exp2(ms[slot_of(lane)] - mref);  // weight of partial `lane`
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
@@ -805,8 +832,8 @@ __global__ __launch_bounds__(64) void merge_kernel(const RowsArgs a, int group) 
         o1 = fmaf(v[u].y, wt, o1);
     }
     for (int p = kPre; p < np; ++p) {
-        const float wt = fast_exp2(ms[p] - mref);
-        const float2 w = *reinterpret_cast<const float2*>(acc + (int64_t)p * D + d);
+        const float wt = fast_exp2(ms[slot_of(p)] - mref);
+        const float2 w = *reinterpret_cast<const float2*>(acc + (int64_t)slot_of(p) * D + d);
         o0 = fmaf(w.x, wt, o0);
         o1 = fmaf(w.y, wt, o1);
     }
@@ -886,24 +913,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* conte
         order[atomicAdd(&start[key_of(i)], 1)] = i;
 }
 
+template <typename T, int D>
+int32_t launch_merge_typed(const RowsArgs& a, int group, hipStream_t stream) {
+    RowsArgs m = a;  // index order
+    m.order = nullptr;
+    m.rank_shift = -1;
+    hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.num_items, a.num_q_heads), dim3(64), 0, stream, m, group);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
 template <typename T, int D, int G>
 int32_t launch_typed(const RowsArgs& a, hipStream_t stream) {
     const bool split = a.part_tokens > 0;
-    const int64_t units = (int64_t)a.num_items * a.num_kv_heads * (split ? a.nparts : 1);
+    const int64_t units = (int64_t)a.num_items * a.num_kv_heads * (split ? a.nparts - a.prefix_slots : 1);
     if (units > INT32_MAX) return PA_ERR_SHAPE;
     if constexpr (kIs16<T> && G >= kMfmaMinGroup)
         hipLaunchKernelGGL((mfma_rows_kernel<T, D, G>), dim3((unsigned)units), dim3(kWaves * 64), 0, stream, a);
     else
         hipLaunchKernelGGL((rows_kernel<T, D, G>), dim3((unsigned)units), dim3(kWaves * 64), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
-    if (split) {
-        RowsArgs m = a;  // index order
-        m.order = nullptr;
-        m.rank_shift = -1;
-        hipLaunchKernelGGL((merge_kernel<T, D>), dim3(a.num_items, a.num_q_heads), dim3(64), 0,
-                           stream, m, G);
-        if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
-    }
+    if (split && !a.defer_merge) return launch_merge_typed<T, D>(a, G, stream);
     return PA_OK;
 }
 
@@ -932,6 +961,22 @@ int32_t launch_plan(const int32_t* context_lens, int32_t seq_begin, int32_t n,
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, context_lens, seq_begin, n,
                        max_context_len, shift, order);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int32_t launch_merge(const RowsArgs& a, hipStream_t stream) {
+    if (a.num_items == 0 || a.part_tokens <= 0) return PA_OK;
+    const int group = a.num_q_heads / a.num_kv_heads;
+    if (a.dtype == PA_BF16) {
+        if (a.head_dim == 64) return launch_merge_typed<uint16_t, 64>(a, group, stream);
+        if (a.head_dim == 128) return launch_merge_typed<uint16_t, 128>(a, group, stream);
+    } else if (a.dtype == PA_F16) {
+        if (a.head_dim == 64) return launch_merge_typed<_Float16, 64>(a, group, stream);
+        if (a.head_dim == 128) return launch_merge_typed<_Float16, 128>(a, group, stream);
+    } else if (a.dtype == PA_F32) {
+        if (a.head_dim == 64) return launch_merge_typed<float, 64>(a, group, stream);
+        if (a.head_dim == 128) return launch_merge_typed<float, 128>(a, group, stream);
+    }
+    return PA_ERR_UNSUPPORTED;
 }
 
 int32_t launch_rows(const RowsArgs& a, hipStream_t stream) {

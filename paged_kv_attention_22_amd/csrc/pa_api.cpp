@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "pa_internal.hpp"
@@ -12,9 +13,10 @@ using namespace pa;
 
 namespace {
 
-// Auxiliary stream of one device: pa_prefill_chunk runs the matrix-core chunk
-// kernel on it, concurrently with the decode rows on the caller's stream
-// (forked from and joined back into the caller's stream with the two events).
+// Auxiliary stream of one device: pa_prefill_chunk and pa_decode_shared_prefix
+// run the matrix-core chunk kernel on it, concurrently with the decode kernels
+// on the caller's stream (forked from and joined back into the caller's stream
+// with the two events).
 // Created on first use, kept for the life of the process; the mutex makes the
 // record / wait / launch sequence atomic across host threads.
 struct AuxStream {
@@ -87,27 +89,33 @@ int32_t check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
-// Split-context choice.  With at least 1024 (row, kv head) units the batch
-// already covers the 256 compute units several times over: one pass, with the
-// longest-first order keeping the tail short.  Fewer units (few sequences,
-// long contexts) are split into partitions, the longest that still give about
-// 1024 workgroups (longer partitions keep each wave streaming longer; shorter
-// ones add partial-state traffic and merge work).
+// Split-context choice.  One workgroup of the decode kernels per compute unit
+// already streams at close to the chip's rate (measured: 256 (row, kv head)
+// units of 4-8k tokens each in one pass beat every split of them), so a batch
+// with at least 256 units runs in one pass.  Fewer units (few sequences, long
+// contexts) are split into as many partitions as bring the launch to about 256
+// workgroups; more partitions only add per-workgroup start-up, partial-state
+// traffic and merge work (measured at 32-128 units: the best split always gave
+// about 256 workgroups).
+constexpr int64_t kSplitTarget = 256;
 int32_t choose_partition(int64_t items, int32_t num_kv_heads, int32_t max_context_len,
                          int32_t requested) {
     if (requested < 0) return -1;
     if (requested > 0) return requested;
     const int64_t units = items * num_kv_heads;
-    if (units >= 1024 || max_context_len <= 128) return -1;
-    int32_t part = 2048;
-    while (part > 64 && units * ceil_div(max_context_len, part) < 1024) part /= 2;
+    if (units >= kSplitTarget || max_context_len <= 128) return -1;
+    const int64_t parts = ceil_div(kSplitTarget, units);
+    const int32_t part = std::max<int32_t>(64, (ceil_div(max_context_len, parts) + 15) / 16 * 16);
     return ceil_div(max_context_len, part) > 1 ? part : -1;
 }
 
+// Partial states of a split launch: items * Hq * slots * (acc[D], m, l) fp32,
+// slots = the partitions of the context plus extra_slots in front (the key
+// parts of a shared prefix).
 size_t split_bytes(int64_t items, int32_t num_q_heads, int32_t head_dim,
-                   int32_t max_context_len, int32_t part) {
+                   int32_t max_context_len, int32_t part, int32_t extra_slots = 0) {
     if (part <= 0 || items <= 0) return 0;
-    const int64_t nparts = ceil_div(max_context_len, part);
+    const int64_t nparts = ceil_div(max_context_len, part) + extra_slots;
     return (size_t)(items * num_q_heads * nparts * (int64_t)(head_dim + 2) * 4);
 }
 
@@ -135,12 +143,12 @@ size_t plan_bytes(int64_t items) { return align256((size_t)items * 4); }
 // Workspace of one vector-path launch: [order (decode rows, when planned)]
 // [split partials].
 size_t rows_bytes(int64_t items, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                  int32_t max_context_len, int32_t part, bool decode_rows) {
+                  int32_t max_context_len, int32_t part, bool decode_rows, int32_t extra_slots = 0) {
     if (items <= 0) return 0;
     size_t n = 0;
     if (decode_rows && use_plan(items, num_kv_heads, max_context_len, part) && items > kRankMaxItems)
         n += plan_bytes(items);  // order array of launch_plan
-    return n + split_bytes(items, num_q_heads, head_dim, max_context_len, part);
+    return n + split_bytes(items, num_q_heads, head_dim, max_context_len, part, extra_slots);
 }
 
 int32_t check_partition(int32_t requested) {
@@ -151,15 +159,16 @@ int32_t check_partition(int32_t requested) {
 // Fills the common part of a RowsArgs and checks the workspace.  Decode rows
 // (no query_start_loc) may get a longest-first order in front of the partials.
 int32_t prepare_rows(RowsArgs& a, int64_t items, int32_t part, void* workspace,
-                     size_t workspace_bytes) {
+                     size_t workspace_bytes, int32_t extra_slots = 0) {
     a.num_items = (int32_t)items;
     a.part_tokens = part;
-    a.nparts = part > 0 ? ceil_div(a.max_context_len, part) : 1;
+    a.nparts = part > 0 ? ceil_div(a.max_context_len, part) + extra_slots : 1;
+    a.prefix_slots = part > 0 ? extra_slots : 0;
     if (part > 0 && a.nparts > 65535) return PA_ERR_SHAPE;
     const bool decode_rows = a.query_start_loc == nullptr;
     const bool plan = decode_rows && use_plan(items, a.num_kv_heads, a.max_context_len, part);
     const size_t need = rows_bytes(items, a.num_q_heads, a.num_kv_heads, a.head_dim,
-                                   a.max_context_len, part, decode_rows);
+                                   a.max_context_len, part, decode_rows, extra_slots);
     if (need > 0) {
         if (workspace == nullptr || workspace_bytes < need) return PA_ERR_WORKSPACE;
         if (!aligned16(workspace)) return PA_ERR_ALIGN;
@@ -339,6 +348,171 @@ int32_t pa_qkv_rope_write(const void* qkv, int64_t qkv_token_stride,
     return launch_qkv_write(a, static_cast<hipStream_t>(stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Launch plan of a shared-prefix decode.
+struct CascadePlan {
+    int32_t prefix_part;   // keys per part of the prefix phase (multiple of 64), 0: no prefix phase
+    int32_t prefix_slots;  // key parts of the longest prefix
+    int32_t part;          // partition of the keys after the prefix (multiple of 16)
+    size_t bytes;          // workspace
+};
+
+// The prefix phase (matrix cores) runs beside the decode kernel, which keeps
+// about one workgroup per compute unit streaming from memory: its key range is
+// split into parts of at least 256 keys until it has about 128 workgroups of
+// 128 rows (row tiles x kv heads x groups x parts), few enough parts to keep
+// the merge short.  The keys after the prefix are split as pa_decode would
+// split the whole context (one partition when it would not split), always
+// into partial states that the merge combines with the prefix's.
+CascadePlan cascade_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t max_context_len, int32_t num_groups, int32_t max_group_size,
+                         int32_t prefix_cap, int32_t partition_tokens) {
+    CascadePlan p = {};
+    const int32_t group = num_q_heads / num_kv_heads;
+    const int32_t plen = prefix_cap & ~15;
+    if (plen > 0) {
+        const int64_t row_tiles = ceil_div((int64_t)max_group_size * group, 128);
+        const int64_t tiles = ceil_div(plen, 64);
+        const int64_t base = row_tiles * num_kv_heads * num_groups;
+        int64_t parts = ceil_div(128, base);
+        parts = std::max<int64_t>(1, std::min<int64_t>(parts, tiles / 4));
+        p.prefix_part = (int32_t)(64 * ceil_div(tiles, parts));
+        p.prefix_slots = ceil_div(plen, p.prefix_part);
+    }
+    int32_t part = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_tokens);
+    if (part <= 0) part = std::max(16, (max_context_len + 15) / 16 * 16);
+    p.part = part;
+    p.bytes = rows_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, part, true,
+                         p.prefix_slots);
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t max_context_len, int32_t num_groups,
+                                               int32_t max_group_size, int32_t max_prefix_len,
+                                               int32_t partition_tokens) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+        num_groups <= 0 || max_group_size <= 0 || max_prefix_len < 0 || max_prefix_len > max_context_len ||
+        num_q_heads % num_kv_heads != 0 || check_partition(partition_tokens))
+        return 0;
+    return cascade_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, num_groups,
+                        max_group_size, max_prefix_len, partition_tokens).bytes;
+}
+
+int32_t pa_decode_shared_prefix(const void* q, const void* k_pool, const void* v_pool, pa_pool_desc pool,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                                const int32_t* group_start, const int32_t* prefix_lens, int32_t num_groups,
+                                int32_t max_group_size, int32_t max_prefix_len, int32_t num_q_heads,
+                                float scale, void* out, int32_t partition_tokens, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    if (int32_t st = check_pool(pool)) return st;
+    if (int32_t st = check_heads(num_q_heads, pool.num_kv_heads)) return st;
+    if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
+        (int64_t)max_context_len > (int64_t)max_blocks_per_seq * pool.block_size)
+        return PA_ERR_SHAPE;
+    if (int32_t st = check_partition(partition_tokens)) return st;
+    if (num_seqs == 0) return PA_OK;
+    if (num_groups <= 0 || num_groups > num_seqs || num_groups > 65535 || max_group_size <= 0 ||
+        max_group_size > num_seqs || max_prefix_len < 0 || max_prefix_len > max_context_len)
+        return PA_ERR_SHAPE;
+    const int32_t group = num_q_heads / pool.num_kv_heads;
+    if (!chunks_supported(pool.dtype, pool.head_dim, group)) return PA_ERR_UNSUPPORTED;
+    if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out || !group_start || !prefix_lens)
+        return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_ALIGN;
+
+    const int32_t prefix_cap = (int32_t)std::min<int64_t>(max_prefix_len, (int64_t)max_blocks_per_seq * pool.block_size);
+    const CascadePlan cp = cascade_plan(num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim, max_context_len,
+                                        num_groups, max_group_size, prefix_cap, partition_tokens);
+    RowsArgs a = {};
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_tables = block_tables;
+    a.max_blocks = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.query_start_loc = nullptr;
+    a.seq_begin = 0;
+    a.seq_end = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = pool.num_kv_heads;
+    a.head_dim = pool.head_dim;
+    a.num_blocks = pool.num_blocks;
+    a.block_shift = block_shift_of(pool.block_size);
+    a.dtype = pool.dtype;
+    a.max_context_len = max_context_len;
+    a.scale = scale;
+    a.out = out;
+    a.group_start = group_start;
+    a.prefix_lens = prefix_lens;
+    a.num_groups = num_groups;
+    a.prefix_cap = prefix_cap;
+    a.prefix_part_tokens = cp.prefix_part > 0 ? cp.prefix_part : 64;
+    if (int32_t st = prepare_rows(a, num_seqs, cp.part, workspace, workspace_bytes, cp.prefix_slots)) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (cp.prefix_slots == 0) return run_rows(a, s);
+    {
+        // Prefix phase: each group's members are the rows of one "chunk" that
+        // sees the whole prefix, read through the first member's table.
+        ChunkArgs c = {};
+        c.q = q;
+        c.query_start_loc = group_start;
+        c.num_seqs = num_groups;
+        c.max_query_len = max_group_size;
+        c.k_pool = k_pool;
+        c.v_pool = v_pool;
+        c.block_tables = block_tables;
+        c.max_blocks = max_blocks_per_seq;
+        c.context_lens = prefix_lens;
+        c.max_context_len = prefix_cap;
+        c.num_q_heads = num_q_heads;
+        c.num_kv_heads = pool.num_kv_heads;
+        c.head_dim = pool.head_dim;
+        c.num_blocks = pool.num_blocks;
+        c.block_shift = a.block_shift;
+        c.dtype = pool.dtype;
+        c.total_rows = num_seqs;
+        c.scale = scale;
+        c.out = out;
+        c.min_pairs = 0;
+        c.causal = 0;
+        c.table_row_qsl = 1;
+        c.key_parts = cp.prefix_slots;
+        c.key_part_tokens = cp.prefix_part;
+        c.partials = a.ws;
+        c.part_slots = a.nparts;
+        c.num_items = num_seqs;
+        c.prefer_large = 1;
+        // The prefix phase (matrix cores, LDS, cache-resident keys) runs on the
+        // auxiliary stream beside the decode kernel (HBM); they write disjoint
+        // partial slots, and the merge waits for both.
+        AuxStream* ax = aux_for(s);
+        if (ax == nullptr) {
+            if (int32_t st = launch_chunks(c, s)) return st;
+            return run_rows(a, s);
+        }
+        std::lock_guard<std::mutex> lock(ax->mu);
+        if (hipEventRecord(ax->fork, s) != hipSuccess || hipStreamWaitEvent(ax->stream, ax->fork, 0) != hipSuccess)
+            return PA_ERR_LAUNCH;
+        // decode kernel first: its workgroups take one slot per compute unit,
+        // the prefix workgroups fill in beside them
+        a.defer_merge = 1;
+        if (int32_t st = run_rows(a, s)) return st;
+        if (int32_t st = launch_chunks(c, ax->stream)) return st;
+        if (hipEventRecord(ax->join, ax->stream) != hipSuccess) return PA_ERR_LAUNCH;
+        if (hipStreamWaitEvent(s, ax->join, 0) != hipSuccess) return PA_ERR_LAUNCH;
+        return launch_merge(a, s);
+    }
+}
+
 size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_prefill_seqs,
                                   int32_t total_query_tokens, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len,
@@ -466,6 +640,8 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
         c.scale = scale;
         c.out = out;
         c.min_pairs = kMfmaMinPairs;
+        c.causal = 1;
+        c.key_parts = 1;
     }
     // The chunks (matrix cores, LDS) and the decode rows (HBM) use different
     // parts of the chip: with both present, the chunks run on the auxiliary

@@ -68,9 +68,27 @@ struct RowsArgs {
     int32_t nparts;       // partitions per item when split
     float* ws;            // split partials: acc [items,Hq,nparts,D], m, l [items,Hq,nparts]
     int32_t block_shift;  // log2 of the pool's block size
+    // Shared-prefix mode (decode items, group_start != NULL): the sequences
+    // group_start[g] .. group_start[g+1]-1 share their first prefix_lens[g]
+    // tokens (clamped to prefix_cap, rounded down to a multiple of 16), which
+    // the chunk kernel attended in parts of prefix_part_tokens keys, writing
+    // partial slots 0.. of each (item, q head).  This launch covers the keys
+    // after the prefix, always as partials, at slots prefix_slots + part; the
+    // merge combines both.
+    const int32_t* group_start;
+    const int32_t* prefix_lens;
+    int32_t num_groups;
+    int32_t prefix_cap;
+    int32_t prefix_part_tokens;
+    int32_t prefix_slots;
+    // Split launches: 1 leaves the merge to a later launch_merge call.
+    int32_t defer_merge;
 };
 
 int32_t launch_rows(const RowsArgs& a, hipStream_t stream);
+// The log-sum-exp merge of a split launch (launch_rows does it itself unless
+// defer_merge is set).
+int32_t launch_merge(const RowsArgs& a, hipStream_t stream);
 
 // Most decode items the attention kernels rank themselves (256 threads x 8);
 // larger batches get their order from launch_plan.
@@ -143,6 +161,23 @@ struct ChunkArgs {
     void* out;
     int32_t min_pairs;
     int32_t block_shift;  // log2 of the pool's block size
+    // 1: row i of an n-row chunk sees keys 0 .. L-n+i.  0 (a shared prefix):
+    // every row sees keys 0 .. L-1, L rounded down to a multiple of 16.
+    int32_t causal;
+    // 1: sequence s reads its keys through table row query_start_loc[s] (a
+    // group's first member) instead of row s.
+    int32_t table_row_qsl;
+    // key_parts > 1: the keys are split into parts of key_part_tokens (a
+    // multiple of 64), one workgroup per (row tile, part).
+    int32_t key_parts, key_part_tokens;
+    // Non-NULL: each row leaves its partial state (acc, m, l) of its key part
+    // kp at slot (row's item * Hq + q head) * part_slots + kp of the split
+    // layout with num_items items, instead of writing out.
+    float* partials;
+    int32_t part_slots, num_items;
+    // 1: always the 128-row, single-key-range launch shape (70 KiB of LDS,
+    // leaving room on each compute unit for a concurrent decode kernel).
+    int32_t prefer_large;
 };
 
 // Returns PA_ERR_UNSUPPORTED when no matrix-core kernel exists for the shape

@@ -117,12 +117,17 @@ def test_partition_choice_and_workspace(pa):
     # explicit requests are honoured; -1 means one pass
     assert pa.decode_partition_tokens(256, 8, 2048, -1) == -1
     assert pa.decode_partition_tokens(256, 8, 2048, 128) == 128
-    # the library's own choice is one pass for short contexts, split otherwise
+    # the library's own choice: one pass for short contexts and for at least
+    # 256 (row, kv head) units; otherwise partitions bringing the launch to
+    # about 256 workgroups (multiples of 16, at least 64 tokens)
     assert pa.decode_partition_tokens(4, 1, 64, 0) == -1
-    p = pa.decode_partition_tokens(64, 4, 8192, 0)
-    assert p > 0 and p % 16 == 0
-    # many (row, kv head) units: one pass, longest first
+    assert pa.decode_partition_tokens(64, 4, 8192, 0) == -1
     assert pa.decode_partition_tokens(256, 8, 2048, 0) == -1
+    assert pa.decode_partition_tokens(32, 4, 8192, 0) == 4096
+    assert pa.decode_partition_tokens(16, 4, 8192, 0) == 2048
+    assert pa.decode_partition_tokens(8, 4, 8192, 0) == 1024
+    assert pa.decode_partition_tokens(3, 1, 1000, 0) == 64     # 86 parts wanted: 64-token floor
+    assert pa.decode_partition_tokens(5, 4, 1500, 0) == 128    # ceil(1500 / 13) = 116 -> 128
     # workspace = the longest-first order (items int32, 256-byte aligned) when
     # the batch is larger than the kernels rank themselves (2048 rows), then
     # items * Hq * nparts * (D + 2) fp32 partials
@@ -139,10 +144,10 @@ def test_prefill_workspace_covers_both_vector_path_layouts(pa):
     """With matrix-core chunks the vector path covers (Hq/Hkv = 2) 7 row slots
     per prefill sequence instead of every prefill row; the workspace size holds
     whichever of the two needs more.  Four one-row chunks, no decode rows, 2048
-    context: 4 rows x 8 kv heads split into 64-token parts (32 parts) against
-    28 slots x 8 kv heads split into 256-token parts (8 parts)."""
-    rows = 4 * 16 * 32 * 130 * 4
-    slots = 28 * 16 * 8 * 130 * 4
+    context: 4 rows x 8 kv heads split into 256-token parts (8 parts) against
+    28 slots x 8 kv heads split into 1024-token parts (2 parts)."""
+    rows = 4 * 16 * 8 * 130 * 4
+    slots = 28 * 16 * 2 * 130 * 4
     assert pa.prefill_workspace_bytes(4, 4, 4, 16, 8, 128, 2048, 0) == max(rows, slots)
     # one pass requested: no partials, and no longest-first order for chunk rows
     assert pa.prefill_workspace_bytes(4, 4, 4, 16, 8, 128, 2048, -1) == 0
@@ -154,8 +159,34 @@ def test_prefill_workspace_parts_are_disjoint(pa):
     decode row (8 units, split into 32 parts of 64 tokens) and four one-row
     chunks (sized as in the test above)."""
     dec = 1 * 16 * 32 * 130 * 4
-    pre = 28 * 16 * 8 * 130 * 4
+    pre = 28 * 16 * 2 * 130 * 4
     assert pa.prefill_workspace_bytes(5, 4, 5, 16, 8, 128, 2048, 0) == (dec + 255) // 256 * 256 + pre
+
+
+def test_shared_prefix_validation(pa):
+    L = pa.lib()
+
+    def call(**kw):
+        a = dict(q=FAKE, S=4, maxL=64, gs=FAKE, pl=FAKE, ng=2, mg=3, mp=32, pool=pool(hkv=1, d=64),
+                 Hq=2, ws=FAKE, wsb=1 << 20, part=0)
+        a.update(kw)
+        return L.pa_decode_shared_prefix(a["q"], FAKE, FAKE, a["pool"], FAKE, 4, FAKE, a["S"], a["maxL"],
+                                         a["gs"], a["pl"], a["ng"], a["mg"], a["mp"], a["Hq"], 0.125, FAKE,
+                                         a["part"], a["ws"], a["wsb"], 0)
+    assert call(S=0, q=0) == 0                   # empty batch: no-op
+    assert call(gs=0) == 1 and call(pl=0) == 1
+    assert call(ng=0) == 2                       # every sequence needs a group
+    assert call(ng=5) == 2                       # more groups than sequences
+    assert call(mg=5) == 2                       # group larger than the batch
+    assert call(mp=65) == 2                      # prefix longer than any context
+    assert call(mp=-1) == 2
+    assert call(pool=pool(hkv=1, d=64, dtype=0)) == 4   # fp32: no matrix-core path
+    assert call(part=24) == 2
+    assert call(wsb=16) == 5                     # workspace too small
+    need = pa.decode_shared_prefix_workspace_bytes(4, 2, 1, 64, 64, 2, 3, 32, 0)
+    # partials: the prefix's key parts plus the rest's partitions, (D + 2) fp32 each
+    assert need > 0 and need % (4 * 2 * 66 * 4) == 0
+    assert pa.decode_shared_prefix_workspace_bytes(4, 2, 1, 64, 64, 0, 3, 32, 0) == 0
 
 
 def test_qkv_rope_write_validation(pa):

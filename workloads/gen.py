@@ -75,6 +75,7 @@ class PagedBatch:
     slot_mapping: np.ndarray      # int32 [T_new]
     num_prefill_seqs: int
     recipe: str
+    shared_prefix_tokens: int = 0   # leading tokens every sequence's table shares
 
     @property
     def num_seqs(self) -> int:
@@ -233,7 +234,7 @@ def make_batch(
         query_start_loc=qsl.astype(np.int32), block_tables=tables.astype(np.int32),
         k_pool=k_pool, v_pool=v_pool, q=q, new_k=new_k, new_v=new_v,
         slot_mapping=slots.astype(np.int32), num_prefill_seqs=num_prefill_seqs,
-        recipe=recipe,
+        recipe=recipe, shared_prefix_tokens=shared_prefix_blocks * bs,
     )
 
 
