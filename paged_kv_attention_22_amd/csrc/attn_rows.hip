@@ -18,758 +18,23 @@
 // lanes with DPP row operations.  The running max is only raised when a score
 // exceeds it by more than 2^8 (lazy rescaling): the exponentials stay below
 // 256, and the accumulator is rescaled rarely instead of every block.
-#include "pa_device.hpp"
-#include "pa_internal.hpp"
-
-#include <type_traits>
+#include "rows_body.hpp"
 
 namespace pa {
 namespace {
 
-constexpr float kNegInf = -__builtin_inff();
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kWaves = 4;
-// Smallest GQA group that takes the matrix-core decode path (bf16).
-constexpr int kMfmaMinGroup = 4;
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef short shortx4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
-
-// The 16x16x32 matrix-core product for each 16-bit element type.
-template <typename T>
-struct Mma;
-template <>
-struct Mma<uint16_t> {
-    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
-    static __device__ __forceinline__ floatx4 mfma(v8 a, v8 b, floatx4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-};
-template <>
-struct Mma<_Float16> {
-    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
-    static __device__ __forceinline__ floatx4 mfma(v8 a, v8 b, floatx4 c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-    }
-};
-
-// 16-lane transposing LDS read: lane i of each group of 16 receives element
-// i%4 of the 8-byte words addressed by lanes i/4 + 4k, k = 0..3.
-__device__ __forceinline__ uint2 ld_tr16(const unsigned char* p) {
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p)));
-}
-
-template <typename T>
-struct Elem;
-template <>
-struct Elem<uint16_t> {
-    static constexpr int kPerChunk = 8;  // bf16 bit patterns
-};
-template <>
-struct Elem<_Float16> {
-    static constexpr int kPerChunk = 8;
-};
-template <>
-struct Elem<float> {
-    static constexpr int kPerChunk = 4;
-};
-
-template <typename T>
-__device__ __forceinline__ float chunk_dot(const uint4& q, const uint4& k) {
-    if constexpr (kIs16<T>) {
-        float s = dot16<T>(q.x, k.x, 0.0f);
-        s = dot16<T>(q.y, k.y, s);
-        s = dot16<T>(q.z, k.z, s);
-        return dot16<T>(q.w, k.w, s);
-    } else {
-        float s = __uint_as_float(q.x) * __uint_as_float(k.x);
-        s = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), s);
-        s = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), s);
-        return fmaf(__uint_as_float(q.w), __uint_as_float(k.w), s);
-    }
-}
-
-template <typename T>
-__device__ __forceinline__ void unpack(const uint4& c, float* v) {
-    if constexpr (kIs16<T>) {
-        v[0] = lo16<T>(c.x); v[1] = hi16<T>(c.x);
-        v[2] = lo16<T>(c.y); v[3] = hi16<T>(c.y);
-        v[4] = lo16<T>(c.z); v[5] = hi16<T>(c.z);
-        v[6] = lo16<T>(c.w); v[7] = hi16<T>(c.w);
-    } else {
-        v[0] = __uint_as_float(c.x); v[1] = __uint_as_float(c.y);
-        v[2] = __uint_as_float(c.z); v[3] = __uint_as_float(c.w);
-    }
-}
-
-// Store E fp32 values (already normalised) as one 16-byte chunk of T.
-template <typename T>
-__device__ __forceinline__ void store_chunk(T* dst, const float* o) {
-    if constexpr (kIs16<T>) {
-        st16(dst, make_uint4(pack16<T>(o[0], o[1]), pack16<T>(o[2], o[3]),
-                             pack16<T>(o[4], o[5]), pack16<T>(o[6], o[7])));
-    } else {
-        st16(dst, make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]),
-                             __float_as_uint(o[2]), __float_as_uint(o[3])));
-    }
-}
-
-struct Item {
-    int seq;
-    int item;  // index of the item (its partial-state slots)
-    int row;
-    int n;     // query rows of the sequence
-    int i;     // this row's index among them
-    bool skip; // left to the matrix-core kernel
-};
-
-// Inclusive sum over the kWaves*64 threads of a workgroup of one value per
-// thread.  `tmp` holds one int per wave; the caller synchronises before
-// reusing it.
-__device__ __forceinline__ int block_inclusive_sum(int v, int* tmp) {
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(v, o);
-        if (lane >= o) v += y;
-    }
-    if (lane == 63) tmp[w] = v;
-    __syncthreads();
-    int before = 0;
-    for (int i = 0; i < w; ++i) before += tmp[i];
-    return v + before;
-}
-
-// Longest-first order computed by every workgroup itself: the decode items
-// sorted by descending bucket min(L, max_context_len) >> rank_shift (kRank
-// buckets), equal buckets in index order.  Returns the item handled z-th.
-// The order is a function of the lengths alone, so all workgroups of a launch
-// agree on it; each pays one pass over the lengths (kRankKeep per thread, in
-// registers), a histogram in LDS and two workgroup-wide sums, instead of a
-// separate sorting launch ahead of the attention kernel.  Called by every
-// thread of the workgroup.
-constexpr int kRankBuckets = kWaves * 64;  // one bucket per thread
-constexpr int kRankKeep = 8;               // items per thread
-__device__ __forceinline__ int rank_select(const RowsArgs& a, int z) {
-    __shared__ int hist[kRankBuckets];
-    __shared__ int tmp[kWaves];
-    __shared__ int pick[2];
-    const int t = threadIdx.x;
-    const int n = a.num_items;
-    const int32_t* lens = a.context_lens + a.seq_begin;
-    // thread t owns items t*kRankKeep .. t*kRankKeep+kRankKeep-1: index order
-    // within a bucket follows thread order, then j
-    int pos[kRankKeep];  // position of the item's bucket, longest first; -1: no item
-#pragma unroll
-    for (int j = 0; j < kRankKeep; ++j) {
-        const int i = t * kRankKeep + j;
-        const int L = i < n ? lens[i] : 0;
-        const int key = min(min(max(L, 0), a.max_context_len) >> a.rank_shift, kRankBuckets - 1);
-        pos[j] = i < n ? kRankBuckets - 1 - key : -1;
-    }
-    hist[t] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kRankKeep; ++j)
-        if (pos[j] >= 0) atomicAdd(&hist[pos[j]], 1);
-    __syncthreads();
-    const int c = hist[t];
-    const int incl = block_inclusive_sum(c, tmp);
-    if (incl - c <= z && z < incl) {  // bucket t holds rank z
-        pick[0] = t;
-        pick[1] = z - (incl - c);
-    }
-    __syncthreads();
-    const int pb = pick[0], r = pick[1];
-    int m = 0;
-#pragma unroll
-    for (int j = 0; j < kRankKeep; ++j) m += pos[j] == pb;
-    const int incl2 = block_inclusive_sum(m, tmp);  // (every thread has read pick)
-    if (incl2 - m <= r && r < incl2) {              // the r-th item of bucket pb is here
-        int k = r - (incl2 - m);
-#pragma unroll
-        for (int j = 0; j < kRankKeep; ++j) {
-            if (pos[j] == pb) {
-                if (k == 0) pick[0] = t * kRankKeep + j;
-                --k;
-            }
-        }
-    }
-    __syncthreads();
-    return pick[0];
-}
-
-// Which sequence and q/out row grid index z stands for.  Decode items read
-// nothing but the processing order (in-kernel ranking or an order array); the
-// context length is loaded separately so that its latency overlaps the first
-// q and block-id loads.
-__device__ __forceinline__ Item locate(const RowsArgs& a, int z, int group) {
-    Item it;
-    it.skip = false;
-    it.item = z;
-    if (a.query_start_loc == nullptr) {
-        const int zz = a.rank_shift >= 0 ? rank_select(a, z) : (a.order != nullptr ? a.order[z] : z);
-        it.item = zz;
-        it.seq = a.seq_begin + zz;
-        it.row = a.row_begin + zz;
-        it.n = 1;
-        it.i = 0;
-        return it;
-    }
-    const int32_t* qsl = a.query_start_loc;
-    if (a.small_rows > 0) {
-        it.seq = a.seq_begin + z / a.small_rows;
-        it.i = z % a.small_rows;
-        const int q0 = qsl[it.seq];
-        it.n = qsl[it.seq + 1] - q0;
-        it.row = q0 + it.i;
-        it.skip = it.i >= it.n || it.n * group >= a.mfma_min_pairs;
-        return it;
-    }
-    const int row = a.row_begin + z;
-    int lo = a.seq_begin, hi = a.seq_end - 1;  // last s with qsl[s] <= row
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (qsl[mid] <= row) lo = mid; else hi = mid - 1;
-    }
-    it.seq = lo;
-    it.row = row;
-    it.n = qsl[lo + 1] - qsl[lo];
-    it.i = row - qsl[lo];
-    it.skip = a.mfma_min_pairs > 0 && it.n * group >= a.mfma_min_pairs;
-    return it;
-}
-
-// Shared-prefix mode: 16-token chunks of the prefix of sequence seq's group
-// (the last group g with group_start[g] <= seq), which the chunk kernel has
-// attended; the decode kernels start after them.
-__device__ __forceinline__ int prefix_chunks(const RowsArgs& a, int seq) {
-    int lo = 0, hi = a.num_groups - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (a.group_start[mid] <= seq) lo = mid; else hi = mid - 1;
-    }
-    return min(max(a.prefix_lens[lo], 0), a.prefix_cap) >> 4;
-}
-
-// Keys visible to the row: 0 .. L-n+i, with L clamped to what the table holds.
-__device__ __forceinline__ int visible_len(const RowsArgs& a, const Item& it, int L) {
-    const int cap = (int)min((int64_t)a.max_context_len, (int64_t)a.max_blocks << a.block_shift);
-    L = min(max(L, 0), cap);
-    return min(max(L - it.n + it.i + 1, 0), L);
-}
-
-// Workgroups are numbered with the kv head fastest, then the partition, then
-// the row: the kv heads of one row and partition read the same token rows of
-// the pool (each head a 2*D-byte slice of every row) at about the same time.
-__device__ __forceinline__ void unit_of(const RowsArgs& a, int& z, int& g, int& part) {
-    const int id = blockIdx.x;
-    const int nparts = a.part_tokens > 0 ? a.nparts - a.prefix_slots : 1;  // partitions launched
-    g = id % a.num_kv_heads;
-    const int rest = id / a.num_kv_heads;
-    part = rest % nparts;
-    z = rest / nparts;
-}
-
-// Merge the per-wave softmax states kWaves x (m, l, acc[D]) of the G heads
-// of one (row, kv head, partition) left in LDS, then write the normalised
-// output (final_out) or the partition's partial state for merge_kernel.
-template <typename T, int D, int G>
-__device__ __forceinline__ void combine_waves(const RowsArgs& a, const Item& it, int z, int g, int part,
-                                              bool final_out, const float (&s_acc)[kWaves][G][D],
-                                              const float (&s_m)[kWaves][G], const float (&s_l)[kWaves][G]) {
-    constexpr int E = Elem<T>::kPerChunk;
-    constexpr int CPR = D / E;  // 16-byte chunks per output row
-    const int Hq = a.num_q_heads;
-    for (int t = threadIdx.x; t < G * CPR; t += kWaves * 64) {
-        const int h = t / CPR, cc = t % CPR;
-        float M = s_m[0][h];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-        const float mref = (M == kNegInf) ? 0.0f : M;
-        float den = 0.0f, o[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float wt = fast_exp2(s_m[w][h] - mref);
-            den = fmaf(s_l[w][h], wt, den);
-#pragma unroll
-            for (int e = 0; e < E; ++e) o[e] = fmaf(s_acc[w][h][cc * E + e], wt, o[e]);
-        }
-        const int hq = g * G + h;
-        if (final_out) {
-            const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-#pragma unroll
-            for (int e = 0; e < E; ++e) o[e] *= inv;
-            store_chunk<T>(static_cast<T*>(a.out) + ((int64_t)it.row * Hq + hq) * D + cc * E, o);
-        } else {
-            const int64_t slot = ((int64_t)it.item * Hq + hq) * a.nparts + part;
-            float* wa = a.ws + slot * D + cc * E;
-#pragma unroll
-            for (int e = 0; e < E; e += 4) st16(wa + e, make_uint4(__float_as_uint(o[e]), __float_as_uint(o[e + 1]),
-                                                                   __float_as_uint(o[e + 2]), __float_as_uint(o[e + 3])));
-            if (cc == 0) {
-                const int64_t nslots = (int64_t)a.num_items * Hq * a.nparts;
-                a.ws[nslots * D + slot] = M;
-                a.ws[nslots * D + nslots + slot] = den;
-            }
-        }
-    }
-}
+using namespace rows_impl;
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
-    constexpr int E = Elem<T>::kPerChunk;
-    constexpr int V = 1;                      // 16-byte chunks per lane per token
-    constexpr int EL = V * E;                 // elements per lane per token
-    constexpr int R = D / EL;                 // lanes per token row
-    constexpr int TPW = 64 / R;               // token rows per wave
-    constexpr int NT = kBlock / TPW;          // tokens of one chunk per lane
-    static_assert(TPW >= 1 && NT >= 1 && R >= 4, "lane layout");
-    static_assert(8 % TPW == 0, "each lane's rows split evenly between a chunk's two halves");
-    constexpr float kLazy = 8.0f;             // log2 headroom before rescaling
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = lane % R;
-    const int rg = lane / R;
-    int z, g, part;
-    unit_of(a, z, g, part);
-
-    const Item it = locate(a, z, G);
-    if (it.skip) return;
-    const bool split = a.part_tokens > 0;
-    const int pb = split ? a.part_tokens / kBlock : 0;
-    // shared-prefix mode: the chunks after the group's prefix, always split
-    const bool cascade = a.group_start != nullptr;
-    const int b0 = (cascade ? prefix_chunks(a, it.seq) : 0) + (split ? part * pb : 0);
-    const int first = b0 + wave;  // this wave's blocks: first + k*kWaves
-
-    // Issue the length, q and first block-id loads together.
-    const int Lraw = a.context_lens[it.seq];
-    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
-    // Chunk u of this lane covers elements (u*R + c)*E .. +E of the row.
-    const T* qp = static_cast<const T*>(a.q) + ((int64_t)it.row * Hq + g * G) * D + c * E;
-    uint4 qv[G][V];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int u = 0; u < V; ++u) qv[h][u] = ld16(qp + h * D + u * R * E);
-    // Block ids: lane i holds the table entry behind this wave's chunk
-    // kbase + i (one load per 64 chunks): the block holding the chunk (blocks
-    // of 16 or 32), or the first of its two blocks with the second in ids_hi
-    // (blocks of 8).
-    const int32_t* bt = a.block_tables + (int64_t)it.seq * a.max_blocks;
-    const int bsh = a.block_shift;
-    const ChunkMap cm = chunk_map(bsh);
-    int ids = 0, ids_hi = 0;
-    auto fetch_ids = [&](int kbase) {
-        const int jj = first + (kbase + lane) * kWaves;
-        ids = bt[min((jj << cm.mul) >> cm.shr, a.max_blocks - 1)];
-        ids_hi = bt[min(((jj << cm.mul) + cm.mul) >> cm.shr, a.max_blocks - 1)];
-    };
-    fetch_ids(0);
-
-    const int len = visible_len(a, it, Lraw);
-    const int nblk = (len + kBlock - 1) / kBlock;
-    int b1 = nblk;
-    bool final_out = true;
-    if (split) {
-        b1 = min(nblk, b0 + pb);
-        // the merge ignores missing partitions
-        if (b0 >= b1 && (cascade || !(part == 0 && nblk == 0))) return;
-        final_out = !cascade && nblk <= pb;  // a single partition writes the output itself
-    }
-
-    float m[G], l[G], acc[G][EL];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m[h] = kNegInf;
-        l[h] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EL; ++e) acc[h][e] = 0.0f;
-    }
-
-    // This wave's blocks are jb = first + k*kWaves, k < nk; blocks below
-    // len/16 are full, and only the sequence's last block can be partial.
-    const int nk = b1 > first ? (b1 - first + kWaves - 1) / kWaves : 0;
-    const int nfull = len / kBlock;
-    const int nkf = nfull > first ? min(nk, (nfull - first + kWaves - 1) / kWaves) : 0;
-    // First pool rows of chunk k's tokens 0-7 (lo) and 8-15 (hi); ids are
-    // clamped into the pool.
-    auto rows_of = [&](int k, int64_t& lo, int64_t& hi) {
-        if ((k & 63) == 0 && k != 0) fetch_ids(k);
-        const int bl = min(max(__builtin_amdgcn_readlane(ids, k & 63), 0), a.num_blocks - 1);
-        const int bh = min(max(__builtin_amdgcn_readlane(ids_hi, k & 63), 0), a.num_blocks - 1);
-        const int off = ((first + k * kWaves) << 4) & cm.in_block;
-        lo = ((int64_t)bl << bsh) + off;
-        hi = ((int64_t)bh << bsh) + off + cm.hi_off;
-    };
-
-    const int64_t tok_stride = (int64_t)Hkv * D;  // elements between tokens
-    const T* kbase = static_cast<const T*>(a.k_pool) + (int64_t)g * D + c * E + rg * tok_stride;
-    const T* vbase = static_cast<const T*>(a.v_pool) + (int64_t)g * D + c * E + rg * tok_stride;
-    const float sl2 = a.scale * kLog2e;
-
-    auto load = [&](uint4 (&kk)[NT][V], uint4 (&vv)[NT][V], int k) {
-        int64_t lo, hi;
-        rows_of(k, lo, hi);
-        // element offsets of the chunk's rows 0 and 8 (wave-uniform)
-        const int64_t o_lo = lo * tok_stride, o_hi = (hi - 8) * tok_stride;
-#pragma unroll
-        for (int i = 0; i < NT; ++i)
-#pragma unroll
-            for (int u = 0; u < V; ++u) {
-                // this lane's row rg + i*TPW of the chunk is in its first half iff i*TPW < 8
-                const int64_t o = (i * TPW < 8 ? o_lo : o_hi) + (i * TPW) * tok_stride + u * R * E;
-                kk[i][u] = ld16_stream(kbase + o);
-                vv[i][u] = ld16_stream(vbase + o);
-            }
-    };
-    auto compute = [&](const uint4 (&kk)[NT][V], const uint4 (&vv)[NT][V], int k, bool masked) {
-        bool valid[NT];
-        const int tok0 = (first + k * kWaves) * kBlock + rg;
-#pragma unroll
-        for (int i = 0; i < NT; ++i) valid[i] = !masked || tok0 + i * TPW < len;
-        float sc[NT][G];
-#pragma unroll
-        for (int i = 0; i < NT; ++i)
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float d = chunk_dot<T>(qv[h][0], kk[i][0]);
-#pragma unroll
-                for (int u = 1; u < V; ++u) d += chunk_dot<T>(qv[h][u], kk[i][u]);
-                d = group_sum<R>(d) * sl2;
-                // excluded, never weighted by zero: past-the-length slots may hold NaN
-                sc[i][h] = valid[i] ? d : kNegInf;
-            }
-        float vf[NT][EL];
-#pragma unroll
-        for (int i = 0; i < NT; ++i)
-#pragma unroll
-            for (int u = 0; u < V; ++u) {
-                const uint4 w = valid[i] ? vv[i][u] : make_uint4(0, 0, 0, 0);
-                unpack<T>(w, &vf[i][u * E]);
-            }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float mb = sc[0][h];
-#pragma unroll
-            for (int i = 1; i < NT; ++i) mb = fmaxf(mb, sc[i][h]);
-            if (mb > m[h] + kLazy) {  // raise the reference and rescale
-                const float alpha = fast_exp2(m[h] - mb);
-                l[h] *= alpha;
-#pragma unroll
-                for (int e = 0; e < EL; ++e) acc[h][e] *= alpha;
-                m[h] = mb;
-            }
-            const float mref = (m[h] == kNegInf) ? 0.0f : m[h];
-#pragma unroll
-            for (int i = 0; i < NT; ++i) {
-                const float p = fast_exp2(sc[i][h] - mref);
-                l[h] += p;
-#pragma unroll
-                for (int e = 0; e < EL; ++e) acc[h][e] = fmaf(p, vf[i][e], acc[h][e]);
-            }
-        }
-    };
-
-    // Full blocks, two register buffers: the next block's loads are in flight
-    // while the current one is computed.  The reload at the end of the loop
-    // is unconditional (clamped to the last full block, which is then already
-    // cached) so that both buffers keep their registers across iterations.
-    uint4 ka[NT][V], va[NT][V], kb[NT][V], vb[NT][V];
-    int k = 0;
-    if (nkf > 0) load(ka, va, 0);
-    for (; k + 1 < nkf; k += 2) {
-        load(kb, vb, k + 1);
-        compute(ka, va, k, false);
-        load(ka, va, min(k + 2, nkf - 1));
-        compute(kb, vb, k + 1, false);
-    }
-    if (k < nkf) {
-        compute(ka, va, k, false);
-        ++k;
-    }
-    if (k < nk) {  // the partial last block
-        load(ka, va, k);
-        compute(ka, va, k, true);
-    }
-
-    // Merge the lane groups of this wave (they hold disjoint token subsets).
-#pragma unroll
-    for (int o = R; o < 64; o <<= 1) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float mo = __shfl_xor(m[h], o);
-            const float lo = __shfl_xor(l[h], o);
-            const float mn = fmaxf(m[h], mo);
-            const float mref = (mn == kNegInf) ? 0.0f : mn;
-            const float a1 = fast_exp2(m[h] - mref), a2 = fast_exp2(mo - mref);
-            l[h] = l[h] * a1 + lo * a2;
-#pragma unroll
-            for (int e = 0; e < EL; ++e) {
-                const float ao = __shfl_xor(acc[h][e], o);
-                acc[h][e] = acc[h][e] * a1 + ao * a2;
-            }
-            m[h] = mn;
-        }
-    }
-
-    // Merge the waves through LDS, then write the output or the partial state.
-    __shared__ float s_acc[kWaves][G][D];
-    __shared__ float s_m[kWaves][G];
-    __shared__ float s_l[kWaves][G];
-    if (rg == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-#pragma unroll
-            for (int e = 0; e < EL; ++e) s_acc[wave][h][((e / E) * R + c) * E + e % E] = acc[h][e];
-            if (c == 0) {
-                s_m[wave][h] = m[h];
-                s_l[wave][h] = l[h];
-            }
-        }
-    }
-    __syncthreads();
-    combine_waves<T, D, G>(a, it, z, g, a.prefix_slots + part, final_out, s_acc, s_m, s_l);
+    __shared__ __align__(16) unsigned char lds[rows_lds_bytes<D, G>()];
+    rows_block<T, D, G>(a, blockIdx.x, lds);
 }
 
-// Decode rows on the matrix cores, for large GQA groups (bf16).  Same work
-// unit, partitions, processing order and wave merge as rows_kernel; the
-// per-token arithmetic moves to v_mfma_f32_16x16x32_bf16 so that the vector
-// units no longer pay G dot products, reductions and FMAs per loaded byte.
-// Each wave streams its own 32-token steps (two blocks):
-//   S^T = K * Q^T    A = the K rows straight from memory (lane l: token l%16,
-//                    dims 32*ks + 8*(l/16) .. +7), B = the group's q rows
-//                    (heads padded to 16 with zeros) held in registers; lane
-//                    l ends with head l%16's scores for tokens 16*mt +
-//                    4*(l/16) + r.
-//   O^T += V^T P^T   B = those probabilities (slot p < 4: token 4*(l/16)+p,
-//                    p >= 4: 16+4*(l/16)+p-4), A = V^T read with
-//                    ds_read_b64_tr_b16 from the wave's own row-major V tile in
-//                    LDS (written with 16-byte stores; no barrier needed, the
-//                    tile is private to the wave).
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a) {
-    using V8 = typename Mma<T>::v8;
-    constexpr int KS = D / 32;                // 32-dim slices (first product)
-    constexpr int MT = D / 16;                // 16-dim output tiles (second product)
-    constexpr int CPR = D / 8;                // 16-byte chunks per token row
-    constexpr int VL = 32 * CPR / 64;         // V chunks per lane per step
-    constexpr int VROW = D * 2 + 32;          // LDS bytes per V row (padded: the
-                                              // transposing reads take 4 rows x 32 B)
-    constexpr int VT = 32 * VROW;             // one wave's V tile
-    constexpr float kLazy = 8.0f;
-    static_assert(G <= 16, "group fits the 16 columns of one MFMA tile");
-    __shared__ __align__(16) unsigned char s_v[kWaves * VT];
-    __shared__ float s_acc[kWaves][G][D];
-    __shared__ float s_m[kWaves][G];
-    __shared__ float s_l[kWaves][G];
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int li = lane & 15, kg = lane >> 4;
-    int z, g, part;
-    unit_of(a, z, g, part);
-    const Item it = locate(a, z, G);
-    if (it.skip) return;
-    const bool split = a.part_tokens > 0;
-    const int pb = split ? a.part_tokens / kBlock : 0;
-    // shared-prefix mode: the chunks after the group's prefix, always split
-    const bool cascade = a.group_start != nullptr;
-    const int b0 = (cascade ? prefix_chunks(a, it.seq) : 0) + (split ? part * pb : 0);
-
-    const int Lraw = a.context_lens[it.seq];
-    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
-    V8 qf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (li < G)
-            v = ld16(static_cast<const T*>(a.q) + ((int64_t)it.row * Hq + g * G + li) * D + ks * 32 + kg * 8);
-        qf[ks] = __builtin_bit_cast(V8, v);
-    }
-    // Block ids: lane i holds the table entry behind chunk
-    // b0 + 2*(wave + (kbase + i/2)*kWaves) + i%2 (as in rows_kernel: blocks of
-    // 8 keep the chunk's second block in ids_hi).
-    const int32_t* bt = a.block_tables + (int64_t)it.seq * a.max_blocks;
-    const int bsh = a.block_shift;
-    const ChunkMap cm = chunk_map(bsh);
-    int ids = 0, ids_hi = 0;
-    auto fetch_ids = [&](int kbase) {
-        const int jj = b0 + 2 * (wave + (kbase + (lane >> 1)) * kWaves) + (lane & 1);
-        ids = bt[min((jj << cm.mul) >> cm.shr, a.max_blocks - 1)];
-        ids_hi = bt[min(((jj << cm.mul) + cm.mul) >> cm.shr, a.max_blocks - 1)];
-    };
-    fetch_ids(0);
-
-    const int len = visible_len(a, it, Lraw);
-    const int nblk = (len + kBlock - 1) / kBlock;
-    int b1 = nblk;
-    bool final_out = true;
-    if (split) {
-        b1 = min(nblk, b0 + pb);
-        if (b0 >= b1 && (cascade || !(part == 0 && nblk == 0))) return;
-        final_out = !cascade && nblk <= pb;
-    }
-    // Steps of this wave: pair k covers blocks jb = b0 + 2*(wave + k*kWaves)
-    // and jb + 1; the steps with both blocks full come first, then at most one
-    // step that needs masking.
-    const int first = b0 + 2 * wave;
-    const int nk = b1 > first ? (b1 - first + 2 * kWaves - 1) / (2 * kWaves) : 0;
-    const int full_end = min(b1, len / kBlock);  // blocks below this are full
-    const int nkf = full_end >= first + 2 ? min(nk, (full_end - first - 2) / (2 * kWaves) + 1) : 0;
-    // First pool rows of the step's chunk `half`, tokens 0-7 (lo) and 8-15 (hi).
-    auto rows_of = [&](int k, int half, int64_t& lo, int64_t& hi) {
-        if ((k & 31) == 0 && k != 0 && half == 0) fetch_ids(k);
-        const int ln = ((k & 31) << 1) | half;
-        const int bl = min(max(__builtin_amdgcn_readlane(ids, ln), 0), a.num_blocks - 1);
-        const int bh = min(max(__builtin_amdgcn_readlane(ids_hi, ln), 0), a.num_blocks - 1);
-        const int off = ((first + 2 * kWaves * k + half) << 4) & cm.in_block;
-        lo = ((int64_t)bl << bsh) + off;
-        hi = ((int64_t)bh << bsh) + off + cm.hi_off;
-    };
-
-    const int64_t tok_stride = (int64_t)Hkv * D;
-    const T* kpool = static_cast<const T*>(a.k_pool) + (int64_t)g * D;
-    const T* vpool = static_cast<const T*>(a.v_pool) + (int64_t)g * D;
-    constexpr int TPS = 64 / CPR;  // V rows one 64-lane slice covers
-    static_assert(8 % TPS == 0, "a V slice stays inside half a chunk");
-    const int k_lane = li * (int)tok_stride + kg * 8;                             // K row li, column
-    const int v_lane = (lane / CPR) * (int)tok_stride + (lane % CPR) * 8;          // V row, column
-    unsigned char* vt = s_v + wave * VT;
-    const float sl2 = a.scale * kLog2e;
-
-    float m = kNegInf, lsum = 0.0f;
-    floatx4 acc[MT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) acc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    auto load = [&](uint4 (&kf)[2][KS], uint4 (&vr)[VL], int k) {
-        const int jb = first + 2 * kWaves * k;
-        int64_t lo0, hi0, lo1, hi1;
-        rows_of(k, 0, lo0, hi0);
-        if (jb + 1 < b1) {
-            rows_of(k, 1, lo1, hi1);
-        } else {
-            lo1 = lo0;
-            hi1 = hi0;
-        }
-        // Wave-uniform element offsets of rows 0 and 8 of both chunks; the
-        // lanes add their own (loop-invariant) row and column offsets.
-        const int64_t o_lo0 = lo0 * tok_stride, o_hi0 = (hi0 - 8) * tok_stride;
-        const int64_t o_lo1 = lo1 * tok_stride, o_hi1 = (hi1 - 8) * tok_stride;
-        // K: lane row li of chunk mt lies in the chunk's first half iff li < 8
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const T* kp = kpool + (mt ? (li < 8 ? o_lo1 : o_hi1) : (li < 8 ? o_lo0 : o_hi0));
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = ld16_stream(kp + k_lane + ks * 32);
-        }
-        // V: slice u covers step tokens u*TPS .. u*TPS+TPS-1, all in one half
-        // of one chunk (known at compile time)
-#pragma unroll
-        for (int u = 0; u < VL; ++u) {
-            const int t0 = u * TPS;
-            const int64_t o = (t0 >> 4) ? ((t0 & 15) < 8 ? o_lo1 : o_hi1) : ((t0 & 15) < 8 ? o_lo0 : o_hi0);
-            vr[u] = ld16_stream(vpool + o + (int64_t)(t0 & 15) * tok_stride + v_lane);
-        }
-    };
-    auto compute = [&](const uint4 (&kf)[2][KS], const uint4 (&vr)[VL], int k, bool masked) {
-        const int pos0 = (first + 2 * kWaves * k) * kBlock;  // first token of the step
-        const int pend = min(len, b1 * kBlock);              // tokens at or past this are excluded
-#pragma unroll
-        for (int u = 0; u < VL; ++u) {
-            const int c = lane + 64 * u, tk = c / CPR, piece = c % CPR;
-            // excluded tokens are zeroed, never weighted by zero (their slots may hold NaN)
-            const uint4 w = (!masked || pos0 + tk < pend) ? vr[u] : make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4*>(vt + tk * VROW + piece * 16) = w;
-        }
-        floatx4 st[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) c = Mma<T>::mfma(__builtin_bit_cast(V8, kf[mt][ks]), qf[ks], c);
-            st[mt] = c;
-        }
-        float sc[8];
-        float mx = kNegInf;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float v = st[mt][r] * sl2;
-                const bool ok = !masked || pos0 + mt * 16 + kg * 4 + r < pend;
-                sc[mt * 4 + r] = ok ? v : kNegInf;
-                mx = fmaxf(mx, sc[mt * 4 + r]);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (mx > m + kLazy) {  // raise the reference and rescale
-            const float alpha = fast_exp2(m - mx);
-            lsum *= alpha;
-#pragma unroll
-            for (int i = 0; i < MT; ++i) acc[i] *= alpha;
-            m = mx;
-        }
-        const float mref = (m == kNegInf) ? 0.0f : m;
-        uint32_t pk[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // the sum takes the probabilities as rounded for the product
-            const uint32_t lo = to16<T>(fast_exp2(sc[2 * i] - mref));
-            const uint32_t hi = to16<T>(fast_exp2(sc[2 * i + 1] - mref));
-            lsum += lo16<T>(lo) + lo16<T>(hi);
-            pk[i] = lo | (hi << 16);
-        }
-        const V8 pb = __builtin_bit_cast(V8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's V tile is in LDS
-        const unsigned char* v0 = vt + (4 * kg + ((lane >> 2) & 3)) * VROW + (lane & 3) * 8;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const uint2 lo = ld_tr16(v0 + mt * 32);
-            const uint2 hi = ld_tr16(v0 + 16 * VROW + mt * 32);
-            acc[mt] = Mma<T>::mfma(__builtin_bit_cast(V8, make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, acc[mt]);
-        }
-    };
-
-    uint4 ka[2][KS], va[VL], kb[2][KS], vb[VL];
-    int k = 0;
-    if (nkf > 0) load(ka, va, 0);
-    for (; k + 1 < nkf; k += 2) {
-        load(kb, vb, k + 1);
-        compute(ka, va, k, false);
-        load(ka, va, min(k + 2, nkf - 1));
-        compute(kb, vb, k + 1, false);
-    }
-    if (k < nkf) {
-        compute(ka, va, k, false);
-        ++k;
-    }
-    if (k < nk) {  // the step holding the partial block and/or the partition end
-        load(ka, va, k);
-        compute(ka, va, k, true);
-    }
-
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    if (li < G) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s_acc[wave][li][mt * 16 + kg * 4 + r] = acc[mt][r];
-        if (kg == 0) {
-            s_m[wave][li] = m;
-            s_l[wave][li] = lsum;
-        }
-    }
-    __syncthreads();
-    combine_waves<T, D, G>(a, it, z, g, a.prefix_slots + part, final_out, s_acc, s_m, s_l);
+    __shared__ __align__(16) unsigned char lds[mfma_rows_lds_bytes<D, G>()];
+    mfma_rows_block<T, D, G>(a, blockIdx.x, lds);
 }
 
 // Log-sum-exp merge of the partitions of one (row, q head):
@@ -782,7 +47,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(64) void merge_kernel(const RowsArgs a, int group) {
     constexpr int kPre = 8;
     const int z = blockIdx.x, hq = blockIdx.y;
-    const Item it = locate(a, z, group);
+    const Item it = locate(a, z, group, nullptr);  // index order: no ranking
     if (it.skip) return;
     const int len = visible_len(a, it, a.context_lens[it.seq]);
     const int pb = a.part_tokens / kBlock;

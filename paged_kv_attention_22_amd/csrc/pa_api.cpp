@@ -24,6 +24,7 @@ struct AuxStream {
     std::mutex mu;
     hipStream_t stream = nullptr;
     hipEvent_t fork = nullptr;
+    hipEvent_t started = nullptr;  // the auxiliary stream has passed its fork wait
     hipEvent_t join = nullptr;
     bool ok = false;
 };
@@ -45,6 +46,7 @@ AuxStream* aux_for(hipStream_t s) {
         if (cur != dev && hipSetDevice(dev) != hipSuccess) return;
         a.ok = hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking) == hipSuccess &&
                hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) == hipSuccess &&
+               hipEventCreateWithFlags(&a.started, hipEventDisableTiming) == hipSuccess &&
                hipEventCreateWithFlags(&a.join, hipEventDisableTiming) == hipSuccess;
         if (cur != dev) (void)hipSetDevice(cur);
     });
@@ -103,7 +105,7 @@ int32_t choose_partition(int64_t items, int32_t num_kv_heads, int32_t max_contex
     if (requested < 0) return -1;
     if (requested > 0) return requested;
     const int64_t units = items * num_kv_heads;
-    if (units >= kSplitTarget || max_context_len <= 128) return -1;
+    if (units <= 0 || units >= kSplitTarget || max_context_len <= 128) return -1;
     const int64_t parts = ceil_div(kSplitTarget, units);
     const int32_t part = std::max<int32_t>(64, (ceil_div(max_context_len, parts) + 15) / 16 * 16);
     return ceil_div(max_context_len, part) > 1 ? part : -1;
@@ -598,7 +600,13 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
     const bool mfma = prefill_rows > 0 && chunks_supported(pool.dtype, pool.head_dim, group);
     pre.mfma_min_pairs = mfma ? kMfmaMinPairs : 0;
     pre.small_rows = mfma ? small_rows_for(group) : 0;
-    const int64_t pre_items = mfma ? (int64_t)num_prefill_seqs * pre.small_rows : prefill_rows;
+    // Every chunk has at most max_query_len rows, so the smallest has at least
+    // prefill_rows - (num_prefill_seqs - 1) * max_query_len: when even that
+    // many rows give a matrix-core tile, no chunk is left to the vector path
+    // and its launch (all slots idle) is skipped.
+    const int64_t min_chunk = prefill_rows - (int64_t)(num_prefill_seqs - 1) * max_query_len;
+    const bool any_small = !mfma || min_chunk * group < kMfmaMinPairs;
+    const int64_t pre_items = mfma ? (any_small ? (int64_t)num_prefill_seqs * pre.small_rows : 0) : prefill_rows;
     if (pre_items > INT32_MAX) return PA_ERR_SHAPE;
     dec.query_start_loc = nullptr;
     dec.seq_begin = num_prefill_seqs;
@@ -644,22 +652,32 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
         c.key_parts = 1;
     }
     // The chunks (matrix cores, LDS) and the decode rows (HBM) use different
-    // parts of the chip: with both present, the chunks run on the auxiliary
-    // stream while the vector path runs on the caller's stream.  They read the
-    // same pools and write disjoint rows of out; only the vector path uses the
-    // workspace.
+    // parts of the chip and run concurrently: the chunk kernel on the
+    // auxiliary stream, the vector path on the caller's stream.  They read the
+    // same pools and write disjoint rows of out; the two vector-path launches
+    // use disjoint parts of the workspace.  The order matters: a chunk
+    // workgroup (4 waves of 256 registers, 70 KiB of LDS) fits on a compute
+    // unit beside one decode workgroup but not beside the three the decode
+    // kernel places on an idle one, so the chunks must reach the compute units
+    // first (measured: with the decode rows first the chunk kernel waited for
+    // their workgroups to drain and the mixed step took 10% longer).  The
+    // auxiliary stream marks `started` once it has passed its fork wait, just
+    // before the chunk launch, and the decode rows wait for that mark.  The
+    // long decode kernel stays on the caller's stream, so the final join finds
+    // the chunk kernel long finished.  (One fused launch holding both kinds of
+    // workgroup avoids the waits but measured slower: the decode loop compiled
+    // inside the larger kernel ran 12% slower.)
     AuxStream* ax = (mfma && num_decode > 0) ? aux_for(s) : nullptr;
     if (ax != nullptr) {
         std::lock_guard<std::mutex> lock(ax->mu);
         if (hipEventRecord(ax->fork, s) != hipSuccess ||
-            hipStreamWaitEvent(ax->stream, ax->fork, 0) != hipSuccess)
+            hipStreamWaitEvent(ax->stream, ax->fork, 0) != hipSuccess ||
+            hipEventRecord(ax->started, ax->stream) != hipSuccess)
             return PA_ERR_LAUNCH;
         if (int32_t st = launch_chunks(c, ax->stream)) return st;
         if (hipEventRecord(ax->join, ax->stream) != hipSuccess) return PA_ERR_LAUNCH;
-        // The small chunks' rows go first on `stream`: measured on the mixed
-        // batch, the chunks finish sooner beside the decode rows when the
-        // decode rows start a few microseconds after them.
-        if (int32_t st = run_rows(pre, s)) return st;
+        if (int32_t st = run_rows(pre, s)) return st;  // small chunks, if any
+        if (hipStreamWaitEvent(s, ax->started, 0) != hipSuccess) return PA_ERR_LAUNCH;
         if (int32_t st = run_rows(dec, s)) return st;
         return hipStreamWaitEvent(s, ax->join, 0) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
     }

@@ -121,6 +121,7 @@ def test_partition_choice_and_workspace(pa):
     # 256 (row, kv head) units; otherwise partitions bringing the launch to
     # about 256 workgroups (multiples of 16, at least 64 tokens)
     assert pa.decode_partition_tokens(4, 1, 64, 0) == -1
+    assert pa.decode_partition_tokens(0, 4, 8192, 0) == -1      # no rows (a prefill-only batch's decode part)
     assert pa.decode_partition_tokens(64, 4, 8192, 0) == -1
     assert pa.decode_partition_tokens(256, 8, 2048, 0) == -1
     assert pa.decode_partition_tokens(32, 4, 8192, 0) == 4096
