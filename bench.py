@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 METRIC = "pa_decode HBM GB/s (% of peak) + seq-steps/s, Qwen3-0.6B shape, batch 256"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_qwen3_06b_b256_traffic.json")
-KERNEL_SOURCES = ["attn_rows.hip", "pa_device.hpp", "pa_internal.hpp", "pa_api.cpp"]
+KERNEL_SOURCES = ["attn_rows.hip", "rows_body.hpp", "pa_device.hpp", "pa_internal.hpp", "pa_api.cpp"]
 
 
 def log(msg: str) -> None:
@@ -357,6 +357,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--copy-first", action="store_true",
+                    help="run the plain 1 GiB copy three times before the benchmark, in the same process, "
+                         "so one counter run reads both (the copy's bytes are known)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -369,7 +372,7 @@ def main() -> int:
     import paged_kv_attention_22_amd as pa
     from workloads import PRESETS
 
-    if args.calibrate_copy:
+    if args.calibrate_copy or args.copy_first:
         # An elementwise kernel that reads 1 GiB and writes 1 GiB: the
         # counters' readings for it convert counter units to bytes.
         x = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
@@ -377,9 +380,11 @@ def main() -> int:
         for _ in range(3):
             torch.mul(x, 1, out=y)
         torch.cuda.synchronize()
-        print(json.dumps({"calibration": "torch.mul int32, 1 GiB read + 1 GiB written per launch",
-                          "launches": 3}))
-        return 0
+        del x, y
+        if args.calibrate_copy:
+            print(json.dumps({"calibration": "torch.mul int32, 1 GiB read + 1 GiB written per launch",
+                              "launches": 3}))
+            return 0
 
     if not os.path.exists(pa.LIB_PATH):
         from paged_kv_attention_22_amd import build as pa_build
@@ -479,8 +484,8 @@ def main() -> int:
                       "p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                       "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2)},
         "roofline": {
-            "kernel": ("pa_decode call: plan + rows (split partials) + merge kernels" if part > 0
-                       else "pa_decode call: plan + rows kernels (one pass, longest first)"),
+            "kernel": ("pa_decode call: attention kernel (split partials) + merge kernel" if part > 0
+                       else "pa_decode call: one attention kernel (one pass, longest first, ranked in-kernel)"),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
