@@ -1,5 +1,6 @@
-"""Capture of a decode step (pa_kv_write + pa_decode) in a HIP graph, and a
-large batch that exercises every branch of the longest-first plan."""
+"""Capture in a HIP graph of a decode step (pa_kv_write + pa_decode), a mixed
+step and a shared-prefix decode, and a large batch that exercises every
+branch of the longest-first sorting launch."""
 import numpy as np
 import pytest
 import torch
@@ -138,3 +139,46 @@ def test_mixed_step_graph_replays(pa):
                                b.scale, "bf16")
         print(f"[graph] mixed replay {rep}", flush=True)
         assert_close(f64(out), ref, "bf16", f"mixed replay {rep}")
+
+
+def test_shared_prefix_graph_replays(pa):
+    """pa_decode_shared_prefix (decode kernel on the caller's stream, the
+    prefix tiles on the library's auxiliary stream, then the merge) captured
+    in a graph: replays with new q values match the oracle."""
+    from workloads import long_context
+    b = long_context(seed=74, batch=6, ctx=1200, shared_blocks=30)
+    kp, vp = oracle.kv_write(b.k_pool, b.v_pool, b.new_k, b.new_v, b.slot_mapping)
+    k_pool, v_pool = dev(kp), dev(vp)
+    q, tables, lens = dev(b.q), dev(b.block_tables), dev(b.context_lens)
+    S, P = b.num_seqs, b.shared_prefix_tokens
+    gs = dev(np.array([0, S], np.int32))
+    pl = dev(np.array([P], np.int32))
+    out = torch.empty_like(q)
+    nbytes = pa.decode_shared_prefix_workspace_bytes(S, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                                     b.max_context_len, 1, S, P, 0)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        pa.decode_shared_prefix(q, k_pool, v_pool, tables, lens, b.max_context_len, gs, pl, S, P,
+                                scale=b.scale, out=out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    rng = np.random.default_rng(10)
+    for rep in range(3):
+        q_h = f32_to_bf16_bits(rng.standard_normal(b.q.shape, dtype=np.float32))
+        q.copy_(dev(q_h))
+        out.fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = oracle.decode(q_h, kp, vp, b.block_tables, b.context_lens, b.scale, "bf16")
+        print(f"[graph] shared-prefix replay {rep}", flush=True)
+        assert_close(f64(out), ref, "bf16", f"shared-prefix replay {rep}")
