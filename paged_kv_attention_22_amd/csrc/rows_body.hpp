@@ -674,12 +674,17 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
         // lanes add their own (loop-invariant) row and column offsets.
         const int64_t o_lo0 = lo0 * tok_stride, o_hi0 = (hi0 - 8) * tok_stride;
         const int64_t o_lo1 = lo1 * tok_stride, o_hi1 = (hi1 - 8) * tok_stride;
-        // K: lane row li of chunk mt lies in the chunk's first half iff li < 8
+        // K: lane row li of chunk mt lies in the chunk's first half iff li < 8.
+        // One K load takes 64 bytes of each of 16 rows (half a 128-byte line);
+        // the next slice takes the other half, so these loads are ordinary
+        // (cached) loads: measured 7-10% faster than non-temporal ones, with
+        // which the second half went back to memory.  V loads take whole rows
+        // and stay non-temporal (cached V measured slower).
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             const T* kp = kpool + (mt ? (li < 8 ? o_lo1 : o_hi1) : (li < 8 ? o_lo0 : o_hi0));
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = ld16_stream(kp + k_lane + ks * 32);
+            for (int ks = 0; ks < KS; ++ks) kf[mt][ks] = ld16(kp + k_lane + ks * 32);
         }
         // V: slice u covers step tokens u*TPS .. u*TPS+TPS-1, all in one half
         // of one chunk (known at compile time)
