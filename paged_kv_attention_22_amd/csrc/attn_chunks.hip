@@ -7,20 +7,32 @@ namespace {
 
 using namespace chunk_impl;
 
+// The chip hands workgroups to its XCDs (each with its own L2) round-robin by
+// linear index.  Every row tile and key part of one (sequence, kv head) reads
+// the same keys, so the launch is numbered to put all of them on one XCD:
+// (sequence, kv head) pair c runs on XCD c % kXcds, its `tiles` workgroups
+// spread over that XCD's compute units.  The grid holds tiles * (pairs
+// rounded up to a multiple of kXcds) workgroups; the padding ones exit.
+constexpr int kXcds = 8;
+
 template <typename T, int D, int NT, int DEPTH, int KSPLIT>
-__global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const ChunkArgs a) {
+__global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const ChunkArgs a, int tiles) {
     __shared__ __align__(16) unsigned char lds[lds_bytes<D, KSPLIT>()];
-    chunk_block<T, D, NT, DEPTH, KSPLIT>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+    const int id = blockIdx.x;
+    const int x = id % kXcds, k = id / kXcds;
+    const int pair = k / tiles * kXcds + x;
+    if (pair >= a.num_kv_heads * a.num_seqs) return;
+    chunk_block<T, D, NT, DEPTH, KSPLIT>(a, k % tiles, pair % a.num_kv_heads, pair / a.num_kv_heads, lds);
 }
 
 template <typename T>
-void launch_typed(const ChunkArgs& a, bool small, dim3 grid, dim3 block, hipStream_t stream) {
+void launch_typed(const ChunkArgs& a, bool small, int tiles, dim3 grid, dim3 block, hipStream_t stream) {
     if (a.head_dim == 128) {
-        if (small) hipLaunchKernelGGL((chunk_kernel<T, 128, 1, kDepth, 2>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((chunk_kernel<T, 128, 2, kDepth, 1>), grid, block, 0, stream, a);
+        if (small) hipLaunchKernelGGL((chunk_kernel<T, 128, 1, kDepth, 2>), grid, block, 0, stream, a, tiles);
+        else hipLaunchKernelGGL((chunk_kernel<T, 128, 2, kDepth, 1>), grid, block, 0, stream, a, tiles);
     } else {
-        if (small) hipLaunchKernelGGL((chunk_kernel<T, 64, 1, kDepth, 2>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((chunk_kernel<T, 64, 2, kDepth, 1>), grid, block, 0, stream, a);
+        if (small) hipLaunchKernelGGL((chunk_kernel<T, 64, 1, kDepth, 2>), grid, block, 0, stream, a, tiles);
+        else hipLaunchKernelGGL((chunk_kernel<T, 64, 2, kDepth, 1>), grid, block, 0, stream, a, tiles);
     }
 }
 
@@ -40,11 +52,13 @@ int32_t launch_chunks(const ChunkArgs& a, hipStream_t stream) {
     const int64_t small_tiles = (rows + kRowsSmall - 1) / kRowsSmall * kparts;
     const bool small = !a.prefer_large && small_tiles * a.num_kv_heads * a.num_seqs < kSplitBelow;
     const int64_t tiles = small ? small_tiles : (rows + kRowsLarge - 1) / kRowsLarge * kparts;
-    if (tiles > INT32_MAX || a.num_seqs > 65535) return PA_ERR_SHAPE;
-    const dim3 grid((unsigned)tiles, a.num_kv_heads, a.num_seqs);
+    const int64_t pairs = (int64_t)a.num_kv_heads * a.num_seqs;
+    const int64_t blocks = tiles * ((pairs + kXcds - 1) / kXcds * kXcds);
+    if (blocks > INT32_MAX) return PA_ERR_SHAPE;
+    const dim3 grid((unsigned)blocks);
     const dim3 block(kRowWaves * (small ? 2 : 1) * 64);
-    if (a.dtype == PA_BF16) launch_typed<uint16_t>(a, small, grid, block, stream);
-    else launch_typed<_Float16>(a, small, grid, block, stream);
+    if (a.dtype == PA_BF16) launch_typed<uint16_t>(a, small, (int)tiles, grid, block, stream);
+    else launch_typed<_Float16>(a, small, (int)tiles, grid, block, stream);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

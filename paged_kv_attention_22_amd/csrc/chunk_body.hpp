@@ -151,7 +151,7 @@ __device__ __forceinline__ uint4 ld16_at(const unsigned char* base, uint32_t off
 // LDS of one workgroup: two K and two V tiles per key half.
 template <int D, int KSPLIT>
 constexpr int lds_bytes() {
-    return KSPLIT * 2 * kKeys * ((D * 2 + 16) + (D * 2 + 32));
+    return KSPLIT * 2 * kKeys * ((D * 2 + 32) + (D * 2 + 32));
 }
 
 // One workgroup's work: row tile / key part bx, kv head by, sequence bz, with
@@ -170,11 +170,11 @@ __device__ __forceinline__ void chunk_block(const ChunkArgs& a, int bx, int by, 
     constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
     constexpr int HT = kRowWaves * 64;   // threads of one key half
     constexpr int LOADS = kKeys * CPR / HT;  // chunks per thread per tile
-    // LDS row strides: K rows are read 16 lanes x 16 bytes down a column, a
-    // 16-byte pad spreads those rows over the banks; V rows are read by the
-    // transposing loads as 4 rows x 32 bytes per 16 lanes, which a 32-byte pad
-    // keeps apart.
-    constexpr int KROW = D * 2 + 16;
+    // LDS row strides: K rows are read 16 lanes x 16 bytes down a column and V
+    // rows by the transposing loads as 4 rows x 32 bytes per 16 lanes; a
+    // 32-byte pad spreads both over the banks (a 16-byte pad measured half the
+    // read rate of the 32-byte one for the K pattern).
+    constexpr int KROW = D * 2 + 32;
     constexpr int VROW = D * 2 + 32;
     constexpr int KTILE = kKeys * KROW;
     constexpr int VTILE = kKeys * VROW;
