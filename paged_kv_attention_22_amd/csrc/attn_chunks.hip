@@ -17,12 +17,26 @@ constexpr int kXcds = 8;
 
 template <typename T, int D, int NT, int DEPTH, int KSPLIT>
 __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const ChunkArgs a, int tiles) {
-    __shared__ __align__(16) unsigned char lds[lds_bytes<D, KSPLIT>()];
     const int id = blockIdx.x;
     const int x = id % kXcds, k = id / kXcds;
     const int pair = k / tiles * kXcds + x;
     if (pair >= a.num_kv_heads * a.num_seqs) return;
-    chunk_block<T, D, NT, DEPTH, KSPLIT>(a, k % tiles, pair % a.num_kv_heads, pair / a.num_kv_heads, lds);
+    if constexpr (KSPLIT == 1) {
+        // the tile stages, one LDS array each (the loads into them go
+        // straight from memory to LDS)
+        __shared__ __align__(16) unsigned char k0[stage_bytes<D>()], k1[stage_bytes<D>()], k2[stage_bytes<D>()];
+        __shared__ __align__(16) unsigned char v0[stage_bytes<D>()], v1[stage_bytes<D>()], v2[stage_bytes<D>()];
+        static_assert(kStages == 3, "one array per stage");
+        unsigned char* const kst[kStages] = {k0, k1, k2};
+        unsigned char* const vst[kStages] = {v0, v1, v2};
+        chunk_block<T, D, NT, DEPTH, KSPLIT>(a, k % tiles, pair % a.num_kv_heads, pair / a.num_kv_heads, nullptr,
+                                             kst, vst);
+    } else {
+        __shared__ __align__(16) unsigned char lds[lds_bytes<D, KSPLIT>()];
+        unsigned char* const none[kStages] = {nullptr, nullptr, nullptr};
+        chunk_block<T, D, NT, DEPTH, KSPLIT>(a, k % tiles, pair % a.num_kv_heads, pair / a.num_kv_heads, lds,
+                                             none, none);
+    }
 }
 
 template <typename T>

@@ -148,17 +148,69 @@ __device__ __forceinline__ uint4 ld16_at(const unsigned char* base, uint32_t off
     return make_uint4(x.x, x.y, x.z, x.w);
 }
 
-// LDS of one workgroup: two K and two V tiles per key half.
+// LDS of one workgroup with key halves: two K and two V tiles per half
+// (rows padded, filled from registers).
 template <int D, int KSPLIT>
 constexpr int lds_bytes() {
     return KSPLIT * 2 * kKeys * ((D * 2 + 32) + (D * 2 + 32));
 }
 
-// One workgroup's work: row tile / key part bx, kv head by, sequence bz, with
-// `lds` holding lds_bytes<D, KSPLIT>() bytes (16-byte aligned).  Called by
-// every thread of the workgroup.
+// Without key halves the tiles come straight from memory into LDS
+// (global_load_lds_dwordx4: each wave instruction fills 1 KiB of LDS, lane i
+// the 16 bytes at i*16, so rows cannot be padded): kStages K and kStages V
+// tiles of unpadded rows, each its own LDS array so that the compiler, which
+// tracks these loads per LDS object, does not make reads of one stage wait
+// for loads into another.  A row's 16-byte chunks are stored in swizzled
+// order (chunk j of tile row r at slot j ^ swz(r)) to keep the fragment reads
+// free of bank conflicts.
+constexpr int kStages = 3;
+template <int D>
+constexpr int stage_bytes() {
+    return kKeys * D * 2;
+}
+// K fragment reads take one chunk of 16 consecutive rows: the rows must fall
+// on 16 different 16-byte bank groups (the 64 banks of 4 bytes).
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+    constexpr int cpr = D / 8;  // chunks per row
+    return (r / (16 / cpr)) & (cpr - 1);
+}
+// The transposing V reads take 32 bytes (2 chunks) of 4 consecutive rows per
+// 16 lanes: the chunk pairs of those rows must not share bank groups.
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+    constexpr int cpr = D / 8;
+    return 2 * ((r / (16 / cpr)) & (cpr / 2 - 1));
+}
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (the counter drains in issue order for loads).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
+// One 16-byte-per-lane load from (wave-uniform base + lane offset) into LDS
+// at `dst` (wave-uniform) + lane*16.
+__device__ __forceinline__ void ld16_to_lds(const unsigned char* base, uint32_t off, unsigned char* dst) {
+    const uint64_t v = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    const unsigned char* b = reinterpret_cast<const unsigned char*>(((uint64_t)hi << 32) | lo);
+    __builtin_amdgcn_global_load_lds((global_void*)(b + off), (lds_void*)dst, 16, 0, 0);
+}
+
+// One workgroup's work: row tile / key part bx, kv head by, sequence bz.
+// With key halves (KSPLIT = 2) `lds` holds lds_bytes<D, KSPLIT>() bytes;
+// without, kst and vst are the kStages K and V stage arrays of
+// stage_bytes<D>() bytes each (all 16-byte aligned).  Called by every thread
+// of the workgroup.
 template <typename T, int D, int NT, int DEPTH, int KSPLIT>
-__device__ __forceinline__ void chunk_block(const ChunkArgs& a, int bx, int by, int bz, unsigned char* lds) {
+__device__ __forceinline__ void chunk_block(const ChunkArgs& a, int bx, int by, int bz, unsigned char* lds,
+                                            unsigned char* const (&kst)[kStages],
+                                            unsigned char* const (&vst)[kStages]) {
+    constexpr bool kDma = KSPLIT == 1;
     using V8 = typename Mma<T>::v8;
     using V2 = typename Mma<T>::v2;
     auto as_v8 = [](uint4 v) { return __builtin_bit_cast(V8, v); };
@@ -184,8 +236,8 @@ __device__ __forceinline__ void chunk_block(const ChunkArgs& a, int bx, int by, 
     // Two buffers per key half; the halves' states are merged through lds_k.
     static_assert(KSPLIT == 1 || (kRowWaves * 64 * NT * (MT * 4 + 2) * 4 <= KSPLIT * 2 * KTILE), "merge space");
     static_assert(KSPLIT * 2 * (KTILE + VTILE) == lds_bytes<D, KSPLIT>(), "LDS layout");
-    unsigned char* const lds_k = lds;
-    unsigned char* const lds_v = lds + KSPLIT * 2 * KTILE;
+    unsigned char* const lds_k = lds;  // (null without key halves)
+    unsigned char* const lds_v = kDma ? nullptr : lds + KSPLIT * 2 * KTILE;
 
     const int s = bz, g = by;
     const int nkp = max(a.key_parts, 1);
@@ -310,8 +362,8 @@ __device__ __forceinline__ void chunk_block(const ChunkArgs& a, int bx, int by, 
         }
     };
     // This half's LDS buffers.
-    unsigned char* const hk = lds_k + half * 2 * KTILE;
-    unsigned char* const hv = lds_v + half * 2 * VTILE;
+    unsigned char* const hk = kDma ? nullptr : lds_k + half * 2 * KTILE;
+    unsigned char* const hv = kDma ? nullptr : lds_v + half * 2 * VTILE;
     auto store_tile = [&](int buf, int j0, const uint4 (&kr)[LOADS], const uint4 (&vr)[LOADS]) {
         const bool tail = j0 + kKeys > kend;  // wave-uniform: only the last tile
 #pragma unroll
@@ -327,6 +379,45 @@ __device__ __forceinline__ void chunk_block(const ChunkArgs& a, int bx, int by, 
             st16(hv + buf * VTILE + key * VROW + c * 16, v);
         }
     };
+    // Direct-to-LDS loader (no key halves).  For each u, thread htid loads
+    // tile row r = (htid + u*HT) / CPR into its slot htid % CPR, taking the
+    // row's chunk slot ^ swz(r) (K and V swizzled differently); the 64 lanes
+    // of a wave fill 64/CPR whole rows (1 KiB of LDS), which lie in one pool
+    // block.  A key at or past kend (no row of this workgroup sees it) loads
+    // key kend-1 instead: finite data, whose scores are masked and whose V
+    // rows meet zero probabilities.
+    const int bmask = (1 << bsh) - 1;
+    uint32_t k_off[LOADS], v_off[LOADS];  // lane offsets inside the block, for rows below kend
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+        const int r = (htid + u * HT) / CPR, slot = htid % CPR;
+        const int base = (r & bmask) * tok_stride + g * D;
+        k_off[u] = (uint32_t)((base + (slot ^ swz_k<D>(r)) * 8) * 2);
+        v_off[u] = (uint32_t)((base + (slot ^ swz_v<D>(r)) * 8) * 2);
+    }
+    auto issue_tile = [&](int tile, unsigned char* kd, unsigned char* vd) {
+        const int j0 = (tbase + min(tile, ntiles - 1)) * kKeys;
+        int blk[LOADS];
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {  // scalar loads first, one wait for all
+            const int key0 = (rw * 64 + u * HT) / CPR;  // the wave's first row (wave-uniform)
+            const int bi = min(min(j0 + key0, kend - 1) >> bsh, a.max_blocks - 1);
+            blk[u] = min(max(bt[bi], 0), a.num_blocks - 1);
+        }
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) {
+            const int64_t boff = (int64_t)blk[u] * blk_bytes;
+            // the lane's key moves back only in the last tile (branch-free:
+            // d is zero elsewhere, as tiles start on block boundaries)
+            const int r = (htid + u * HT) / CPR;
+            const int kc = min(j0 + r, kend - 1);
+            const uint32_t d = (uint32_t)(((kc & bmask) - (r & bmask)) * tok_stride * 2);
+            const uint32_t ko = k_off[u] + d, vo = v_off[u] + d;
+            const int row = (rw * 64 + u * HT) / CPR;  // the wave's first row (wave-uniform)
+            ld16_to_lds(kbase + boff, ko, kd + row * (D * 2));
+            ld16_to_lds(vbase + boff, vo, vd + row * (D * 2));
+        }
+    };
 
     const float sl2 = a.scale * kLog2e;
     float m[kNT], lsum[kNT];
@@ -339,11 +430,27 @@ __device__ __forceinline__ void chunk_block(const ChunkArgs& a, int bx, int by, 
         for (int i = 0; i < MT; ++i) acc[nt][i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    // One tile of math on this half's LDS buffer `buf` (keys j0 .. j0+63).
-    auto compute_tile = [&](int j0, int buf) {
+    // LDS read offsets of this lane's fragments: K fragment (mt, ks) at
+    // kt + mt*16 rows + kro[ks]; V^T fragment (kk, mt) at vt + kk*32 rows +
+    // vro[mt] (and 16 rows further for its second half).
+    constexpr int KRB = kDma ? D * 2 : KROW;  // row strides in LDS
+    constexpr int VRB = kDma ? D * 2 : VROW;
+    int kro[KS], vro[MT];
+    {
+        const int k4 = lane >> 2 & 3;  // key row within the lane's group of 4
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            kro[ks] = li * KRB + (kDma ? ((ks * 4 + kg) ^ swz_k<D>(li)) * 16 : (ks * 32 + kg * 8) * 2);
+        const int vr = 4 * kg + k4;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int b = (lane & 3) * 8 + mt * 32;  // byte of the row this lane reads
+            vro[mt] = vr * VRB + (kDma ? ((b >> 4) ^ swz_v<D>(vr)) * 16 + (b & 15) : b);
+        }
+    }
+    // One tile of math on the K and V tiles at kt, vt (keys j0 .. j0+63).
+    auto compute_tile = [&](int j0, const unsigned char* kt, const unsigned char* vt) {
         if (j0 < wkend) {
-            const unsigned char* kt = hk + buf * KTILE;
-            const unsigned char* vt = hv + buf * VTILE;
             // S^T for keys j0 .. j0+63.  Every K fragment is read first and
             // the products follow, so the LDS reads overlap one another
             // instead of each waiting in front of its product; each fragment
@@ -353,7 +460,7 @@ __device__ __forceinline__ void chunk_block(const ChunkArgs& a, int bx, int by, 
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    kf[mt][ks] = ld16(kt + (mt * 16 + li) * KROW + (ks * 32 + kg * 8) * 2);
+                    kf[mt][ks] = ld16(kt + mt * 16 * KRB + kro[ks]);
             __builtin_amdgcn_sched_barrier(0);
             floatx4 st[kNT][4];
 #pragma unroll
@@ -369,15 +476,13 @@ __device__ __forceinline__ void chunk_block(const ChunkArgs& a, int bx, int by, 
             // The V^T fragments of the second product do not depend on the
             // probabilities: reading them now overlaps the reads with the
             // softmax.
-            const int k4 = lane >> 2 & 3;  // key row within the lane's group of 4
             uint2 vlo[2][MT], vhi[2][MT];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const unsigned char* v0 = vt + (32 * kk + 4 * kg + k4) * VROW + (lane & 3) * 8;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    vlo[kk][mt] = ld_tr(v0 + mt * 32);
-                    vhi[kk][mt] = ld_tr(v0 + 16 * VROW + mt * 32);
+                    vlo[kk][mt] = ld_tr(vt + 32 * kk * VRB + vro[mt]);
+                    vhi[kk][mt] = ld_tr(vt + (32 * kk + 16) * VRB + vro[mt]);
                 }
             }
             // Only a tile that crosses some row's last visible key (a
@@ -463,14 +568,10 @@ __device__ __forceinline__ void chunk_block(const ChunkArgs& a, int bx, int by, 
     // (rounded up to a multiple of DEPTH so the unrolled body runs whole); a
     // step past the half's last tile computes nothing and stores an unused
     // buffer.  One barrier per step serves both halves.
-    if (ntiles > 0) {  // ntiles == 0 only for a sequence with no visible keys
-        uint4 tile0k[LOADS], tile0v[LOADS];
-        load_tile(half, tile0k, tile0v);
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d) load_tile(half + KSPLIT * (d + 1), kreg[d], vreg[d]);
-        // An identity DPP move makes the q registers the result of a vector
-        // instruction: the tile loop then never waits on memory for them (its
-        // memory waits are for the tile prefetch only).
+    // An identity DPP move makes the q registers the result of a vector
+    // instruction: the tile loop then never waits on memory for them (its
+    // memory waits are for the tile prefetch only).
+    auto finish_q = [&]() {
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
             const uint32_t keep = 0u - (uint32_t)row_ok[nt];
@@ -484,6 +585,42 @@ __device__ __forceinline__ void chunk_block(const ChunkArgs& a, int bx, int by, 
                 qf[nt][ks] = as_v8(v);
             }
         }
+    };
+
+    if constexpr (kDma) {
+        // Pipeline without key halves: kStages LDS stages; at step i tile i
+        // is computed from stage i % kStages while tiles i+1 and i+2 are on
+        // their way into the other two.  Each step waits for its own loads of
+        // tile i (leaving tile i+1's in flight), then one barrier makes every
+        // wave's share of tile i visible and tells that every wave is done
+        // with tile i-1, whose stage then receives tile i+2.  The steps are
+        // unrolled by kStages so every stage is a fixed LDS array; steps past
+        // the last tile compute nothing and reload the last tile.
+        if (ntiles > 0) {  // ntiles == 0 only for a sequence with no visible keys
+            issue_tile(0, kst[0], vst[0]);
+            issue_tile(1, kst[1], vst[1]);
+            finish_q();
+            const int nsteps = (ntiles + kStages - 1) / kStages * kStages;
+            for (int i0 = 0; i0 < nsteps; i0 += kStages) {
+#pragma unroll
+                for (int r = 0; r < kStages; ++r) {
+                    const int i = i0 + r;
+                    wait_vmem<2 * LOADS>();
+                    __builtin_amdgcn_s_barrier();
+                    // keeps the compiler from moving LDS reads above the barrier
+                    asm volatile("" ::: "memory");
+                    issue_tile(i + 2, kst[(r + 2) % kStages], vst[(r + 2) % kStages]);
+                    compute_tile((tbase + i) * kKeys, kst[r], vst[r]);
+                }
+            }
+            wait_vmem<0>();  // the reloads past the last tile
+        }
+    } else if (ntiles > 0) {  // ntiles == 0 only for a sequence with no visible keys
+        uint4 tile0k[LOADS], tile0v[LOADS];
+        load_tile(half, tile0k, tile0v);
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) load_tile(half + KSPLIT * (d + 1), kreg[d], vreg[d]);
+        finish_q();
         store_tile(0, (tbase + half) * kKeys, tile0k, tile0v);
         __syncthreads();
         const int hsteps = (ntiles + KSPLIT - 1) / KSPLIT;
@@ -493,7 +630,7 @@ __device__ __forceinline__ void chunk_block(const ChunkArgs& a, int bx, int by, 
             for (int r = 0; r < DEPTH; ++r) {  // unrolled: static register buffers
                 const int i = i0 + r;
                 const int tile = half + KSPLIT * i;
-                compute_tile((tbase + tile) * kKeys, i & 1);
+                compute_tile((tbase + tile) * kKeys, hk + (i & 1) * KTILE, hv + (i & 1) * VTILE);
                 store_tile((i + 1) & 1, (tbase + tile + KSPLIT) * kKeys, kreg[r], vreg[r]);
                 load_tile(tile + KSPLIT * (1 + DEPTH), kreg[r], vreg[r]);
                 __syncthreads();

@@ -656,7 +656,7 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
     // auxiliary stream, the vector path on the caller's stream.  They read the
     // same pools and write disjoint rows of out; the two vector-path launches
     // use disjoint parts of the workspace.  The order matters: a chunk
-    // workgroup (4 waves of 256 registers, 72 KiB of LDS) fits on a compute
+    // workgroup (4 waves of 256 registers, 96 KiB of LDS) fits on a compute
     // unit beside one decode workgroup but not beside the three the decode
     // kernel places on an idle one, so the chunks must reach the compute units
     // first (measured: with the decode rows first the chunk kernel waited for

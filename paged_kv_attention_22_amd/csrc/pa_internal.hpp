@@ -175,7 +175,7 @@ struct ChunkArgs {
     // layout with num_items items, instead of writing out.
     float* partials;
     int32_t part_slots, num_items;
-    // 1: always the 128-row, single-key-range launch shape (72 KiB of LDS,
+    // 1: always the 128-row, single-key-range launch shape (96 KiB of LDS,
     // leaving room on each compute unit for a concurrent decode kernel).
     int32_t prefer_large;
 };
