@@ -99,21 +99,82 @@ def kv_write_bytes(b) -> int:
     return 2 * 2 * T * b.num_kv_heads * b.head_dim * b.elem_bytes + 4 * b.slot_mapping.size
 
 
+class Timer:
+    """HIP events created with hipEventDisableSystemFence, for timing only: an
+    ordinary event record performs a system-scope release (cache write-back
+    and invalidation) that stretches the interval it brackets and slows the
+    work after it.  The events come from the HIP runtime torch has already
+    loaded (same soname), so they take torch's stream handles."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n: int):
+        import ctypes
+        import torch
+        self._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._ev = []
+        for _ in range(2 * n):
+            e = ctypes.c_void_p()
+            self._check(self._hip.hipEventCreateWithFlags(ctypes.byref(e),
+                                                          ctypes.c_uint(self.DISABLE_SYSTEM_FENCE)))
+            self._ev.append(e)
+        self._stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    @staticmethod
+    def _check(rc: int) -> None:
+        if rc != 0:
+            raise RuntimeError(f"HIP event call failed with hipError {rc}")
+
+    def start(self, i: int) -> None:
+        self._check(self._hip.hipEventRecord(self._ev[2 * i], self._stream))
+
+    def stop(self, i: int) -> None:
+        self._check(self._hip.hipEventRecord(self._ev[2 * i + 1], self._stream))
+
+    def us(self, i: int) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        self._check(self._hip.hipEventSynchronize(self._ev[2 * i + 1]))
+        self._check(self._hip.hipEventElapsedTime(ctypes.byref(ms), self._ev[2 * i], self._ev[2 * i + 1]))
+        return ms.value * 1e3
+
+    def close(self) -> None:
+        for e in self._ev:
+            self._hip.hipEventDestroy(e)
+        self._ev = []
+
+
 def time_calls(fn, steps: int, warmup: int):
-    """Per-call durations (us) from HIP events on the current stream."""
+    """Per-call durations (us) from fence-free HIP events on the current
+    stream (the one the library launches on)."""
     import numpy as np
     import torch
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    t = Timer(steps)
     for i in range(steps):
-        ev[i][0].record()
+        t.start(i)
         fn(i)
-        ev[i][1].record()
+        t.stop(i)
     torch.cuda.synchronize()
-    return np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    us = np.array([t.us(i) for i in range(steps)])
+    t.close()
+    return us
+
+
+def time_steps(fn, steps: int, warmup: int) -> float:
+    """Mean wall time (us) of `steps` calls enqueued back to back between two
+    synchronisations, with nothing else on the stream."""
+    import torch
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e6 / steps
 
 
 def bench_mixed(args, b, up, dev) -> dict:
@@ -155,13 +216,14 @@ def bench_mixed(args, b, up, dev) -> dict:
         pa.decode(dec["q"], kp, vp, dec["tables"], dec["lens"], maxc, scale=b.scale)
 
     log(f"[bench] timing {args.steps} mixed steps")
+    step_mean_us = time_steps(step, args.steps, args.warmup)
     step_us = time_calls(step, args.steps, args.warmup)
     chunk_us = time_calls(chunks, args.steps, args.warmup)
     dec_us = time_calls(decode_rows, args.steps, args.warmup)
     flops = chunk_flops(b)
     es = b.elem_bytes
     dec_bytes = int(b.context_lens[npre:].sum()) * 2 * b.num_kv_heads * b.head_dim * es
-    ms = float(np.mean(step_us)) * 1e-3
+    ms = step_mean_us * 1e-3
     return {
         "metric": "pa_prefill_chunk mixed batch step time (KV write + chunks + decode rows)",
         "value": round(ms * 1e3, 2), "unit": "us", "n_gpus": 1, "steps": args.steps,
@@ -169,6 +231,9 @@ def bench_mixed(args, b, up, dev) -> dict:
         "scaling": "weak", "vs_baseline": None, "dtype": b.dtype, "data": "synthetic",
         "config": {"workload": b.name, "recipe": b.recipe, "seed": b.seed, "num_seqs": S,
                    "num_prefill_seqs": npre, "total_query_tokens": b.total_query_tokens},
+        "step_us_events": {"median": round(float(np.median(step_us)), 2),
+                           "p10": round(float(np.percentile(step_us, 10)), 2),
+                           "p90": round(float(np.percentile(step_us, 90)), 2)},
         "chunks": {"us": round(float(np.median(chunk_us)), 2), "gflop": round(flops / 1e9, 3),
                    "tflops": round(flops / (float(np.median(chunk_us)) * 1e-6) / 1e12, 2),
                    "peak_tflops": 2500.0},
@@ -421,32 +486,37 @@ def main() -> int:
     ws_bytes = pa.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
                                          b.max_context_len, args.partition)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i, t=None):
         kp, vp = pools[i & 1]
         pa.kv_write(new_k, new_v, slots, kp, vp)
-        if ev is not None:
-            ev[0].record(stream)
+        if t is not None:
+            t.start(i)
         pa.decode(q, kp, vp, tables, lens, b.max_context_len, scale=b.scale, out=out,
                   partition_tokens=args.partition, workspace=ws)
-        if ev is not None:
-            ev[1].record(stream)
+        if t is not None:
+            t.stop(i)
 
     log(f"[bench] warmup {args.warmup} steps (partition_tokens={part})")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    # Whole steps, back to back between two synchronisations, nothing else on
+    # the stream: the step throughput (value).
     log(f"[bench] timing {args.steps} steps")
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, events[i])
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_ms = [e0.elapsed_time(e1) for e0, e1 in events]
+    # The same steps again with fence-free HIP events around each pa_decode
+    # call: the decode duration (roofline).
+    timer = Timer(args.steps)
+    for i in range(args.steps):
+        step(i, timer)
+    torch.cuda.synchronize()
+    dec_ms = [timer.us(i) * 1e-3 for i in range(args.steps)]
+    timer.close()
     log(f"[bench] done: {wall * 1e3 / args.steps:.3f} ms/step, decode median "
         f"{float(np.median(dec_ms)) * 1e3:.1f} us")
 

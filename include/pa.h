@@ -26,7 +26,7 @@
  * - Every tensor pointer is DEVICE memory owned by the caller.  The library
  *   allocates no device memory and is reentrant.  Scratch memory is passed in
  *   as `workspace`, sized by the matching *_workspace_bytes.  The only state it
- *   keeps is one auxiliary stream and three events per device, created by the
+ *   keeps is one auxiliary stream and two events per device, created by the
  *   first pa_prefill_chunk call that mixes matrix-core chunks with decode rows
  *   (or the first pa_decode_shared_prefix call with a prefix) and kept for the
  *   life of the process (see pa_prefill_chunk).
@@ -273,12 +273,11 @@ int32_t pa_decode_shared_prefix(const void* q, const void* k_pool, const void* v
  * L-n+i and attends to keys 0 .. L-n+i (causal, aligned to the context end).
  * Chunks giving at least 16 (row, head) pairs per kv head run on the matrix
  * cores; the rest, and the decode rows, run on the vector path.  When
- * matrix-core chunks and decode rows are both present, the matrix-core kernel
- * runs on the library's auxiliary stream for the device, concurrently with the
- * vector path on `stream`: it waits for the work enqueued on `stream` before
- * the call, the decode rows start once it is about to launch, and work
- * enqueued on `stream` after the call waits for it (event fork/join, which
- * HIP graph capture records as well).
+ * matrix-core chunks and decode rows are both present, the vector path runs
+ * on the library's auxiliary stream for the device, concurrently with the
+ * matrix-core kernel on `stream`: it waits for the work enqueued on `stream`
+ * before the call, and work enqueued on `stream` after the call waits for it
+ * (event fork/join, which HIP graph capture records as well).
  * The workspace (pa_prefill_workspace_bytes) holds the decode rows' processing
  * order and split-context partials, then, 256-byte aligned, the prefill rows'
  * split-context partials; the two parts never overlap.

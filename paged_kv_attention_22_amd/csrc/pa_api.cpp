@@ -13,10 +13,11 @@ using namespace pa;
 
 namespace {
 
-// Auxiliary stream of one device: pa_prefill_chunk and pa_decode_shared_prefix
-// run the matrix-core chunk kernel on it, concurrently with the decode kernels
-// on the caller's stream (forked from and joined back into the caller's stream
-// with the two events).
+// Auxiliary stream of one device: pa_prefill_chunk runs its decode rows on it
+// beside the matrix-core chunk kernel on the caller's stream, and
+// pa_decode_shared_prefix its prefix phase (chunk kernel) beside the decode
+// kernel on the caller's stream; forked from and joined back into the caller's
+// stream with the two events.
 // Created on first use, kept for the life of the process; the mutex makes the
 // record / wait / launch sequence atomic across host threads.
 struct AuxStream {
@@ -24,7 +25,6 @@ struct AuxStream {
     std::mutex mu;
     hipStream_t stream = nullptr;
     hipEvent_t fork = nullptr;
-    hipEvent_t started = nullptr;  // the auxiliary stream has passed its fork wait
     hipEvent_t join = nullptr;
     bool ok = false;
 };
@@ -46,7 +46,6 @@ AuxStream* aux_for(hipStream_t s) {
         if (cur != dev && hipSetDevice(dev) != hipSuccess) return;
         a.ok = hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking) == hipSuccess &&
                hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) == hipSuccess &&
-               hipEventCreateWithFlags(&a.started, hipEventDisableTiming) == hipSuccess &&
                hipEventCreateWithFlags(&a.join, hipEventDisableTiming) == hipSuccess;
         if (cur != dev) (void)hipSetDevice(cur);
     });
@@ -652,33 +651,35 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
         c.key_parts = 1;
     }
     // The chunks (matrix cores, LDS) and the decode rows (HBM) use different
-    // parts of the chip and run concurrently: the chunk kernel on the
-    // auxiliary stream, the vector path on the caller's stream.  They read the
-    // same pools and write disjoint rows of out; the two vector-path launches
-    // use disjoint parts of the workspace.  The order matters: a chunk
-    // workgroup (4 waves of 256 registers, 96 KiB of LDS) fits on a compute
-    // unit beside one decode workgroup but not beside the three the decode
-    // kernel places on an idle one, so the chunks must reach the compute units
-    // first (measured: with the decode rows first the chunk kernel waited for
-    // their workgroups to drain and the mixed step took 10% longer).  The
-    // auxiliary stream marks `started` once it has passed its fork wait, just
-    // before the chunk launch, and the decode rows wait for that mark.  The
-    // long decode kernel stays on the caller's stream, so the final join finds
-    // the chunk kernel long finished.  (One fused launch holding both kinds of
-    // workgroup avoids the waits but measured slower: the decode loop compiled
-    // inside the larger kernel ran 12% slower.)
+    // parts of the chip and run concurrently: the chunk kernel on the caller's
+    // stream, the vector path on the auxiliary stream.  They read the same
+    // pools and write disjoint rows of out; the two vector-path launches use
+    // disjoint parts of the workspace.  The order matters: a chunk workgroup
+    // (4 waves of 256 registers, 96 KiB of LDS) fits on a compute unit beside
+    // one decode workgroup but not beside the three the decode kernel places
+    // on an idle one, so the chunks must reach the compute units first
+    // (measured: with the decode rows first the chunk kernel waited for their
+    // workgroups to drain and the mixed step took 10% longer).  A kernel on
+    // the caller's stream starts about 1 us after the previous one ends, while
+    // every wait across streams costs 8-14 us (measured on MI355X, whatever
+    // the event flags), so the chunk kernel, launched right after the fork
+    // mark, is on the compute units well before the decode rows pass their
+    // fork wait, and the one cross-stream hop in front of the long decode
+    // kernel is the fork itself.  (Chunks on the auxiliary stream behind the
+    // fork, with the decode rows waiting for a `started` mark, put two hops in
+    // front of the decode rows and measured 209 us per mixed step.  One fused
+    // launch holding both kinds of workgroup avoids the waits but measured
+    // slower: the decode loop compiled inside the larger kernel ran 12%
+    // slower.)
     AuxStream* ax = (mfma && num_decode > 0) ? aux_for(s) : nullptr;
     if (ax != nullptr) {
         std::lock_guard<std::mutex> lock(ax->mu);
-        if (hipEventRecord(ax->fork, s) != hipSuccess ||
-            hipStreamWaitEvent(ax->stream, ax->fork, 0) != hipSuccess ||
-            hipEventRecord(ax->started, ax->stream) != hipSuccess)
+        if (hipEventRecord(ax->fork, s) != hipSuccess || hipStreamWaitEvent(ax->stream, ax->fork, 0) != hipSuccess)
             return PA_ERR_LAUNCH;
-        if (int32_t st = launch_chunks(c, ax->stream)) return st;
+        if (int32_t st = launch_chunks(c, s)) return st;
+        if (int32_t st = run_rows(pre, ax->stream)) return st;  // small chunks, if any
+        if (int32_t st = run_rows(dec, ax->stream)) return st;
         if (hipEventRecord(ax->join, ax->stream) != hipSuccess) return PA_ERR_LAUNCH;
-        if (int32_t st = run_rows(pre, s)) return st;  // small chunks, if any
-        if (hipStreamWaitEvent(s, ax->started, 0) != hipSuccess) return PA_ERR_LAUNCH;
-        if (int32_t st = run_rows(dec, s)) return st;
         return hipStreamWaitEvent(s, ax->join, 0) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
     }
     if (mfma)

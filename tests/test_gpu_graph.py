@@ -97,8 +97,8 @@ def test_large_batch_plan(pa):
 
 
 def test_mixed_step_graph_replays(pa):
-    """A mixed step (KV write + pa_prefill_chunk, whose MFMA chunks run on the
-    library's auxiliary stream) captured in a graph: the fork/join is captured
+    """A mixed step (KV write + pa_prefill_chunk, whose decode rows run on the
+    library's auxiliary stream beside the MFMA chunks) captured in a graph: the fork/join is captured
     too, and replays with new q values match the oracle."""
     from workloads import mixed_prefill
     b = mixed_prefill(seed=73, chunks=2, chunk_len=48, prior_hi=120, n_decode=20,
