@@ -31,10 +31,10 @@ __global__ __launch_bounds__(kWaves * 64) void rows_kernel(const RowsArgs a) {
     rows_block<T, D, G>(a, blockIdx.x, lds);
 }
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(kWaves * 64) void mfma_rows_kernel(const RowsArgs a) {
-    __shared__ __align__(16) unsigned char lds[mfma_rows_lds_bytes<D, G>()];
-    mfma_rows_block<T, D, G>(a, blockIdx.x, lds);
+template <typename T, int D, int G, int W>
+__global__ __launch_bounds__(W * 64) void mfma_rows_kernel(const RowsArgs a) {
+    __shared__ __align__(16) unsigned char lds[mfma_rows_lds_bytes<D, G, W>()];
+    mfma_rows_block<T, D, G, W>(a, blockIdx.x, lds);
 }
 
 // Log-sum-exp merge of the partitions of one (row, q head):
@@ -192,9 +192,17 @@ int32_t launch_typed(const RowsArgs& a, hipStream_t stream) {
     const bool split = a.part_tokens > 0;
     const int64_t units = (int64_t)a.num_items * a.num_kv_heads * (split ? a.nparts - a.prefix_slots : 1);
     if (units > INT32_MAX) return PA_ERR_SHAPE;
-    if constexpr (kIs16<T> && G >= kMfmaMinGroup)
-        hipLaunchKernelGGL((mfma_rows_kernel<T, D, G>), dim3((unsigned)units), dim3(kWaves * 64), 0, stream, a);
-    else
+    if constexpr (kIs16<T> && G >= kMfmaMinGroup) {
+        // Eight waves per workgroup (two per SIMD) keep twice the loads in
+        // flight of four; a decode beside the shared-prefix tiles keeps four,
+        // which leave room on each compute unit for a prefix workgroup.
+        if (a.group_start != nullptr)
+            hipLaunchKernelGGL((mfma_rows_kernel<T, D, G, kWaves>), dim3((unsigned)units), dim3(kWaves * 64), 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((mfma_rows_kernel<T, D, G, kMaxWaves>), dim3((unsigned)units), dim3(kMaxWaves * 64),
+                               0, stream, a);
+    } else
         hipLaunchKernelGGL((rows_kernel<T, D, G>), dim3((unsigned)units), dim3(kWaves * 64), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return PA_ERR_LAUNCH;
     if (split && !a.defer_merge) return launch_merge_typed<T, D>(a, G, stream);

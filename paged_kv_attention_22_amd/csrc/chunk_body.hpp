@@ -351,9 +351,14 @@ __device__ __forceinline__ void chunk_block(const ChunkArgs& a, int bx, int by, 
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {  // scalar loads first, one wait for all
             const int key0 = (rw * 64 + u * HT) / CPR;  // wave-uniform
-            const int bi = min((j0 + key0) >> bsh, a.max_blocks - 1);
-            blk[u] = min(max(bt[bi], 0), a.num_blocks - 1);
+            blk[u] = bt[min((j0 + key0) >> bsh, a.max_blocks - 1)];
         }
+        // Left to itself the compiler clamps each id as soon as it is loaded,
+        // a full scalar-memory round trip per load; keeping the clamps apart
+        // puts all the loads in flight behind one wait.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) blk[u] = min(max(blk[u], 0), a.num_blocks - 1);
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {
             const int64_t boff = (int64_t)blk[u] * blk_bytes;
@@ -401,9 +406,11 @@ __device__ __forceinline__ void chunk_block(const ChunkArgs& a, int bx, int by, 
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {  // scalar loads first, one wait for all
             const int key0 = (rw * 64 + u * HT) / CPR;  // the wave's first row (wave-uniform)
-            const int bi = min(min(j0 + key0, kend - 1) >> bsh, a.max_blocks - 1);
-            blk[u] = min(max(bt[bi], 0), a.num_blocks - 1);
+            blk[u] = bt[min(min(j0 + key0, kend - 1) >> bsh, a.max_blocks - 1)];
         }
+        __builtin_amdgcn_sched_barrier(0);  // as in load_tile: one wait for all the id loads
+#pragma unroll
+        for (int u = 0; u < LOADS; ++u) blk[u] = min(max(blk[u], 0), a.num_blocks - 1);
 #pragma unroll
         for (int u = 0; u < LOADS; ++u) {
             const int64_t boff = (int64_t)blk[u] * blk_bytes;

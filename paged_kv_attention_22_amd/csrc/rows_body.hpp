@@ -13,7 +13,8 @@ namespace rows_impl {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;      // waves of a vector-path workgroup
+constexpr int kMaxWaves = 8;   // the most waves any decode workgroup has
 // Smallest GQA group that takes the matrix-core decode path (bf16).
 constexpr int kMfmaMinGroup = 4;
 
@@ -110,9 +111,9 @@ struct Item {
     bool skip; // left to the matrix-core kernel
 };
 
-// Inclusive sum over the kWaves*64 threads of a workgroup of one value per
-// thread.  `tmp` holds one int per wave; the caller synchronises before
-// reusing it.
+// Inclusive sum over the threads of a workgroup (at most kMaxWaves waves) of
+// one value per thread.  `tmp` holds one int per wave; the caller
+// synchronises before reusing it.
 __device__ __forceinline__ int block_inclusive_sum(int v, int* tmp) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
 #pragma unroll
@@ -134,15 +135,17 @@ __device__ __forceinline__ int block_inclusive_sum(int v, int* tmp) {
 // agree on it; each pays one pass over the lengths (kRankKeep per thread, in
 // registers), a histogram in LDS and two workgroup-wide sums, instead of a
 // separate sorting launch ahead of the attention kernel.  Called by every
-// thread of the workgroup.
-constexpr int kRankBuckets = kWaves * 64;  // one bucket per thread
+// thread of the workgroup; in a workgroup of more than kWaves waves the
+// threads past the first kRankBuckets hold no items.
+constexpr int kRankBuckets = kWaves * 64;  // one bucket per thread of the first kWaves waves
 constexpr int kRankKeep = 8;               // items per thread
-constexpr int kRankLdsInts = kRankBuckets + kWaves + 2;
+constexpr int kRankLdsInts = kRankBuckets + kMaxWaves + 2;
 __device__ __forceinline__ int rank_select(const RowsArgs& a, int z, int* rank_lds) {
     int* const hist = rank_lds;                    // [kRankBuckets]
-    int* const tmp = rank_lds + kRankBuckets;      // [kWaves]
+    int* const tmp = rank_lds + kRankBuckets;      // [waves]
     int* const pick = tmp + kWaves;                // [2]
     const int t = threadIdx.x;
+    const bool owner = t < kRankBuckets;  // holds a bucket and items
     const int n = a.num_items;
     const int32_t* lens = a.context_lens + a.seq_begin;
     // thread t owns items t*kRankKeep .. t*kRankKeep+kRankKeep-1: index order
@@ -151,17 +154,18 @@ __device__ __forceinline__ int rank_select(const RowsArgs& a, int z, int* rank_l
 #pragma unroll
     for (int j = 0; j < kRankKeep; ++j) {
         const int i = t * kRankKeep + j;
-        const int L = i < n ? lens[i] : 0;
+        const bool has = owner && i < n;
+        const int L = has ? lens[i] : 0;
         const int key = min(min(max(L, 0), a.max_context_len) >> a.rank_shift, kRankBuckets - 1);
-        pos[j] = i < n ? kRankBuckets - 1 - key : -1;
+        pos[j] = has ? kRankBuckets - 1 - key : -1;
     }
-    hist[t] = 0;
+    if (owner) hist[t] = 0;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kRankKeep; ++j)
         if (pos[j] >= 0) atomicAdd(&hist[pos[j]], 1);
     __syncthreads();
-    const int c = hist[t];
+    const int c = owner ? hist[t] : 0;
     const int incl = block_inclusive_sum(c, tmp);
     if (incl - c <= z && z < incl) {  // bucket t holds rank z
         pick[0] = t;
@@ -259,27 +263,28 @@ __device__ __forceinline__ void unit_of(const RowsArgs& a, int id, int& z, int& 
     z = rest / nparts;
 }
 
-// Merge the per-wave softmax states kWaves x (m, l, acc[D]) of the G heads
-// of one (row, kv head, partition) left in LDS, then write the normalised
-// output (final_out) or the partition's partial state for merge_kernel.
-template <typename T, int D, int G>
+// Merge the per-wave softmax states W x (m, l, acc[D]) of the G heads of one
+// (row, kv head, partition) left in LDS by the W waves of the workgroup, then
+// write the normalised output (final_out) or the partition's partial state for
+// merge_kernel.
+template <typename T, int D, int G, int W = kWaves>
 __device__ __forceinline__ void combine_waves(const RowsArgs& a, const Item& it, int z, int g, int part,
-                                              bool final_out, const float (&s_acc)[kWaves][G][D],
-                                              const float (&s_m)[kWaves][G], const float (&s_l)[kWaves][G]) {
+                                              bool final_out, const float (&s_acc)[W][G][D],
+                                              const float (&s_m)[W][G], const float (&s_l)[W][G]) {
     constexpr int E = Elem<T>::kPerChunk;
     constexpr int CPR = D / E;  // 16-byte chunks per output row
     const int Hq = a.num_q_heads;
-    for (int t = threadIdx.x; t < G * CPR; t += kWaves * 64) {
+    for (int t = threadIdx.x; t < G * CPR; t += W * 64) {
         const int h = t / CPR, cc = t % CPR;
         float M = s_m[0][h];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+        for (int w = 1; w < W; ++w) M = fmaxf(M, s_m[w][h]);
         const float mref = (M == kNegInf) ? 0.0f : M;
         float den = 0.0f, o[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < W; ++w) {
             const float wt = fast_exp2(s_m[w][h] - mref);
             den = fmaf(s_l[w][h], wt, den);
 #pragma unroll
@@ -306,11 +311,11 @@ __device__ __forceinline__ void combine_waves(const RowsArgs& a, const Item& it,
     }
 }
 
-// LDS of one rows_block workgroup: the wave merge's (acc, m, l) of each wave
-// and head, then the ranking's ints.
-template <int D, int G>
+// LDS of one rows_block workgroup (W waves): the wave merge's (acc, m, l) of
+// each wave and head, then the ranking's ints.
+template <int D, int G, int W = kWaves>
 constexpr int rows_lds_bytes() {
-    return kWaves * G * (D + 2) * 4 + kRankLdsInts * 4;
+    return W * G * (D + 2) * 4 + kRankLdsInts * 4;
 }
 
 // One workgroup of the vector-path attention: unit `bid` of the launch (see
@@ -551,17 +556,18 @@ __device__ __forceinline__ void rows_block(const RowsArgs& a, int bid, unsigned 
 //                    ds_read_b64_tr_b16 from the wave's own row-major V tile in
 //                    LDS (written with 16-byte stores; no barrier needed, the
 //                    tile is private to the wave).
-// LDS of one mfma_rows_block workgroup: each wave's V tile, then the wave
-// merge's (acc, m, l) and the ranking's ints.
-template <int D, int G>
+// LDS of one mfma_rows_block workgroup of W waves: each wave's V tile, then
+// the wave merge's (acc, m, l) and the ranking's ints.
+template <int D, int G, int W>
 constexpr int mfma_rows_lds_bytes() {
-    return kWaves * 32 * (D * 2 + 32) + rows_lds_bytes<D, G>();
+    return W * 32 * (D * 2 + 32) + rows_lds_bytes<D, G, W>();
 }
 
-// One workgroup of the matrix-core decode path: unit `bid` of the launch, with
-// `lds` holding mfma_rows_lds_bytes<D, G>() bytes (16-byte aligned).  Called
+// One workgroup of W waves of the matrix-core decode path: unit `bid` of the
+// launch, with `lds` holding mfma_rows_lds_bytes<D, G, W>() bytes (16-byte
+// aligned).  Called
 // by every thread of the workgroup.
-template <typename T, int D, int G>
+template <typename T, int D, int G, int W>
 __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsigned char* lds) {
     using V8 = typename Mma<T>::v8;
     constexpr int KS = D / 32;                // 32-dim slices (first product)
@@ -573,13 +579,13 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
     constexpr int VT = 32 * VROW;             // one wave's V tile
     constexpr float kLazy = 8.0f;
     static_assert(G <= 16, "group fits the 16 columns of one MFMA tile");
-    // LDS: [V tiles kWaves x VT][acc kWaves x G x D][m][l][ranking]
+    // LDS: [V tiles W x VT][acc W x G x D][m][l][ranking]
     unsigned char* const s_v = lds;
-    unsigned char* const rl = lds + kWaves * VT;
-    float (&s_acc)[kWaves][G][D] = *reinterpret_cast<float (*)[kWaves][G][D]>(rl);
-    float (&s_m)[kWaves][G] = *reinterpret_cast<float (*)[kWaves][G]>(rl + kWaves * G * D * 4);
-    float (&s_l)[kWaves][G] = *reinterpret_cast<float (*)[kWaves][G]>(rl + kWaves * G * (D + 1) * 4);
-    int* const rank_lds = reinterpret_cast<int*>(rl + kWaves * G * (D + 2) * 4);
+    unsigned char* const rl = lds + W * VT;
+    float (&s_acc)[W][G][D] = *reinterpret_cast<float (*)[W][G][D]>(rl);
+    float (&s_m)[W][G] = *reinterpret_cast<float (*)[W][G]>(rl + W * G * D * 4);
+    float (&s_l)[W][G] = *reinterpret_cast<float (*)[W][G]>(rl + W * G * (D + 1) * 4);
+    int* const rank_lds = reinterpret_cast<int*>(rl + W * G * (D + 2) * 4);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -605,14 +611,14 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
         qf[ks] = __builtin_bit_cast(V8, v);
     }
     // Block ids: lane i holds the table entry behind chunk
-    // b0 + 2*(wave + (kbase + i/2)*kWaves) + i%2 (as in rows_kernel: blocks of
+    // b0 + 2*(wave + (kbase + i/2)*W) + i%2 (as in rows_kernel: blocks of
     // 8 keep the chunk's second block in ids_hi).
     const int32_t* bt = a.block_tables + (int64_t)it.seq * a.max_blocks;
     const int bsh = a.block_shift;
     const ChunkMap cm = chunk_map(bsh);
     int ids = 0, ids_hi = 0;
     auto fetch_ids = [&](int kbase) {
-        const int jj = b0 + 2 * (wave + (kbase + (lane >> 1)) * kWaves) + (lane & 1);
+        const int jj = b0 + 2 * (wave + (kbase + (lane >> 1)) * W) + (lane & 1);
         ids = bt[min((jj << cm.mul) >> cm.shr, a.max_blocks - 1)];
         ids_hi = bt[min(((jj << cm.mul) + cm.mul) >> cm.shr, a.max_blocks - 1)];
     };
@@ -627,20 +633,20 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
         if (b0 >= b1 && (cascade || !(part == 0 && nblk == 0))) return;
         final_out = !cascade && nblk <= pb;
     }
-    // Steps of this wave: pair k covers blocks jb = b0 + 2*(wave + k*kWaves)
+    // Steps of this wave: pair k covers blocks jb = b0 + 2*(wave + k*W)
     // and jb + 1; the steps with both blocks full come first, then at most one
     // step that needs masking.
     const int first = b0 + 2 * wave;
-    const int nk = b1 > first ? (b1 - first + 2 * kWaves - 1) / (2 * kWaves) : 0;
+    const int nk = b1 > first ? (b1 - first + 2 * W - 1) / (2 * W) : 0;
     const int full_end = min(b1, len / kBlock);  // blocks below this are full
-    const int nkf = full_end >= first + 2 ? min(nk, (full_end - first - 2) / (2 * kWaves) + 1) : 0;
+    const int nkf = full_end >= first + 2 ? min(nk, (full_end - first - 2) / (2 * W) + 1) : 0;
     // First pool rows of the step's chunk `half`, tokens 0-7 (lo) and 8-15 (hi).
     auto rows_of = [&](int k, int half, int64_t& lo, int64_t& hi) {
         if ((k & 31) == 0 && k != 0 && half == 0) fetch_ids(k);
         const int ln = ((k & 31) << 1) | half;
         const int bl = min(max(__builtin_amdgcn_readlane(ids, ln), 0), a.num_blocks - 1);
         const int bh = min(max(__builtin_amdgcn_readlane(ids_hi, ln), 0), a.num_blocks - 1);
-        const int off = ((first + 2 * kWaves * k + half) << 4) & cm.in_block;
+        const int off = ((first + 2 * W * k + half) << 4) & cm.in_block;
         lo = ((int64_t)bl << bsh) + off;
         hi = ((int64_t)bh << bsh) + off + cm.hi_off;
     };
@@ -661,7 +667,7 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
     for (int i = 0; i < MT; ++i) acc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
     auto load = [&](uint4 (&kf)[2][KS], uint4 (&vr)[VL], int k) {
-        const int jb = first + 2 * kWaves * k;
+        const int jb = first + 2 * W * k;
         int64_t lo0, hi0, lo1, hi1;
         rows_of(k, 0, lo0, hi0);
         if (jb + 1 < b1) {
@@ -696,7 +702,7 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
         }
     };
     auto compute = [&](const uint4 (&kf)[2][KS], const uint4 (&vr)[VL], int k, bool masked) {
-        const int pos0 = (first + 2 * kWaves * k) * kBlock;  // first token of the step
+        const int pos0 = (first + 2 * W * k) * kBlock;  // first token of the step
         const int pend = min(len, b1 * kBlock);              // tokens at or past this are excluded
 #pragma unroll
         for (int u = 0; u < VL; ++u) {
@@ -785,7 +791,7 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
         }
     }
     __syncthreads();
-    combine_waves<T, D, G>(a, it, z, g, a.prefix_slots + part, final_out, s_acc, s_m, s_l);
+    combine_waves<T, D, G, W>(a, it, z, g, a.prefix_slots + part, final_out, s_acc, s_m, s_l);
 }
 
 }  // namespace rows_impl

@@ -38,6 +38,12 @@ WORKLOADS = {
                                   head_dim=128, draw_lens=lambda rng: rng.integers(1, 700, size=21)),
     "g8_d64": lambda: make_batch(62, name="g8_d64", dtype="bf16", num_q_heads=16, num_kv_heads=2,
                                  head_dim=64, draw_lens=lambda rng: rng.integers(1, 900, size=19)),
+    # more than 256 rows at G = 7 in one pass: the matrix-core decode's
+    # eight-wave workgroups rank the lengths themselves (threads past the
+    # first 256 hold no items)
+    "g7_d128_ranked": lambda: make_batch(65, name="g7_d128_ranked", dtype="bf16", num_q_heads=28,
+                                         num_kv_heads=4, head_dim=128,
+                                         draw_lens=lambda rng: rng.integers(1, 260, size=300)),
     "g5_d128_f32": lambda: make_batch(63, name="g5_d128_f32", dtype="f32", num_q_heads=10,
                                       num_kv_heads=2, head_dim=128,
                                       draw_lens=lambda rng: rng.integers(1, 300, size=6)),
