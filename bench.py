@@ -1,7 +1,10 @@
 """Benchmark: one decode step of the paged-KV attention hot path on one GPU.
 
-A step is the KV write of every sequence's new token followed by batched GQA
-decode attention over the paged pool, on the Qwen3-0.6B-shaped workload
+A step is the KV write of every sequence's new token and batched GQA decode
+attention over the paged pool (by default one pa_decode_append call, which
+fuses the two; the two-call step, pa_kv_write then pa_decode, is timed beside
+it and the pa_decode call alone gives the roofline), on the Qwen3-0.6B-shaped
+workload
 (16 q / 8 kv heads, head_dim 128, bf16, block size 16, 256 sequences with
 context = U[100,1024] + U[0,1024] capped at 2048, pool 1.2x the blocks in use,
 permuted block ids).  Inputs are synthetic and resident in HBM before timing.
@@ -408,7 +411,10 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # about 20 ms of untimed work by default: the clocks are still rising over
+    # the first few milliseconds of load (measured: a timed loop right after 5
+    # steps ran ~2% slower than the same loop later)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--partition", type=int, default=0,
                     help="partition_tokens for pa_decode (0 = library choice, -1 = one pass)")
     ap.add_argument("--workload", default="qwen3_06b_decode",
@@ -487,7 +493,13 @@ def main() -> int:
                                          b.max_context_len, args.partition)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
-    def step(i, t=None):
+    def step(i):
+        # the step's KV write fused into the decode launch
+        kp, vp = pools[i & 1]
+        pa.decode_append(q, new_k, new_v, kp, vp, tables, lens, b.max_context_len, scale=b.scale, out=out,
+                         partition_tokens=args.partition, workspace=ws)
+
+    def two_call_step(i, t=None):
         kp, vp = pools[i & 1]
         pa.kv_write(new_k, new_v, slots, kp, vp)
         if t is not None:
@@ -500,25 +512,32 @@ def main() -> int:
     log(f"[bench] warmup {args.warmup} steps (partition_tokens={part})")
     for i in range(args.warmup):
         step(i)
+        two_call_step(i)
     torch.cuda.synchronize()
     # Whole steps, back to back between two synchronisations, nothing else on
-    # the stream: the step throughput (value).
+    # the stream: first as two calls (pa_kv_write, then pa_decode), then
+    # fused (the step throughput, value).
     log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        two_call_step(i)
+    torch.cuda.synchronize()
+    wall_two = time.perf_counter() - t0
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # The same steps again with fence-free HIP events around each pa_decode
-    # call: the decode duration (roofline).
+    # The two-call steps again with fence-free HIP events around each
+    # pa_decode call: the decode duration (roofline).
     timer = Timer(args.steps)
     for i in range(args.steps):
-        step(i, timer)
+        two_call_step(i, timer)
     torch.cuda.synchronize()
     dec_ms = [timer.us(i) * 1e-3 for i in range(args.steps)]
     timer.close()
-    log(f"[bench] done: {wall * 1e3 / args.steps:.3f} ms/step, decode median "
-        f"{float(np.median(dec_ms)) * 1e3:.1f} us")
+    log(f"[bench] done: {wall * 1e3 / args.steps:.3f} ms/step ({wall_two * 1e3 / args.steps:.3f} as two calls), "
+        f"decode median {float(np.median(dec_ms)) * 1e3:.1f} us")
 
     ms_per_step = wall * 1e3 / args.steps
     dbytes, wbytes = decode_bytes(b), kv_write_bytes(b)
@@ -545,8 +564,11 @@ def main() -> int:
             "head_dim": b.head_dim, "block_size": int(b.k_pool.shape[1]), "num_blocks": b.num_blocks,
             "mean_context": round(float(b.context_lens.mean()), 2),
             "max_context": b.max_context_len, "partition_tokens": part,
-            "step": "pa_kv_write (one new token per sequence) + pa_decode",
+            "step": "pa_decode_append: the KV write of one new token per sequence fused into pa_decode",
         },
+        "two_call_step": {"ms_per_step": round(wall_two * 1e3 / args.steps, 5),
+                          "value": round((dbytes + wbytes) / (wall_two / args.steps) / 1e9, 2),
+                          "calls": "pa_kv_write + pa_decode"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(b.num_seqs / (ms_per_step * 1e-3), 1),
         "decode_us": {"mean": round(dec_mean_s * 1e6, 2),

@@ -206,6 +206,44 @@ int32_t pa_decode(const void* q, const void* k_pool, const void* v_pool,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_append -- a decode step with the step's KV-cache write fused into
+ * the attention launch: the mini_engine page names the fused KV-cache write
+ * as a fusion target (Next: fused kernels) and mini-vllm derives slots on the
+ * GPU (Milestones, item 7).  Sequence s's new token sits at position
+ * L_s - 1 (L_s = context_lens[s], which counts it); its K and V rows are
+ * stored at that position's pool slot,
+ *     block_tables[s][(L_s - 1) / B] * B + (L_s - 1) % B,
+ * and attended as pa_decode attends, in one launch and without a slot
+ * mapping.  Pools and out are bit-identical to
+ *     pa_kv_write(k_new, v_new, strides, slots of those positions) + pa_decode
+ * (the same arithmetic in the same order; the new rows are used from
+ * registers instead of being read back).
+ *
+ * q, out, block_tables, context_lens, max_context_len, scale, partition
+ *                 as for pa_decode (same workspace: pa_decode_workspace_bytes)
+ * k_new, v_new    [num_seqs, num_kv_heads, head_dim] device rows, token s at
+ *                 k_new + s * k_new_stride elements (16-byte aligned strides
+ *                 >= num_kv_heads * head_dim, so views into a packed QKV
+ *                 buffer work)
+ * k_pool, v_pool  written at the new tokens' slots only
+ * A sequence with L_s = 0 has no new token (nothing written, zero output); a
+ * table entry outside [0, num_blocks) means nothing is written for that
+ * sequence (as pa_kv_write skips a slot outside the pool).  Precondition
+ * (unchecked): the block receiving sequence s's new token is read by no other
+ * sequence of the call (a block being filled is never a shared prefix block).
+ * Errors as for pa_decode, plus PA_ERR_NULL for a missing k_new / v_new and
+ * PA_ERR_ALIGN for misaligned rows or strides.
+ */
+int32_t pa_decode_append(const void* q, const void* k_new, const void* v_new,
+                         int64_t k_new_stride, int64_t v_new_stride,
+                         void* k_pool, void* v_pool, pa_pool_desc pool,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs,
+                         int32_t max_context_len, int32_t num_q_heads, float scale,
+                         void* out, int32_t partition_tokens,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_shared_prefix -- pa_decode for groups of sequences that share a
  * prompt prefix (the blocks a prefix-cache hit points several block tables
  * at: Capstone page, Week 5 -- Prefix caching; its acceptance criteria run

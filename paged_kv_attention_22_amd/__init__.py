@@ -46,6 +46,8 @@ _SIGNATURES = {
     "pa_decode_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (c_i32, [c_vp, c_vp, c_vp, PoolDesc, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
                           c_f, c_vp, c_i32, c_vp, c_size, c_vp]),
+    "pa_decode_append": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, PoolDesc, c_vp, c_i32, c_vp,
+                                 c_i32, c_i32, c_i32, c_f, c_vp, c_i32, c_vp, c_size, c_vp]),
     "pa_decode_shared_prefix_workspace_bytes": (c_size, [c_i32] * 9),
     "pa_decode_shared_prefix": (c_i32, [c_vp, c_vp, c_vp, PoolDesc, c_vp, c_i32, c_vp, c_i32, c_i32,
                                         c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_f, c_vp, c_i32,
@@ -220,6 +222,34 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale
                          int(max_context_len), Hq, float(scale), _contig(out, "out"),
                          int(partition_tokens), wp, wb, _stream(stream))
     _check(st, "pa_decode")
+    return out
+
+
+def decode_append(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, max_context_len, scale=None,
+                  out=None, partition_tokens=0, workspace=None, stream=None):
+    """Decode step with the KV write fused in: sequence s's new K/V rows
+    (k_new[s], v_new[s]: [S, Hkv, D], token stride free) are stored at the pool
+    slot of position context_lens[s] - 1 and attended; same pools and output
+    as kv_write (slots of those positions) followed by decode()."""
+    S, Hq, D = q.shape
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.dim() != 3 or t.shape[0] != S or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError(f"{name} must be [S, Hkv, D] with contiguous token rows")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != v_pool.dtype:
+        raise TypeError("k_new/v_new and pools must share an element type")
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    hkv = k_pool.shape[2]
+    need = decode_workspace_bytes(S, Hq, hkv, D, max_context_len, partition_tokens)
+    wp, wb = _workspace(need, workspace, q.device)
+    st = lib().pa_decode_append(_contig(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), k_new.stride(0),
+                                v_new.stride(0), _contig(k_pool, "k_pool"), _contig(v_pool, "v_pool"),
+                                pool_desc(k_pool), _i32(block_tables, "block_tables"), block_tables.shape[1],
+                                _i32(context_lens, "context_lens"), S, int(max_context_len), Hq, float(scale),
+                                _contig(out, "out"), int(partition_tokens), wp, wb, _stream(stream))
+    _check(st, "pa_decode_append")
     return out
 
 

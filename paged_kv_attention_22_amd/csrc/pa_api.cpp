@@ -195,6 +195,53 @@ int32_t run_rows(const RowsArgs& a, hipStream_t s) {
     return launch_rows(a, s);
 }
 
+// pa_decode, and pa_decode_append when k_new is set (validated by the caller).
+int32_t decode_impl(const void* q, const void* k_new, const void* v_new, int64_t k_new_stride,
+                    int64_t v_new_stride, const void* k_pool, const void* v_pool, pa_pool_desc pool,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads, float scale, void* out,
+                    int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+    if (int32_t st = check_pool(pool)) return st;
+    if (int32_t st = check_heads(num_q_heads, pool.num_kv_heads)) return st;
+    if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
+        (int64_t)max_context_len > (int64_t)max_blocks_per_seq * pool.block_size)
+        return PA_ERR_SHAPE;
+    if (int32_t st = check_partition(partition_tokens)) return st;
+    if (num_seqs == 0) return PA_OK;
+    if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PA_ERR_ALIGN;
+
+    RowsArgs a = {};
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_tables = block_tables;
+    a.max_blocks = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.query_start_loc = nullptr;
+    a.seq_begin = 0;
+    a.seq_end = num_seqs;
+    a.row_begin = 0;
+    a.mfma_min_pairs = 0;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = pool.num_kv_heads;
+    a.head_dim = pool.head_dim;
+    a.num_blocks = pool.num_blocks;
+    a.block_shift = block_shift_of(pool.block_size);
+    a.dtype = pool.dtype;
+    a.max_context_len = max_context_len;
+    a.scale = scale;
+    a.out = out;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_new_stride = k_new_stride;
+    a.v_new_stride = v_new_stride;
+    const int32_t part = choose_partition(num_seqs, pool.num_kv_heads, max_context_len, partition_tokens);
+    if (int32_t st = prepare_rows(a, num_seqs, part, workspace, workspace_bytes)) return st;
+    return run_rows(a, static_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -264,41 +311,29 @@ int32_t pa_decode(const void* q, const void* k_pool, const void* v_pool, pa_pool
                   const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
                   int32_t num_q_heads, float scale, void* out, int32_t partition_tokens,
                   void* workspace, size_t workspace_bytes, void* stream) {
-    if (int32_t st = check_pool(pool)) return st;
-    if (int32_t st = check_heads(num_q_heads, pool.num_kv_heads)) return st;
-    if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
-        (int64_t)max_context_len > (int64_t)max_blocks_per_seq * pool.block_size)
-        return PA_ERR_SHAPE;
-    if (int32_t st = check_partition(partition_tokens)) return st;
-    if (num_seqs == 0) return PA_OK;
-    if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return PA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool))
-        return PA_ERR_ALIGN;
+    return decode_impl(q, nullptr, nullptr, 0, 0, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, max_context_len, num_q_heads, scale, out, partition_tokens,
+                       workspace, workspace_bytes, stream);
+}
 
-    RowsArgs a = {};
-    a.q = q;
-    a.k_pool = k_pool;
-    a.v_pool = v_pool;
-    a.block_tables = block_tables;
-    a.max_blocks = max_blocks_per_seq;
-    a.context_lens = context_lens;
-    a.query_start_loc = nullptr;
-    a.seq_begin = 0;
-    a.seq_end = num_seqs;
-    a.row_begin = 0;
-    a.mfma_min_pairs = 0;
-    a.num_q_heads = num_q_heads;
-    a.num_kv_heads = pool.num_kv_heads;
-    a.head_dim = pool.head_dim;
-    a.num_blocks = pool.num_blocks;
-    a.block_shift = block_shift_of(pool.block_size);
-    a.dtype = pool.dtype;
-    a.max_context_len = max_context_len;
-    a.scale = scale;
-    a.out = out;
-    const int32_t part = choose_partition(num_seqs, pool.num_kv_heads, max_context_len, partition_tokens);
-    if (int32_t st = prepare_rows(a, num_seqs, part, workspace, workspace_bytes)) return st;
-    return run_rows(a, static_cast<hipStream_t>(stream));
+int32_t pa_decode_append(const void* q, const void* k_new, const void* v_new, int64_t k_new_stride,
+                         int64_t v_new_stride, void* k_pool, void* v_pool, pa_pool_desc pool,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                         int32_t num_q_heads, float scale, void* out, int32_t partition_tokens,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    if (int32_t st = check_pool(pool)) return st;
+    if (num_seqs > 0) {
+        if (!k_new || !v_new) return PA_ERR_NULL;
+        const int64_t row_elems = (int64_t)pool.num_kv_heads * pool.head_dim;
+        if (k_new_stride < row_elems || v_new_stride < row_elems) return PA_ERR_SHAPE;
+        const int es = elem_size(pool.dtype);
+        if (!aligned16(k_new) || !aligned16(v_new) || (k_new_stride * es) % 16 || (v_new_stride * es) % 16)
+            return PA_ERR_ALIGN;
+    }
+    return decode_impl(q, k_new, v_new, k_new_stride, v_new_stride, k_pool, v_pool, pool, block_tables,
+                       max_blocks_per_seq, context_lens, num_seqs, max_context_len, num_q_heads, scale, out,
+                       partition_tokens, workspace, workspace_bytes, stream);
 }
 
 int32_t pa_qkv_rope_write(const void* qkv, int64_t qkv_token_stride,

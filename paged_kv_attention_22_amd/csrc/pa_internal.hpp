@@ -83,6 +83,15 @@ struct RowsArgs {
     int32_t prefix_slots;
     // Split launches: 1 leaves the merge to a later launch_merge call.
     int32_t defer_merge;
+    // Append mode (decode items only, k_new != NULL): sequence s's new token
+    // is the one at position len-1 (len = its clamped context length); its K
+    // and V rows are at k_new + s*k_new_stride and v_new + s*v_new_stride
+    // (elements, [Hkv, D] each).  The workgroup that attends position len-1
+    // uses them in place of the pool's contents and stores them at that
+    // position's pool slot when its table entry lies inside the pool.
+    const void* k_new;
+    const void* v_new;
+    int64_t k_new_stride, v_new_stride;
 };
 
 int32_t launch_rows(const RowsArgs& a, hipStream_t stream);

@@ -364,6 +364,7 @@ __device__ __forceinline__ void rows_block(const RowsArgs& a, int bid, unsigned 
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int u = 0; u < V; ++u) qv[h][u] = ld16(qp + h * D + u * R * E);
+    const bool append = a.k_new != nullptr;
     // Block ids: lane i holds the table entry behind this wave's chunk
     // kbase + i (one load per 64 chunks): the block holding the chunk (blocks
     // of 16 or 32), or the first of its two blocks with the second in ids_hi
@@ -400,19 +401,24 @@ __device__ __forceinline__ void rows_block(const RowsArgs& a, int bid, unsigned 
     }
 
     // This wave's blocks are jb = first + k*kWaves, k < nk; blocks below
-    // len/16 are full, and only the sequence's last block can be partial.
+    // len/16 are full, and only the sequence's last block can be partial.  In
+    // append mode the block holding position len-1 also takes the tail path,
+    // which puts the new token in.
     const int nk = b1 > first ? (b1 - first + kWaves - 1) / kWaves : 0;
-    const int nfull = len / kBlock;
+    const int nfull = (append ? max(len - 1, 0) : len) / kBlock;
     const int nkf = nfull > first ? min(nk, (nfull - first + kWaves - 1) / kWaves) : 0;
     // First pool rows of chunk k's tokens 0-7 (lo) and 8-15 (hi); ids are
     // clamped into the pool.
-    auto rows_of = [&](int k, int64_t& lo, int64_t& hi) {
-        if ((k & 63) == 0 && k != 0) fetch_ids(k);
+    auto chunk_rows = [&](int k, int64_t& lo, int64_t& hi) {  // ids of chunk k already fetched
         const int bl = min(max(__builtin_amdgcn_readlane(ids, k & 63), 0), a.num_blocks - 1);
         const int bh = min(max(__builtin_amdgcn_readlane(ids_hi, k & 63), 0), a.num_blocks - 1);
         const int off = ((first + k * kWaves) << 4) & cm.in_block;
         lo = ((int64_t)bl << bsh) + off;
         hi = ((int64_t)bh << bsh) + off + cm.hi_off;
+    };
+    auto rows_of = [&](int k, int64_t& lo, int64_t& hi) {
+        if ((k & 63) == 0 && k != 0) fetch_ids(k);
+        chunk_rows(k, lo, hi);
     };
 
     const int64_t tok_stride = (int64_t)Hkv * D;  // elements between tokens
@@ -484,24 +490,64 @@ __device__ __forceinline__ void rows_block(const RowsArgs& a, int bid, unsigned 
     };
 
     // Full blocks, two register buffers: the next block's loads are in flight
-    // while the current one is computed.  The reload at the end of the loop
-    // is unconditional (clamped to the last full block, which is then already
-    // cached) so that both buffers keep their registers across iterations.
+    // while the current one is computed.  The load at the end of the loop is
+    // unconditional (clamped to this wave's last block, which is then the
+    // partial tail block or an already cached full one) so that both buffers
+    // keep their registers across iterations; with an even number of full
+    // blocks the tail block is then in flight when the loop ends.  (With an
+    // odd number it is loaded after the last full block: a second live buffer
+    // for it costs registers, and with them occupancy, on several shapes.)
     uint4 ka[NT][V], va[NT][V], kb[NT][V], vb[NT][V];
+    const int last = nk - 1;
     int k = 0;
     if (nkf > 0) load(ka, va, 0);
     for (; k + 1 < nkf; k += 2) {
         load(kb, vb, k + 1);
         compute(ka, va, k, false);
-        load(ka, va, min(k + 2, nkf - 1));
+        load(ka, va, min(k + 2, last));
         compute(kb, vb, k + 1, false);
     }
+    const bool tail_loaded = nkf > 0 && k == nkf;  // the loop's last load was block nkf
     if (k < nkf) {
         compute(ka, va, k, false);
         ++k;
     }
-    if (k < nk) {  // the partial last block
-        load(ka, va, k);
+    if (k < nk && !tail_loaded) load(ka, va, k);
+    if (k < nk) {  // the partial last block (or, appending, the one holding the new token), in ka
+        if (append && ((len - 1) >> 4) == first + k * kWaves) {
+            // The new token's K and V row (this lane's chunks) replace what
+            // the pool holds at position len-1 and are stored there.  A table
+            // entry outside the pool gets neither (the read stays clamped, as
+            // pa_decode after a pa_kv_write that skipped the slot would see
+            // it).  Only this wave of this workgroup touches that row's slice
+            // of kv head g.
+            const T* kn = static_cast<const T*>(a.k_new) + it.seq * a.k_new_stride + (int64_t)g * D + c * E;
+            const T* vn = static_cast<const T*>(a.v_new) + it.seq * a.v_new_stride + (int64_t)g * D + c * E;
+            uint4 knew[V], vnew[V];
+#pragma unroll
+            for (int u = 0; u < V; ++u) {
+                knew[u] = ld16(kn + u * R * E);
+                vnew[u] = ld16(vn + u * R * E);
+            }
+            const int row = (len - 1) & 15;  // row of the chunk
+            const int raw = __builtin_amdgcn_readlane(row < 8 ? ids : ids_hi, k & 63);
+            const bool in_pool = raw >= 0 && raw < a.num_blocks;
+            int64_t lo, hi;
+            chunk_rows(k, lo, hi);
+            const int64_t o_lo = lo * tok_stride, o_hi = (hi - 8) * tok_stride;
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                if (!in_pool || rg + i * TPW != row) continue;
+                const int64_t o = (i * TPW < 8 ? o_lo : o_hi) + (i * TPW) * tok_stride;
+#pragma unroll
+                for (int u = 0; u < V; ++u) {
+                    ka[i][u] = knew[u];
+                    va[i][u] = vnew[u];
+                    st16(const_cast<T*>(kbase) + o + u * R * E, knew[u]);
+                    st16(const_cast<T*>(vbase) + o + u * R * E, vnew[u]);
+                }
+            }
+        }
         compute(ka, va, k, true);
     }
 
@@ -610,6 +656,7 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
             v = ld16(static_cast<const T*>(a.q) + ((int64_t)it.row * Hq + g * G + li) * D + ks * 32 + kg * 8);
         qf[ks] = __builtin_bit_cast(V8, v);
     }
+    const bool append = a.k_new != nullptr;
     // Block ids: lane i holds the table entry behind chunk
     // b0 + 2*(wave + (kbase + i/2)*W) + i%2 (as in rows_kernel: blocks of
     // 8 keep the chunk's second block in ids_hi).
@@ -638,17 +685,22 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
     // step that needs masking.
     const int first = b0 + 2 * wave;
     const int nk = b1 > first ? (b1 - first + 2 * W - 1) / (2 * W) : 0;
-    const int full_end = min(b1, len / kBlock);  // blocks below this are full
+    // blocks below this are full (appending, the block holding position len-1
+    // takes the tail step, which puts the new token in)
+    const int full_end = min(b1, (append ? max(len - 1, 0) : len) / kBlock);
     const int nkf = full_end >= first + 2 ? min(nk, (full_end - first - 2) / (2 * W) + 1) : 0;
     // First pool rows of the step's chunk `half`, tokens 0-7 (lo) and 8-15 (hi).
-    auto rows_of = [&](int k, int half, int64_t& lo, int64_t& hi) {
-        if ((k & 31) == 0 && k != 0 && half == 0) fetch_ids(k);
+    auto chunk_rows = [&](int k, int half, int64_t& lo, int64_t& hi) {  // ids already fetched
         const int ln = ((k & 31) << 1) | half;
         const int bl = min(max(__builtin_amdgcn_readlane(ids, ln), 0), a.num_blocks - 1);
         const int bh = min(max(__builtin_amdgcn_readlane(ids_hi, ln), 0), a.num_blocks - 1);
         const int off = ((first + 2 * W * k + half) << 4) & cm.in_block;
         lo = ((int64_t)bl << bsh) + off;
         hi = ((int64_t)bh << bsh) + off + cm.hi_off;
+    };
+    auto rows_of = [&](int k, int half, int64_t& lo, int64_t& hi) {
+        if ((k & 31) == 0 && k != 0 && half == 0) fetch_ids(k);
+        chunk_rows(k, half, lo, hi);
     };
 
     const int64_t tok_stride = (int64_t)Hkv * D;
@@ -760,21 +812,64 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
         }
     };
 
+    // Two register buffers, as in rows_block: the load at the end of the loop
+    // is clamped to this wave's last step, so with an even number of full
+    // steps the tail step is in flight when the loop ends.  (With an odd
+    // number it is loaded after the last full step: a second live buffer for
+    // it would push this kernel past 256 registers.)
     uint4 ka[2][KS], va[VL], kb[2][KS], vb[VL];
+    const int last = nk - 1;
     int k = 0;
     if (nkf > 0) load(ka, va, 0);
     for (; k + 1 < nkf; k += 2) {
         load(kb, vb, k + 1);
         compute(ka, va, k, false);
-        load(ka, va, min(k + 2, nkf - 1));
+        load(ka, va, min(k + 2, last));
         compute(kb, vb, k + 1, false);
     }
+    const bool tail_loaded = nkf > 0 && k == nkf;  // the loop's last load was step nkf
     if (k < nkf) {
         compute(ka, va, k, false);
         ++k;
     }
-    if (k < nk) {  // the step holding the partial block and/or the partition end
-        load(ka, va, k);
+    if (k < nk && !tail_loaded) load(ka, va, k);
+    if (k < nk) {  // the step holding the partial block and/or the partition end, in ka
+        const int jb = first + 2 * W * k, tc = (len - 1) >> 4;
+        if (append && (tc == jb || (tc == jb + 1 && jb + 1 < b1))) {
+            // The new token's K and V row replace what the pool holds at
+            // position len-1 and are stored there; a table entry outside the
+            // pool gets neither (as in the vector path).  K: lanes of row
+            // `row` of chunk mt hold columns ks*32 + kg*8; V: the lanes whose
+            // step token is mt*16 + row hold piece lane % CPR.  (Requested
+            // here: kept in registers from the start, they push this kernel
+            // past 256 registers.)
+            const T* kn = static_cast<const T*>(a.k_new) + it.seq * a.k_new_stride + (int64_t)g * D;
+            const T* vn = static_cast<const T*>(a.v_new) + it.seq * a.v_new_stride + (int64_t)g * D;
+            uint4 knew[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) knew[ks] = ld16(kn + ks * 32 + kg * 8);
+            const uint4 vnew = ld16(vn + (lane % CPR) * 8);
+            const int mt = tc - jb, row = (len - 1) & 15;
+            const int raw = __builtin_amdgcn_readlane(row < 8 ? ids : ids_hi, ((k & 31) << 1) | mt);
+            const bool in_pool = raw >= 0 && raw < a.num_blocks;
+            int64_t lo, hi;
+            chunk_rows(k, mt, lo, hi);
+            const int64_t orow = (row < 8 ? lo * tok_stride : (hi - 8) * tok_stride) + (int64_t)row * tok_stride;
+            if (in_pool && li == row) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    if (mt == 0) ka[0][ks] = knew[ks];
+                    else ka[1][ks] = knew[ks];
+                    st16(const_cast<T*>(kpool) + orow + kg * 8 + ks * 32, knew[ks]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < VL; ++u) {
+                if (!in_pool || (lane + 64 * u) / CPR != mt * 16 + row) continue;
+                va[u] = vnew;
+                st16(const_cast<T*>(vpool) + orow + (lane % CPR) * 8, vnew);
+            }
+        }
         compute(ka, va, k, true);
     }
 

@@ -79,6 +79,32 @@ def test_decode_validation(pa):
     assert decode(pa, S=0, q=0) == 0                   # empty batch: no-op
 
 
+def decode_append(pa, **kw):
+    args = dict(q=FAKE, kn=FAKE, vn=FAKE, ks=64, vs=64, k=FAKE, v=FAKE, pool=pool(), bt=FAKE, maxb=4,
+                ctx=FAKE, S=2, maxL=64, Hq=2, scale=0.125, out=FAKE, part=-1, ws=0, wsb=0)
+    args.update(kw)
+    return pa.lib().pa_decode_append(args["q"], args["kn"], args["vn"], args["ks"], args["vs"], args["k"],
+                                     args["v"], args["pool"], args["bt"], args["maxb"], args["ctx"], args["S"],
+                                     args["maxL"], args["Hq"], args["scale"], args["out"], args["part"],
+                                     args["ws"], args["wsb"], 0)
+
+
+def test_decode_append_validation(pa):
+    """pa_decode_append checks its new-row arguments, then everything
+    pa_decode checks."""
+    assert decode_append(pa, kn=0) == 1                 # NULL new rows
+    assert decode_append(pa, vn=0) == 1
+    assert decode_append(pa, ks=32) == 2                # stride < Hkv * D
+    assert decode_append(pa, vs=68) == 7                # stride not 16-byte aligned (bf16)
+    assert decode_append(pa, kn=FAKE + 8) == 7          # row not 16-byte aligned
+    assert decode_append(pa, ks=66, vs=66, pool=pool(dtype=0)) == 7  # fp32: 264-byte stride
+    assert decode_append(pa, q=0) == 1                  # then pa_decode's checks
+    assert decode_append(pa, pool=pool(bs=12)) == 4
+    assert decode_append(pa, maxL=65) == 2
+    assert decode_append(pa, part=16, ws=0, wsb=0) == 5
+    assert decode_append(pa, S=0, q=0, kn=0, vn=0) == 0  # empty batch: no-op
+
+
 def test_kv_write_validation(pa):
     L = pa.lib()
     p = pool()

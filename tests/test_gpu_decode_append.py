@@ -1,0 +1,164 @@
+"""pa_decode_append: the decode step with the KV-cache write fused in.
+
+Its contract is equality with the two-call step it replaces: pa_kv_write of
+every sequence's new K/V row at the slot of position context_len - 1 (taken
+from the block table), then pa_decode.  Both sides run the same arithmetic in
+the same order, so pools and outputs must match bit for bit; the output is
+also checked against the fp64 oracle.  The generator poisons (NaN) the slots
+the step's write fills, so a new row that is not put in shows up as a
+non-finite output.  Both decode paths (vector, and matrix-core at G >= 4),
+one pass and split partitions, fp32 / bf16 / fp16, block sizes 8 / 16 / 32,
+strided new rows, empty sequences, tables pointing outside the pool and a
+new token that fills a block to its last slot are covered."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import DeviceBatch, assert_close, bits, dev, ensure_built, f64
+from workloads import long_context, make_batch, qwen25_05b_decode, qwen3_06b_decode, tiny_f32
+
+pytestmark = pytest.mark.gpu
+
+PARTS = [-1, 0, 16, 64]
+
+WORKLOADS = {
+    "tiny_f32": tiny_f32,
+    "qwen3_small": lambda: qwen3_06b_decode(batch=13, prompt=(1, 300), gen=(0, 200)),
+    "qwen3_full": qwen3_06b_decode,
+    "qwen25_full": qwen25_05b_decode,
+    "long_small": lambda: long_context(batch=3, ctx=1500, shared_blocks=40),
+    "g4_d128_f16": lambda: make_batch(81, name="g4_d128_f16", dtype="f16", num_q_heads=16, num_kv_heads=4,
+                                      head_dim=128, draw_lens=lambda rng: rng.integers(1, 700, size=21)),
+    "g7_d128_ranked": lambda: make_batch(82, name="g7_d128_ranked", dtype="bf16", num_q_heads=28,
+                                         num_kv_heads=4, head_dim=128,
+                                         draw_lens=lambda rng: rng.integers(1, 260, size=300)),
+    "qwen3_bs8": lambda: qwen3_06b_decode(batch=19, prompt=(1, 400), gen=(0, 300), block_size=8),
+    "qwen25_bs32": lambda: qwen25_05b_decode(batch=17, lo=1, hi=900, block_size=32),
+}
+
+
+@pytest.fixture(scope="module")
+def pa():
+    ensure_built()
+    import paged_kv_attention_22_amd as m
+    return m
+
+
+def append_slots(b) -> np.ndarray:
+    """Pool slot of each sequence's position L - 1, read from its table (-1
+    for an empty sequence); an entry outside the pool gives a slot outside the
+    pool, which pa_kv_write skips."""
+    bs = b.k_pool.shape[1]
+    slots = np.full(b.num_seqs, -1, dtype=np.int32)
+    for s, L in enumerate(b.context_lens.tolist()):
+        if L > 0:
+            p = L - 1
+            slots[s] = int(b.block_tables[s, p // bs]) * bs + p % bs
+    return slots
+
+
+def two_calls(pa, d, b, slots, part, new_k=None, new_v=None):
+    kp, vp = d.k_pool.clone(), d.v_pool.clone()
+    pa.kv_write(d.new_k if new_k is None else new_k, d.new_v if new_v is None else new_v,
+                dev(slots), kp, vp)
+    out = pa.decode(d.q, kp, vp, d.block_tables, d.context_lens, b.max_context_len, scale=b.scale,
+                    partition_tokens=part)
+    torch.cuda.synchronize()
+    return out, kp, vp
+
+
+def fused(pa, d, b, part, new_k=None, new_v=None):
+    kp, vp = d.k_pool.clone(), d.v_pool.clone()
+    out = pa.decode_append(d.q, d.new_k if new_k is None else new_k, d.new_v if new_v is None else new_v,
+                           kp, vp, d.block_tables, d.context_lens, b.max_context_len, scale=b.scale,
+                           partition_tokens=part)
+    torch.cuda.synchronize()
+    return out, kp, vp
+
+
+def raw(x: np.ndarray) -> np.ndarray:
+    """Bit patterns of a host pool (fp32 values, or 16-bit patterns already)."""
+    return x.view(np.uint32) if x.dtype == np.float32 else x.view(np.uint16)
+
+
+def assert_same(a, b, what):
+    for x, y, name in zip(a, b, ("out", "k_pool", "v_pool")):
+        assert np.array_equal(bits(x), bits(y)), f"{what}: {name} differs"
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_append_equals_write_then_decode(pa, name):
+    b = WORKLOADS[name]()
+    assert b.num_prefill_seqs == 0
+    slots = append_slots(b)
+    assert np.array_equal(slots, b.slot_mapping[:b.num_seqs]), "generator writes position L-1"
+    d = DeviceBatch(b)
+    kp, vp = oracle.kv_write(b.k_pool, b.v_pool, b.new_k, b.new_v, slots)
+    ref = oracle.decode(b.q, kp, vp, b.block_tables, b.context_lens, b.scale, b.dtype)
+    for part in PARTS:
+        print(f"[append] {name} B={b.num_seqs} Hq={b.num_q_heads} Hkv={b.num_kv_heads} D={b.head_dim} "
+              f"bs={b.k_pool.shape[1]} part={part}", flush=True)
+        got = fused(pa, d, b, part)
+        assert_same(got, two_calls(pa, d, b, slots, part), f"{name} part={part}")
+        assert_close(f64(got[0]), ref, b.dtype, f"{name} part={part}")
+        assert np.array_equal(bits(got[1]), raw(kp)) and np.array_equal(bits(got[2]), raw(vp))
+
+
+def test_append_strided_rows(pa):
+    """New rows as views into a packed [S, (Hq + 2 Hkv) * D] buffer."""
+    b = qwen3_06b_decode(batch=23, prompt=(1, 500), gen=(0, 300))
+    d = DeviceBatch(b)
+    S, hq, hkv, D = b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim
+    packed = torch.zeros(S, (hq + 2 * hkv) * D, dtype=d.q.dtype, device=d.q.device)
+    packed[:, hq * D:(hq + hkv) * D] = d.new_k.reshape(S, -1)
+    packed[:, (hq + hkv) * D:] = d.new_v.reshape(S, -1)
+    nk = packed[:, hq * D:(hq + hkv) * D].view(S, hkv, D)
+    nv = packed[:, (hq + hkv) * D:].view(S, hkv, D)
+    assert nk.stride(0) == (hq + 2 * hkv) * D
+    slots = append_slots(b)
+    for part in (-1, 64):
+        assert_same(fused(pa, d, b, part, nk, nv), two_calls(pa, d, b, slots, part), f"strided part={part}")
+
+
+@pytest.mark.parametrize("group", [2, 7])
+def test_append_edge_cases(pa, group):
+    """Empty sequences (nothing written, zero output), a last-block table
+    entry outside the pool (nothing written; the read is clamped into the pool
+    as pa_decode clamps it), new tokens that fill a block's last slot or open a
+    new block, and a one-token context.  q and the new rows are drawn here, one
+    per sequence (the generator gives empty sequences none)."""
+    lens = np.array([0, 16, 17, 1, 32, 0, 31, 100, 48, 5], dtype=np.int32)
+    b = make_batch(90 + group, name=f"edge_g{group}", dtype="bf16", num_q_heads=4 * group, num_kv_heads=4,
+                   head_dim=128, draw_lens=lambda rng: lens,
+                   draw_query_lens=lambda rng, ls: np.minimum(ls, 1))
+    b.block_tables[7, (100 - 1) // 16] = b.num_blocks + 3   # the block of position 99: outside the pool
+    d = DeviceBatch(b)
+    S = b.num_seqs
+    g = torch.Generator(device="cpu").manual_seed(1234 + group)
+    d.q = torch.randn(S, b.num_q_heads, 128, generator=g).to(torch.bfloat16).cuda()
+    nk = torch.randn(S, 4, 128, generator=g).to(torch.bfloat16).cuda()
+    nv = torch.randn(S, 4, 128, generator=g).to(torch.bfloat16).cuda()
+    slots = append_slots(b)
+    assert slots[7] >= b.num_blocks * 16 and slots[0] == -1 and slots[5] == -1
+    for part in (-1, 16):
+        got = fused(pa, d, b, part, nk, nv)
+        assert_same(got, two_calls(pa, d, b, slots, part, nk, nv), f"edge g={group} part={part}")
+        o = bits(got[0])
+        assert not o[0].any() and not o[5].any()          # empty sequences: zeros
+        # nothing but the new tokens' slots (inside the pool) changed
+        for pool_new, pool_old in ((got[1], d.k_pool), (got[2], d.v_pool)):
+            changed = np.nonzero((bits(pool_new) != bits(pool_old)).reshape(-1, 4 * 128).any(axis=1))[0]
+            assert set(changed.tolist()) <= {int(x) for x in slots if 0 <= x < b.num_blocks * 16}
+
+
+def test_append_rejects_leave_pools(pa):
+    b = qwen3_06b_decode(batch=5, prompt=(1, 100), gen=(0, 50))
+    d = DeviceBatch(b)
+    before = bits(d.k_pool)
+    bad = d.new_k[:, :, :64]                              # row too short: [S, Hkv, 64] in a D = 128 pool
+    with pytest.raises((RuntimeError, ValueError)):
+        pa.decode_append(d.q, bad, d.new_v, d.k_pool, d.v_pool, d.block_tables, d.context_lens,
+                         b.max_context_len, scale=b.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(d.k_pool), before)
