@@ -1,5 +1,5 @@
-"""Capture in a HIP graph of a decode step (pa_kv_write + pa_decode), a mixed
-step and a shared-prefix decode, and a large batch that exercises every
+"""Capture in a HIP graph of a decode step (pa_kv_write + pa_decode, and the
+fused pa_decode_append), a mixed step and a shared-prefix decode, and a large batch that exercises every
 branch of the longest-first sorting launch."""
 import numpy as np
 import pytest
@@ -71,6 +71,59 @@ def test_decode_step_graph_replays(pa):
         print(f"[graph] replay {rep}: max L {int(L.max())}", flush=True)
         assert_close(f64(out), ref, "bf16", f"replay {rep}")
         assert np.array_equal(bits(k_pool), kp_h), f"replay {rep}: pool write"
+
+
+@pytest.mark.parametrize("part", [-1, 64])
+def test_decode_append_graph_replays(pa, part):
+    """The fused step (pa_decode_append) captured once and replayed with new
+    q, new rows and shorter lengths written eagerly in between: the slot of
+    each new row follows the lengths on the device, and every replay must
+    match the oracle for the pool state it produced (pool bit-exact)."""
+    b = qwen3_06b_decode(seed=74, batch=40, prompt=(30, 400), gen=(0, 300))
+    maxL = b.max_context_len
+    k_pool, v_pool = dev(b.k_pool), dev(b.v_pool)
+    q, new_k, new_v = dev(b.q), dev(b.new_k), dev(b.new_v)
+    tables, lens = dev(b.block_tables), dev(b.context_lens)
+    out = torch.empty_like(q)
+    nbytes = pa.decode_workspace_bytes(b.num_seqs, 16, 8, 128, maxL, part)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        pa.decode_append(q, new_k, new_v, k_pool, v_pool, tables, lens, maxL, scale=b.scale, out=out,
+                         partition_tokens=part, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                   # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+
+    kp_h, vp_h = oracle.kv_write(b.k_pool, b.v_pool, b.new_k, b.new_v, b.slot_mapping)  # warm-up's write
+    rng = np.random.default_rng(6)
+    L = b.context_lens.astype(np.int64)
+    for rep in range(4):
+        L = np.maximum(L - rng.integers(0, 20, size=L.shape), 1)
+        pos = L - 1
+        slots_h = (b.block_tables[np.arange(b.num_seqs), pos // 16].astype(np.int64) * 16
+                   + pos % 16).astype(np.int32)
+        q_h = f32_to_bf16_bits(rng.standard_normal(b.q.shape, dtype=np.float32))
+        nk_h = f32_to_bf16_bits(rng.standard_normal(b.new_k.shape, dtype=np.float32))
+        nv_h = f32_to_bf16_bits(rng.standard_normal(b.new_v.shape, dtype=np.float32))
+        q.copy_(dev(q_h)); new_k.copy_(dev(nk_h)); new_v.copy_(dev(nv_h))
+        lens.copy_(dev(L.astype(np.int32)))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        kp_h, vp_h = oracle.kv_write(kp_h, vp_h, nk_h, nv_h, slots_h)
+        ref = oracle.decode(q_h, kp_h, vp_h, b.block_tables, L, b.scale, "bf16")
+        print(f"[graph] append part={part} replay {rep}: max L {int(L.max())}", flush=True)
+        assert_close(f64(out), ref, "bf16", f"append replay {rep}")
+        assert np.array_equal(bits(k_pool), kp_h) and np.array_equal(bits(v_pool), vp_h), \
+            f"append replay {rep}: pool write"
 
 
 def test_large_batch_plan(pa):
