@@ -385,6 +385,22 @@ def bench_shared_prefix(args, b, up) -> dict:
     }
 
 
+def copy_reference(steps: int) -> dict:
+    """What a plain streaming kernel reaches on the same GPU in the same run:
+    torch's elementwise int32 multiply over 1 GiB (1 GiB read + 1 GiB
+    written), timed like the decode calls.  Context for the roofline fraction,
+    not part of it (the fraction stays against the 8 TB/s published peak)."""
+    import numpy as np
+    import torch
+    x = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    y = torch.empty_like(x)
+    us = time_calls(lambda i: torch.mul(x, 1, out=y), max(steps, 10), 10)
+    del x, y
+    gbs = 2 * (1 << 30) / (float(np.mean(us)) * 1e-6) / 1e9
+    return {"kernel": "torch.mul int32, 1 GiB read + 1 GiB written", "us": round(float(np.mean(us)), 2),
+            "gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(b, min_seconds: float = 10.0) -> dict:
     """The fp64 oracle on the same step (KV write + decode), one thread,
     repeated over the whole batch until at least min_seconds have passed."""
@@ -589,6 +605,7 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    result["copy_reference"] = copy_reference(args.steps)
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(b)
