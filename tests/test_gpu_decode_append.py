@@ -7,7 +7,8 @@ the same order, so pools and outputs must match bit for bit; the output is
 also checked against the fp64 oracle.  The generator poisons (NaN) the slots
 the step's write fills, so a new row that is not put in shows up as a
 non-finite output.  Both decode paths (vector, and matrix-core at G >= 4),
-one pass and split partitions, fp32 / bf16 / fp16, block sizes 8 / 16 / 32,
+one pass and split partitions, in-kernel ranking and the sorting launch of
+batches over 2048 sequences, fp32 / bf16 / fp16, block sizes 8 / 16 / 32,
 strided new rows, empty sequences, tables pointing outside the pool and a
 new token that fills a block to its last slot are covered."""
 import numpy as np
@@ -33,6 +34,9 @@ WORKLOADS = {
     "g7_d128_ranked": lambda: make_batch(82, name="g7_d128_ranked", dtype="bf16", num_q_heads=28,
                                          num_kv_heads=4, head_dim=128,
                                          draw_lens=lambda rng: rng.integers(1, 260, size=300)),
+    # more than 2048 sequences: the processing order comes from the sorting launch
+    "many_2100": lambda: make_batch(83, name="many_2100", dtype="bf16", num_q_heads=4, num_kv_heads=2,
+                                    head_dim=64, draw_lens=lambda rng: rng.integers(1, 60, size=2100)),
     "qwen3_bs8": lambda: qwen3_06b_decode(batch=19, prompt=(1, 400), gen=(0, 300), block_size=8),
     "qwen25_bs32": lambda: qwen25_05b_decode(batch=17, lo=1, hi=900, block_size=32),
 }
