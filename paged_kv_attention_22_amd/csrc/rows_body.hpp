@@ -7,6 +7,14 @@
 #include "pa_internal.hpp"
 #include <type_traits>
 
+// No implicit contraction of a*b+c in the decode bodies: each body is inlined
+// into several code paths (the full-block loop, the tail block, the fused
+// append), and a multiply-add the compiler fuses in one copy but not in
+// another would round differently, so the same block of keys would give
+// different bits depending on the path that read it.  Explicit fmaf calls are
+// still fused.
+#pragma clang fp contract(off)
+
 namespace pa {
 namespace rows_impl {
 
