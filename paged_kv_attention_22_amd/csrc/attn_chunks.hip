@@ -39,15 +39,22 @@ __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const Ch
     }
 }
 
+// Launch shapes: 64 rows with key halves (small launches), 128 rows in one
+// key range (large launches sharing the chip), 128 rows with key halves (large
+// launches that run alone).
+enum Shape { kSmallHalves, kLargeRange, kLargeHalves };
+
+template <typename T, int D>
+void launch_shape(const ChunkArgs& a, Shape shape, int tiles, dim3 grid, dim3 block, hipStream_t stream) {
+    if (shape == kSmallHalves) hipLaunchKernelGGL((chunk_kernel<T, D, 1, kDepth, 2>), grid, block, 0, stream, a, tiles);
+    else if (shape == kLargeRange) hipLaunchKernelGGL((chunk_kernel<T, D, 2, kDepth, 1>), grid, block, 0, stream, a, tiles);
+    else hipLaunchKernelGGL((chunk_kernel<T, D, 2, kDepth, 2>), grid, block, 0, stream, a, tiles);
+}
+
 template <typename T>
-void launch_typed(const ChunkArgs& a, bool small, int tiles, dim3 grid, dim3 block, hipStream_t stream) {
-    if (a.head_dim == 128) {
-        if (small) hipLaunchKernelGGL((chunk_kernel<T, 128, 1, kDepth, 2>), grid, block, 0, stream, a, tiles);
-        else hipLaunchKernelGGL((chunk_kernel<T, 128, 2, kDepth, 1>), grid, block, 0, stream, a, tiles);
-    } else {
-        if (small) hipLaunchKernelGGL((chunk_kernel<T, 64, 1, kDepth, 2>), grid, block, 0, stream, a, tiles);
-        else hipLaunchKernelGGL((chunk_kernel<T, 64, 2, kDepth, 1>), grid, block, 0, stream, a, tiles);
-    }
+void launch_typed(const ChunkArgs& a, Shape shape, int tiles, dim3 grid, dim3 block, hipStream_t stream) {
+    if (a.head_dim == 128) launch_shape<T, 128>(a, shape, tiles, grid, block, stream);
+    else launch_shape<T, 64>(a, shape, tiles, grid, block, stream);
 }
 
 }  // namespace
@@ -66,13 +73,14 @@ int32_t launch_chunks(const ChunkArgs& a, hipStream_t stream) {
     const int64_t small_tiles = (rows + kRowsSmall - 1) / kRowsSmall * kparts;
     const bool small = !a.prefer_large && small_tiles * a.num_kv_heads * a.num_seqs < kSplitBelow;
     const int64_t tiles = small ? small_tiles : (rows + kRowsLarge - 1) / kRowsLarge * kparts;
+    const Shape shape = small ? kSmallHalves : (a.alone ? kLargeHalves : kLargeRange);
     const int64_t pairs = (int64_t)a.num_kv_heads * a.num_seqs;
     const int64_t blocks = tiles * ((pairs + kXcds - 1) / kXcds * kXcds);
     if (blocks > INT32_MAX) return PA_ERR_SHAPE;
     const dim3 grid((unsigned)blocks);
-    const dim3 block(kRowWaves * (small ? 2 : 1) * 64);
-    if (a.dtype == PA_BF16) launch_typed<uint16_t>(a, small, (int)tiles, grid, block, stream);
-    else launch_typed<_Float16>(a, small, (int)tiles, grid, block, stream);
+    const dim3 block(kRowWaves * (shape == kLargeRange ? 1 : 2) * 64);
+    if (a.dtype == PA_BF16) launch_typed<uint16_t>(a, shape, (int)tiles, grid, block, stream);
+    else launch_typed<_Float16>(a, shape, (int)tiles, grid, block, stream);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -684,6 +684,7 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
         c.min_pairs = kMfmaMinPairs;
         c.causal = 1;
         c.key_parts = 1;
+        c.alone = num_decode == 0;  // nothing runs beside the chunk kernel
     }
     // The chunks (matrix cores, LDS) and the decode rows (HBM) use different
     // parts of the chip and run concurrently: the chunk kernel on the caller's

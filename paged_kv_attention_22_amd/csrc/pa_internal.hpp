@@ -187,6 +187,10 @@ struct ChunkArgs {
     // 1: always the 128-row, single-key-range launch shape (96 KiB of LDS,
     // leaving room on each compute unit for a concurrent decode kernel).
     int32_t prefer_large;
+    // 1: nothing else runs beside this launch (a prefill batch without decode
+    // rows): a large launch takes two key halves as well (8 waves, 144 KiB of
+    // LDS per workgroup), which would crowd out a kernel sharing the chip.
+    int32_t alone;
 };
 
 // Returns PA_ERR_UNSUPPORTED when no matrix-core kernel exists for the shape

@@ -29,6 +29,12 @@ WORKLOADS = {
     "mixed_one_row_chunks": lambda: mixed_prefill(chunks=2, chunk_len=1, prior_hi=40,
                                                   n_decode=2, dec_lo=1, dec_hi=50),
     "prefill_only_p0": lambda: mixed_prefill(chunks=2, chunk_len=70, prior_hi=0, n_decode=0),
+    # large launches with no decode rows beside them: 128 rows with key halves
+    "prefill_only_large": lambda: mixed_prefill(seed=17, chunks=4, chunk_len=300, prior_hi=600, n_decode=0),
+    "prefill_only_d64": lambda: mixed_prefill(seed=18, chunks=8, chunk_len=200, prior_hi=500, n_decode=0,
+                                              num_q_heads=14, num_kv_heads=2, head_dim=64),
+    "prefill_only_f16": lambda: mixed_prefill(seed=19, chunks=4, chunk_len=300, prior_hi=600, n_decode=0,
+                                              dtype="f16"),
     "mixed_full": mixed_prefill,
     # head_dim 64 (Qwen2.5-0.5B heads, G = 7): a small launch (key halves) and
     # a large one (two row tiles per wave)
@@ -132,7 +138,8 @@ def test_decode_rows_match_pa_decode(pa):
     assert torch.equal(o.view(torch.int16), whole[rows].view(torch.int16))
 
 
-@pytest.mark.parametrize("shape", [(3, 72, 150), (6, 200, 900)], ids=["key_halves", "one_range"])
+@pytest.mark.parametrize("shape", [(3, 72, 150, 2), (6, 200, 900, 2), (6, 200, 900, 0)],
+                         ids=["key_halves", "one_range", "alone_key_halves"])
 def test_prefill_needle_exact(pa, shape):
     """Causal chunks with one dominant key per (sequence, kv head): q rows are
     c * e0 and K has dim 0 zero except at the needle token (c there), c = 64,
@@ -141,9 +148,10 @@ def test_prefill_needle_exact(pa, shape):
     group of scores left out) overflows the exponentials instead.  Rows
     before it see equal scores and get the mean of their visible V rows.
     The small batch launches the matrix-core kernel with key halves, the
-    larger one without."""
-    chunks, chunk_len, prior_hi = shape
-    b = mixed_prefill(seed=9, chunks=chunks, chunk_len=chunk_len, prior_hi=prior_hi, n_decode=2,
+    larger one without, and the larger one with no decode rows (the chunk
+    kernel alone) with 128-row tiles and key halves."""
+    chunks, chunk_len, prior_hi, n_decode = shape
+    b = mixed_prefill(seed=9, chunks=chunks, chunk_len=chunk_len, prior_hi=prior_hi, n_decode=n_decode,
                       dec_lo=20, dec_hi=100)
     kp, vp = oracle.kv_write(b.k_pool, b.v_pool, b.new_k, b.new_v, b.slot_mapping)
     rng = np.random.default_rng(99)
