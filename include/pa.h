@@ -24,12 +24,14 @@
  * Conventions shared by every call
  * --------------------------------
  * - Every tensor pointer is DEVICE memory owned by the caller.  The library
- *   allocates no device memory and is reentrant.  Scratch memory is passed in
- *   as `workspace`, sized by the matching *_workspace_bytes.  The only state it
- *   keeps is one auxiliary stream and two events per device, created by the
- *   first pa_prefill_chunk call that mixes matrix-core chunks with decode rows
- *   (or the first pa_decode_shared_prefix call with a prefix) and kept for the
- *   life of the process (see pa_prefill_chunk).
+ *   allocates no device memory, keeps no handle, stream, event or other
+ *   global state between calls, and is reentrant.  Scratch memory is passed in
+ *   as `workspace`, sized by the matching *_workspace_bytes.  The two calls
+ *   that can run two kernels side by side (pa_prefill_chunk,
+ *   pa_decode_shared_prefix) take a second stream and two events from the
+ *   caller (pa_aux_stream); without one they run on `stream` alone.  (The
+ *   block manager's state lives in the handle the caller creates and
+ *   destroys.)
  * - Every call validates its host arguments first.  On failure it returns a
  *   non-zero pa_status, enqueues nothing and leaves every output untouched.
  * - On success the work is enqueued on `stream` (a hipStream_t; NULL means the
@@ -71,7 +73,9 @@ typedef enum {
     PA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
     PA_ERR_LAUNCH = 6,      /* the HIP runtime rejected a launch */
     PA_ERR_ALIGN = 7,       /* a pointer or stride breaks 16-byte alignment */
-    PA_ERR_CAPACITY = 8     /* block manager: not enough free blocks (nothing changed) */
+    PA_ERR_CAPACITY = 8,    /* block manager: not enough free blocks (nothing changed) */
+    PA_ERR_STREAM = 9       /* pa_aux_stream incomplete, equal to the call's stream,
+                               or on another device */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
@@ -87,6 +91,28 @@ typedef struct {
     int32_t head_dim;
     int32_t dtype;
 } pa_pool_desc;
+
+/* A second stream owned by the caller, for the calls that can run two
+ * kernels at once (pa_prefill_chunk: decode rows beside matrix-core chunks;
+ * pa_decode_shared_prefix: the prefix phase beside the decode kernel).
+ *   stream      hipStream_t on the same device as the call's stream, and not
+ *               that stream
+ *   fork_event  hipEvent_t; the call records it on its stream and makes
+ *               `stream` wait for it, so the auxiliary work follows everything
+ *               enqueued on the call's stream before the call
+ *   join_event  hipEvent_t; the call records it on `stream` and makes its own
+ *               stream wait for it, so work enqueued on the call's stream after
+ *               the call follows the auxiliary work
+ * Create the events with hipEventDisableTiming (they only order work).  All
+ * three stay the caller's; the library keeps no reference past the call.
+ * Concurrent calls from several host threads must not share one
+ * pa_aux_stream (their records and waits would interleave).  HIP graph capture
+ * records the fork and the join like any other cross-stream dependency. */
+typedef struct {
+    void* stream;
+    void* fork_event;
+    void* join_event;
+} pa_aux_stream;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* pa_status_str(int32_t status);
@@ -269,11 +295,15 @@ int32_t pa_decode_append(const void* q, const void* k_new, const void* v_new,
  * workspace       pa_decode_shared_prefix_workspace_bytes(...) bytes,
  *                 16-byte aligned (never zero)
  *
+ * aux             NULL, or the caller's second stream (pa_aux_stream): the
+ *                 prefix phase then runs on it beside the decode kernel
+ *
  * Work: the prefix of each group is attended on the matrix cores, the group's
  * members as rows of one block that sees all of the prefix (split into key
- * parts over workgroups), on the library's auxiliary stream (forked from and
- * joined back into `stream`); the rest of each context runs on the decode path
- * on `stream`; a log-sum-exp merge on `stream` combines the partial states.
+ * parts over workgroups): on aux->stream (forked from and joined back into
+ * `stream`) when aux is given, else first on `stream`; the rest of each
+ * context runs on the decode path on `stream`; a log-sum-exp merge on
+ * `stream` combines the partial states.
  * Supported: bf16 or fp16 pools (the matrix cores), group size 1..8.
  * Preconditions on the group arrays are not checked beyond memory safety:
  * rows of groups larger than max_group_size, or groups that overlap, give
@@ -294,7 +324,8 @@ int32_t pa_decode_shared_prefix(const void* q, const void* k_pool, const void* v
                                 int32_t num_groups, int32_t max_group_size,
                                 int32_t max_prefix_len, int32_t num_q_heads, float scale,
                                 void* out, int32_t partition_tokens,
-                                void* workspace, size_t workspace_bytes, void* stream);
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                const pa_aux_stream* aux);
 
 /*
  * pa_prefill_chunk -- causal attention for a packed mixed batch.
@@ -311,11 +342,12 @@ int32_t pa_decode_shared_prefix(const void* q, const void* k_pool, const void* v
  * L-n+i and attends to keys 0 .. L-n+i (causal, aligned to the context end).
  * Chunks giving at least 16 (row, head) pairs per kv head run on the matrix
  * cores; the rest, and the decode rows, run on the vector path.  When
- * matrix-core chunks and decode rows are both present, the vector path runs
- * on the library's auxiliary stream for the device, concurrently with the
- * matrix-core kernel on `stream`: it waits for the work enqueued on `stream`
- * before the call, and work enqueued on `stream` after the call waits for it
- * (event fork/join, which HIP graph capture records as well).
+ * matrix-core chunks and decode rows are both present and `aux` is given, the
+ * vector path runs on aux->stream, concurrently with the matrix-core kernel on
+ * `stream`: it waits for the work enqueued on `stream` before the call, and
+ * work enqueued on `stream` after the call waits for it (event fork/join,
+ * which HIP graph capture records as well).  With aux NULL every kernel runs
+ * on `stream`, the matrix-core chunks first.
  * The workspace (pa_prefill_workspace_bytes) holds the decode rows' processing
  * order and split-context partials, then, 256-byte aligned, the prefill rows'
  * split-context partials; the two parts never overlap.
@@ -333,7 +365,8 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc,
                          const int32_t* context_lens, int32_t max_context_len,
                          int32_t num_q_heads, float scale, void* out,
                          int32_t partition_tokens,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         const pa_aux_stream* aux);
 
 /*
  * Host-side block manager (no GPU involved): the block pool's free list, the

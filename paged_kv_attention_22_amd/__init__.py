@@ -12,9 +12,11 @@ stream.  If libpa.so is missing the calls raise; there is no fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
+import threading
 
 import torch
 
@@ -22,7 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 BLOCK_SIZE = 16
 
 PA_OK, PA_F32, PA_BF16, PA_F16 = 0, 0, 1, 2
-PA_ERR_SHAPE, PA_ERR_CAPACITY = 2, 8
+PA_ERR_SHAPE, PA_ERR_WORKSPACE, PA_ERR_CAPACITY, PA_ERR_STREAM = 2, 5, 8, 9
 
 c_i32, c_i64, c_size, c_vp, c_f = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
                                   ctypes.c_void_p, ctypes.c_float)
@@ -31,6 +33,11 @@ c_i32, c_i64, c_size, c_vp, c_f = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size
 class PoolDesc(ctypes.Structure):
     _fields_ = [("num_blocks", c_i32), ("block_size", c_i32), ("num_kv_heads", c_i32),
                 ("head_dim", c_i32), ("dtype", c_i32)]
+
+
+class AuxStream(ctypes.Structure):
+    """pa_aux_stream: a second stream and fork/join events owned by the caller."""
+    _fields_ = [("stream", c_vp), ("fork_event", c_vp), ("join_event", c_vp)]
 
 
 class PAError(RuntimeError):
@@ -51,7 +58,7 @@ _SIGNATURES = {
     "pa_decode_shared_prefix_workspace_bytes": (c_size, [c_i32] * 9),
     "pa_decode_shared_prefix": (c_i32, [c_vp, c_vp, c_vp, PoolDesc, c_vp, c_i32, c_vp, c_i32, c_i32,
                                         c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_f, c_vp, c_i32,
-                                        c_vp, c_size, c_vp]),
+                                        c_vp, c_size, c_vp, ctypes.POINTER(AuxStream)]),
     "pa_qkv_rope_write": (c_i32, [c_vp, c_i64, c_vp, c_i32, c_i32, c_vp, c_vp, c_i32, c_i32, c_f,
                                   c_vp, c_vp, c_f, c_vp, c_vp, c_vp, PoolDesc, c_vp, c_vp]),
     "pa_prefill_workspace_bytes": (c_size, [c_i32] * 8),
@@ -67,7 +74,7 @@ _SIGNATURES = {
     "pa_bm_block_refcount": (c_i32, [c_vp, c_i32]),
     "pa_prefill_chunk": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, PoolDesc,
                                  c_vp, c_i32, c_vp, c_i32, c_i32, c_f, c_vp, c_i32, c_vp,
-                                 c_size, c_vp]),
+                                 c_size, c_vp, ctypes.POINTER(AuxStream)]),
 }
 
 _lib = None
@@ -136,6 +143,54 @@ def _stream(stream) -> int:
     return s.cuda_stream
 
 
+def _on(stream):
+    """Allocations for a call made on `stream`: torch's allocator then keeps
+    a block (workspace, default output) for that stream's work, instead of
+    handing it back to the current stream while the call's kernels still use
+    it."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+class _AuxPerThread(threading.local):
+    def __init__(self):
+        self.by_device = {}
+
+
+_aux = _AuxPerThread()
+
+
+def aux_stream(device=None):
+    """This host thread's second stream and fork/join events on `device`
+    (created on first use, default priority), as the pa_aux_stream that
+    prefill_chunk and decode_shared_prefix pass by default.  One per thread,
+    so calls from several threads never share one.  Returns (stream,
+    AuxStream)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    ent = _aux.by_device.get(idx)
+    if ent is None:
+        with torch.cuda.device(idx):
+            s = torch.cuda.Stream()
+            fork, join = torch.cuda.Event(), torch.cuda.Event()  # timing disabled
+            fork.record(s)  # torch creates an event at its first record
+            join.record(s)
+        ent = (s, fork, join, AuxStream(s.cuda_stream, fork.cuda_event, join.cuda_event))
+        _aux.by_device[idx] = ent
+    return ent[0], ent[3]
+
+
+def _aux_arg(aux, device):
+    """aux: True = this thread's aux_stream(device), False/None = run on the
+    call's stream alone, or an AuxStream."""
+    if aux is True:
+        return ctypes.pointer(aux_stream(device)[1])
+    if aux is False or aux is None:
+        return None
+    if isinstance(aux, AuxStream):
+        return ctypes.pointer(aux)
+    raise TypeError("aux must be True, False, None or an AuxStream")
+
+
 def kv_write(k, v, slot_mapping, k_pool, v_pool, stream=None) -> None:
     """Scatter rows k[t], v[t] ([T, Hkv, D], token stride free) to pool row
     slot_mapping[t]; negative slots are skipped."""
@@ -165,7 +220,8 @@ def qkv_rope_write(qkv, num_q_heads, context_lens, block_tables, k_pool, v_pool,
     S = context_lens.shape[0]
     D = k_pool.shape[3]
     if q_out is None:
-        q_out = torch.empty((T, num_q_heads, D), dtype=qkv.dtype, device=qkv.device)
+        with _on(stream):
+            q_out = torch.empty((T, num_q_heads, D), dtype=qkv.dtype, device=qkv.device)
     qsl = 0 if query_start_loc is None else _i32(query_start_loc, "query_start_loc")
     qn = 0 if q_norm is None else _contig(q_norm, "q_norm")
     kn = 0 if k_norm is None else _contig(k_norm, "k_norm")
@@ -197,11 +253,19 @@ def prefill_workspace_bytes(num_seqs, num_prefill_seqs, total_query_tokens, num_
                                             max_context_len, partition_tokens)
 
 
-def _workspace(nbytes: int, workspace, device) -> tuple[int, int]:
+def _workspace(nbytes: int, workspace, device):
+    """The caller's workspace, or a new one of nbytes (None when none is
+    needed); allocate under _on(stream)."""
     if nbytes == 0:
-        return 0, 0
+        return None
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def _ws_ptr(workspace) -> tuple[int, int]:
+    if workspace is None:
+        return 0, 0
     return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
 
 
@@ -209,13 +273,15 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale
            out=None, partition_tokens=0, workspace=None, stream=None):
     """Batched decode attention, q [S, Hq, D] -> out [S, Hq, D]."""
     S, Hq, D = q.shape
-    if out is None:
-        out = torch.empty_like(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     hkv = k_pool.shape[2]
     need = decode_workspace_bytes(S, Hq, hkv, D, max_context_len, partition_tokens)
-    wp, wb = _workspace(need, workspace, q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        ws = _workspace(need, workspace, q.device)
+    wp, wb = _ws_ptr(ws)
     st = lib().pa_decode(_contig(q, "q"), _contig(k_pool, "k_pool"), _contig(v_pool, "v_pool"),
                          pool_desc(k_pool), _i32(block_tables, "block_tables"),
                          block_tables.shape[1], _i32(context_lens, "context_lens"), S,
@@ -237,13 +303,15 @@ def decode_append(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, m
             raise ValueError(f"{name} must be [S, Hkv, D] with contiguous token rows")
     if k_new.dtype != k_pool.dtype or v_new.dtype != v_pool.dtype:
         raise TypeError("k_new/v_new and pools must share an element type")
-    if out is None:
-        out = torch.empty_like(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     hkv = k_pool.shape[2]
     need = decode_workspace_bytes(S, Hq, hkv, D, max_context_len, partition_tokens)
-    wp, wb = _workspace(need, workspace, q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        ws = _workspace(need, workspace, q.device)
+    wp, wb = _ws_ptr(ws)
     st = lib().pa_decode_append(_contig(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), k_new.stride(0),
                                 v_new.stride(0), _contig(k_pool, "k_pool"), _contig(v_pool, "v_pool"),
                                 pool_desc(k_pool), _i32(block_tables, "block_tables"), block_tables.shape[1],
@@ -263,53 +331,60 @@ def decode_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, he
 
 def decode_shared_prefix(q, k_pool, v_pool, block_tables, context_lens, max_context_len, group_start,
                          prefix_lens, max_group_size, max_prefix_len, scale=None, out=None,
-                         partition_tokens=0, workspace=None, stream=None):
+                         partition_tokens=0, workspace=None, stream=None, aux=True):
     """Decode attention for groups of sequences sharing a prompt prefix:
     group g is sequences group_start[g] .. group_start[g+1]-1 (int32 device
     tensor [G+1]) sharing their first prefix_lens[g] tokens (int32 device
-    [G]).  Same result as decode() within rounding."""
+    [G]).  Same result as decode() within rounding.  aux: see _aux_arg (by
+    default the prefix phase runs on this thread's second stream)."""
     S, Hq, D = q.shape
-    if out is None:
-        out = torch.empty_like(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     hkv = k_pool.shape[2]
     ng = group_start.shape[0] - 1
     need = decode_shared_prefix_workspace_bytes(S, Hq, hkv, D, max_context_len, ng, max_group_size,
                                                 max_prefix_len, partition_tokens)
-    wp, wb = _workspace(need, workspace, q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        ws = _workspace(need, workspace, q.device)
+    wp, wb = _ws_ptr(ws)
     st = lib().pa_decode_shared_prefix(_contig(q, "q"), _contig(k_pool, "k_pool"), _contig(v_pool, "v_pool"),
                                        pool_desc(k_pool), _i32(block_tables, "block_tables"),
                                        block_tables.shape[1], _i32(context_lens, "context_lens"), S,
                                        int(max_context_len), _i32(group_start, "group_start"),
                                        _i32(prefix_lens, "prefix_lens"), ng, int(max_group_size),
                                        int(max_prefix_len), Hq, float(scale), _contig(out, "out"),
-                                       int(partition_tokens), wp, wb, _stream(stream))
+                                       int(partition_tokens), wp, wb, _stream(stream), _aux_arg(aux, q.device))
     _check(st, "pa_decode_shared_prefix")
     return out
 
 
 def prefill_chunk(q, query_start_loc, num_prefill_seqs, max_query_len, k_pool, v_pool,
                   block_tables, context_lens, max_context_len, scale=None, out=None,
-                  partition_tokens=0, workspace=None, stream=None):
-    """Causal attention for a packed mixed batch, q [T, Hq, D] -> out [T, Hq, D]."""
+                  partition_tokens=0, workspace=None, stream=None, aux=True):
+    """Causal attention for a packed mixed batch, q [T, Hq, D] -> out [T, Hq, D].
+    aux: see _aux_arg (by default the decode rows run on this thread's second
+    stream beside the matrix-core chunks)."""
     T, Hq, D = q.shape
     S = context_lens.shape[0]
-    if out is None:
-        out = torch.empty_like(q)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     hkv = k_pool.shape[2]
     need = prefill_workspace_bytes(S, num_prefill_seqs, T, Hq, hkv, D, max_context_len,
                                    partition_tokens)
-    wp, wb = _workspace(need, workspace, q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        ws = _workspace(need, workspace, q.device)
+    wp, wb = _ws_ptr(ws)
     st = lib().pa_prefill_chunk(_contig(q, "q"), _i32(query_start_loc, "query_start_loc"), T, S,
                                 int(num_prefill_seqs), int(max_query_len),
                                 _contig(k_pool, "k_pool"), _contig(v_pool, "v_pool"),
                                 pool_desc(k_pool), _i32(block_tables, "block_tables"),
                                 block_tables.shape[1], _i32(context_lens, "context_lens"),
                                 int(max_context_len), Hq, float(scale), _contig(out, "out"),
-                                int(partition_tokens), wp, wb, _stream(stream))
+                                int(partition_tokens), wp, wb, _stream(stream), _aux_arg(aux, q.device))
     _check(st, "pa_prefill_chunk")
     return out
 

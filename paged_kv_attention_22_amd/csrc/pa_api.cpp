@@ -5,7 +5,6 @@
 #include <stdint.h>
 
 #include <algorithm>
-#include <mutex>
 
 #include "pa_internal.hpp"
 
@@ -13,43 +12,43 @@ using namespace pa;
 
 namespace {
 
-// Auxiliary stream of one device: pa_prefill_chunk runs its decode rows on it
-// beside the matrix-core chunk kernel on the caller's stream, and
-// pa_decode_shared_prefix its prefix phase (chunk kernel) beside the decode
-// kernel on the caller's stream; forked from and joined back into the caller's
-// stream with the two events.
-// Created on first use, kept for the life of the process; the mutex makes the
-// record / wait / launch sequence atomic across host threads.
-struct AuxStream {
-    std::once_flag once;
-    std::mutex mu;
-    hipStream_t stream = nullptr;
-    hipEvent_t fork = nullptr;
-    hipEvent_t join = nullptr;
-    bool ok = false;
-};
-constexpr int kMaxDevices = 64;
-AuxStream g_aux[kMaxDevices];
-
-AuxStream* aux_for(hipStream_t s) {
-    int dev = 0;
+// The caller's second stream for a call that runs two kernels side by side
+// (pa_prefill_chunk: decode rows beside the matrix-core chunk kernel;
+// pa_decode_shared_prefix: the prefix phase beside the decode kernel).  NULL
+// means no second stream: the call then enqueues everything on its own
+// stream, in an order that needs no second one.  The library keeps nothing:
+// the stream and both events belong to the caller for as long as the caller
+// likes.
+int32_t check_aux(const pa_aux_stream* aux, hipStream_t s) {
+    if (aux == nullptr) return PA_OK;
+    if (aux->stream == nullptr || aux->fork_event == nullptr || aux->join_event == nullptr)
+        return PA_ERR_STREAM;
+    hipStream_t x = static_cast<hipStream_t>(aux->stream);
+    if (x == s) return PA_ERR_STREAM;
+    int dev_s = 0, dev_x = 0;
     if (s != nullptr) {
-        if (hipStreamGetDevice(s, &dev) != hipSuccess) return nullptr;
-    } else if (hipGetDevice(&dev) != hipSuccess) {
-        return nullptr;
+        if (hipStreamGetDevice(s, &dev_s) != hipSuccess) return PA_ERR_STREAM;
+    } else if (hipGetDevice(&dev_s) != hipSuccess) {
+        return PA_ERR_STREAM;
     }
-    if (dev < 0 || dev >= kMaxDevices) return nullptr;
-    AuxStream& a = g_aux[dev];
-    std::call_once(a.once, [&] {
-        int cur = 0;
-        if (hipGetDevice(&cur) != hipSuccess) return;
-        if (cur != dev && hipSetDevice(dev) != hipSuccess) return;
-        a.ok = hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking) == hipSuccess &&
-               hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) == hipSuccess &&
-               hipEventCreateWithFlags(&a.join, hipEventDisableTiming) == hipSuccess;
-        if (cur != dev) (void)hipSetDevice(cur);
-    });
-    return a.ok ? &a : nullptr;
+    if (hipStreamGetDevice(x, &dev_x) != hipSuccess || dev_x != dev_s) return PA_ERR_STREAM;
+    return PA_OK;
+}
+
+// Work enqueued on s before this point is also ordered before what is
+// enqueued on the auxiliary stream after it.
+int32_t fork_to(const pa_aux_stream& aux, hipStream_t s) {
+    hipEvent_t e = static_cast<hipEvent_t>(aux.fork_event);
+    if (hipEventRecord(e, s) != hipSuccess) return PA_ERR_LAUNCH;
+    return hipStreamWaitEvent(static_cast<hipStream_t>(aux.stream), e, 0) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+// Work enqueued on s after this point waits for what the auxiliary stream
+// holds now.
+int32_t join_from(const pa_aux_stream& aux, hipStream_t s) {
+    hipEvent_t e = static_cast<hipEvent_t>(aux.join_event);
+    if (hipEventRecord(e, static_cast<hipStream_t>(aux.stream)) != hipSuccess) return PA_ERR_LAUNCH;
+    return hipStreamWaitEvent(s, e, 0) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 int elem_size(int32_t dtype) {
@@ -161,6 +160,10 @@ int32_t check_partition(int32_t requested) {
 // (no query_start_loc) may get a longest-first order in front of the partials.
 int32_t prepare_rows(RowsArgs& a, int64_t items, int32_t part, void* workspace,
                      size_t workspace_bytes, int32_t extra_slots = 0) {
+    // Every context empty: one pass, which writes the zero rows (a split
+    // launch would have no partition to launch).  A shared prefix (extra
+    // slots) needs a context of at least 16 tokens, so it never gets here.
+    if (a.max_context_len == 0) part = -1;
     a.num_items = (int32_t)items;
     a.part_tokens = part;
     a.nparts = part > 0 ? ceil_div(a.max_context_len, part) + extra_slots : 1;
@@ -257,6 +260,7 @@ const char* pa_status_str(int32_t status) {
         case PA_ERR_LAUNCH: return "kernel launch failed";
         case PA_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
         case PA_ERR_CAPACITY: return "not enough free blocks";
+        case PA_ERR_STREAM: return "auxiliary stream or its events missing, equal to the call's stream, or on another device";
         default: return "unknown status";
     }
 }
@@ -448,7 +452,7 @@ int32_t pa_decode_shared_prefix(const void* q, const void* k_pool, const void* v
                                 const int32_t* group_start, const int32_t* prefix_lens, int32_t num_groups,
                                 int32_t max_group_size, int32_t max_prefix_len, int32_t num_q_heads,
                                 float scale, void* out, int32_t partition_tokens, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+                                size_t workspace_bytes, void* stream, const pa_aux_stream* aux) {
     if (int32_t st = check_pool(pool)) return st;
     if (int32_t st = check_heads(num_q_heads, pool.num_kv_heads)) return st;
     if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
@@ -464,6 +468,7 @@ int32_t pa_decode_shared_prefix(const void* q, const void* k_pool, const void* v
     if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out || !group_start || !prefix_lens)
         return PA_ERR_NULL;
     if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool)) return PA_ERR_ALIGN;
+    if (int32_t st = check_aux(aux, static_cast<hipStream_t>(stream))) return st;
 
     const int32_t prefix_cap = (int32_t)std::min<int64_t>(max_prefix_len, (int64_t)max_blocks_per_seq * pool.block_size);
     const CascadePlan cp = cascade_plan(num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim, max_context_len,
@@ -528,23 +533,20 @@ int32_t pa_decode_shared_prefix(const void* q, const void* k_pool, const void* v
         c.num_items = num_seqs;
         c.prefer_large = 1;
         // The prefix phase (matrix cores, LDS, cache-resident keys) runs on the
-        // auxiliary stream beside the decode kernel (HBM); they write disjoint
-        // partial slots, and the merge waits for both.
-        AuxStream* ax = aux_for(s);
-        if (ax == nullptr) {
+        // caller's auxiliary stream beside the decode kernel (HBM); they write
+        // disjoint partial slots, and the merge waits for both.  Without an
+        // auxiliary stream the two run one after the other on `stream`.
+        if (aux == nullptr) {
             if (int32_t st = launch_chunks(c, s)) return st;
             return run_rows(a, s);
         }
-        std::lock_guard<std::mutex> lock(ax->mu);
-        if (hipEventRecord(ax->fork, s) != hipSuccess || hipStreamWaitEvent(ax->stream, ax->fork, 0) != hipSuccess)
-            return PA_ERR_LAUNCH;
+        if (int32_t st = fork_to(*aux, s)) return st;
         // decode kernel first: its workgroups take one slot per compute unit,
         // the prefix workgroups fill in beside them
         a.defer_merge = 1;
         if (int32_t st = run_rows(a, s)) return st;
-        if (int32_t st = launch_chunks(c, ax->stream)) return st;
-        if (hipEventRecord(ax->join, ax->stream) != hipSuccess) return PA_ERR_LAUNCH;
-        if (hipStreamWaitEvent(s, ax->join, 0) != hipSuccess) return PA_ERR_LAUNCH;
+        if (int32_t st = launch_chunks(c, static_cast<hipStream_t>(aux->stream))) return st;
+        if (int32_t st = join_from(*aux, s)) return st;
         return launch_merge(a, s);
     }
 }
@@ -586,7 +588,7 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
                          const int32_t* block_tables, int32_t max_blocks_per_seq,
                          const int32_t* context_lens, int32_t max_context_len, int32_t num_q_heads,
                          float scale, void* out, int32_t partition_tokens, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         size_t workspace_bytes, void* stream, const pa_aux_stream* aux) {
     if (int32_t st = check_pool(pool)) return st;
     if (int32_t st = check_heads(num_q_heads, pool.num_kv_heads)) return st;
     if (num_seqs < 0 || num_prefill_seqs < 0 || num_prefill_seqs > num_seqs ||
@@ -604,6 +606,7 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
     if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool))
         return PA_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int32_t st = check_aux(aux, s)) return st;
     const int32_t group = num_q_heads / pool.num_kv_heads;
 
     RowsArgs base = {};
@@ -687,8 +690,9 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
         c.alone = num_decode == 0;  // nothing runs beside the chunk kernel
     }
     // The chunks (matrix cores, LDS) and the decode rows (HBM) use different
-    // parts of the chip and run concurrently: the chunk kernel on the caller's
-    // stream, the vector path on the auxiliary stream.  They read the same
+    // parts of the chip and run concurrently when the caller passes an
+    // auxiliary stream: the chunk kernel on the caller's stream, the vector
+    // path on the auxiliary stream.  They read the same
     // pools and write disjoint rows of out; the two vector-path launches use
     // disjoint parts of the workspace.  The order matters: a chunk workgroup
     // (4 waves of 256 registers, 96 KiB of LDS) fits on a compute unit beside
@@ -707,16 +711,13 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
     // launch holding both kinds of workgroup avoids the waits but measured
     // slower: the decode loop compiled inside the larger kernel ran 12%
     // slower.)
-    AuxStream* ax = (mfma && num_decode > 0) ? aux_for(s) : nullptr;
-    if (ax != nullptr) {
-        std::lock_guard<std::mutex> lock(ax->mu);
-        if (hipEventRecord(ax->fork, s) != hipSuccess || hipStreamWaitEvent(ax->stream, ax->fork, 0) != hipSuccess)
-            return PA_ERR_LAUNCH;
+    if (aux != nullptr && mfma && num_decode > 0) {
+        hipStream_t x = static_cast<hipStream_t>(aux->stream);
+        if (int32_t st = fork_to(*aux, s)) return st;
         if (int32_t st = launch_chunks(c, s)) return st;
-        if (int32_t st = run_rows(pre, ax->stream)) return st;  // small chunks, if any
-        if (int32_t st = run_rows(dec, ax->stream)) return st;
-        if (hipEventRecord(ax->join, ax->stream) != hipSuccess) return PA_ERR_LAUNCH;
-        return hipStreamWaitEvent(s, ax->join, 0) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+        if (int32_t st = run_rows(pre, x)) return st;  // small chunks, if any
+        if (int32_t st = run_rows(dec, x)) return st;
+        return join_from(*aux, s);
     }
     if (mfma)
         if (int32_t st = launch_chunks(c, s)) return st;

@@ -150,8 +150,9 @@ constexpr int kRankKeep = 8;               // items per thread
 constexpr int kRankLdsInts = kRankBuckets + kMaxWaves + 2;
 __device__ __forceinline__ int rank_select(const RowsArgs& a, int z, int* rank_lds) {
     int* const hist = rank_lds;                    // [kRankBuckets]
-    int* const tmp = rank_lds + kRankBuckets;      // [waves]
-    int* const pick = tmp + kWaves;                // [2]
+    int* const tmp = rank_lds + kRankBuckets;      // [kMaxWaves]: one per wave of any decode workgroup
+    int* const pick = tmp + kMaxWaves;             // [2], past every wave's tmp entry
+    static_assert(kRankBuckets + kMaxWaves + 2 <= kRankLdsInts, "pick lies past tmp[kMaxWaves - 1]");
     const int t = threadIdx.x;
     const bool owner = t < kRankBuckets;  // holds a bucket and items
     const int n = a.num_items;
@@ -633,6 +634,7 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
     constexpr int VT = 32 * VROW;             // one wave's V tile
     constexpr float kLazy = 8.0f;
     static_assert(G <= 16, "group fits the 16 columns of one MFMA tile");
+    static_assert(W <= kMaxWaves, "the ranking's LDS holds one partial sum per wave");
     // LDS: [V tiles W x VT][acc W x G x D][m][l][ranking]
     unsigned char* const s_v = lds;
     unsigned char* const rl = lds + W * VT;

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(pa):
 
 
 def test_status_strings(pa):
-    for code in range(9):
+    for code in range(10):
         assert pa.status_str(code) and pa.status_str(code) != "unknown status"
     assert pa.status_str(99) == "unknown status"
 
@@ -124,11 +124,12 @@ def test_prefill_validation(pa):
 
     def call(**kw):
         a = dict(q=FAKE, qsl=FAKE, T=10, S=3, npre=1, maxq=8, pool=p, maxb=4, maxL=64, Hq=2,
-                 part=-1, ws=0, wsb=0)
+                 part=-1, ws=0, wsb=0, stream=0, aux=None)
         a.update(kw)
+        aux = None if a["aux"] is None else ctypes.pointer(a["aux"])
         return L.pa_prefill_chunk(a["q"], a["qsl"], a["T"], a["S"], a["npre"], a["maxq"], FAKE,
                                   FAKE, a["pool"], FAKE, a["maxb"], FAKE, a["maxL"], a["Hq"], 0.1,
-                                  FAKE, a["part"], a["ws"], a["wsb"], 0)
+                                  FAKE, a["part"], a["ws"], a["wsb"], a["stream"], aux)
     assert call(qsl=0) == 1
     assert call(npre=4) == 2            # more prefill seqs than seqs
     assert call(T=1) == 2               # fewer rows than decode seqs
@@ -137,6 +138,13 @@ def test_prefill_validation(pa):
     assert call(pool=pool(bs=8)) == 2   # max_context_len 64 > 4 blocks of 8
     assert call(pool=pool(bs=24)) == 4
     assert call(T=0, S=0, npre=0) == 0    # empty batch: no-op
+    # a caller-owned second stream must be complete and differ from the call's stream
+    A = pa.AuxStream
+    assert call(aux=A(0, FAKE, FAKE)) == 9
+    assert call(aux=A(FAKE, 0, FAKE)) == 9
+    assert call(aux=A(FAKE, FAKE, 0)) == 9
+    assert call(stream=FAKE, aux=A(FAKE, FAKE + 16, FAKE + 32)) == 9
+    assert call(pool=pool(bs=24), aux=A(0, 0, 0)) == 4   # argument checks come first
 
 
 def test_partition_choice_and_workspace(pa):
@@ -195,11 +203,12 @@ def test_shared_prefix_validation(pa):
 
     def call(**kw):
         a = dict(q=FAKE, S=4, maxL=64, gs=FAKE, pl=FAKE, ng=2, mg=3, mp=32, pool=pool(hkv=1, d=64),
-                 Hq=2, ws=FAKE, wsb=1 << 20, part=0)
+                 Hq=2, ws=FAKE, wsb=1 << 20, part=0, stream=0, aux=None)
         a.update(kw)
+        aux = None if a["aux"] is None else ctypes.pointer(a["aux"])
         return L.pa_decode_shared_prefix(a["q"], FAKE, FAKE, a["pool"], FAKE, 4, FAKE, a["S"], a["maxL"],
                                          a["gs"], a["pl"], a["ng"], a["mg"], a["mp"], a["Hq"], 0.125, FAKE,
-                                         a["part"], a["ws"], a["wsb"], 0)
+                                         a["part"], a["ws"], a["wsb"], a["stream"], aux)
     assert call(S=0, q=0) == 0                   # empty batch: no-op
     assert call(gs=0) == 1 and call(pl=0) == 1
     assert call(ng=0) == 2                       # every sequence needs a group
@@ -210,6 +219,9 @@ def test_shared_prefix_validation(pa):
     assert call(pool=pool(hkv=1, d=64, dtype=0)) == 4   # fp32: no matrix-core path
     assert call(part=24) == 2
     assert call(wsb=16) == 5                     # workspace too small
+    A = pa.AuxStream
+    assert call(aux=A(0, FAKE, FAKE)) == 9       # incomplete second stream
+    assert call(stream=FAKE, aux=A(FAKE, FAKE + 16, FAKE + 32)) == 9   # the call's own stream
     need = pa.decode_shared_prefix_workspace_bytes(4, 2, 1, 64, 64, 2, 3, 32, 0)
     # partials: the prefix's key parts plus the rest's partitions, (D + 2) fp32 each
     assert need > 0 and need % (4 * 2 * 66 * 4) == 0
@@ -242,3 +254,40 @@ def test_qkv_rope_write_validation(pa):
     assert call(pool=pool(hkv=2, d=64, bs=64)) == 4
     assert call(T=0, pool=pool(hkv=2, d=64, bs=8)) == 0
     assert call(pool=pool(hkv=2, d=64, dtype=5)) == 3
+
+
+# Toolchain-owned writable symbols: the HIP runtime's code-object registration,
+# the C runtime's init/fini bookkeeping and the dynamic linker's tables.
+_TOOLCHAIN_DATA = re.compile(r"^(__hip_|__do_|__dso_handle$|_DYNAMIC$|_GLOBAL_OFFSET_TABLE_$|DW\.ref\.|__init$|__fini$"
+                             r"|__bss_start$|_edata$|_end$|__TMC_END__$)")
+
+
+def test_library_keeps_no_mutable_state(pa):
+    """The library keeps no handle, stream, event, lock or other state between
+    calls: its writable data holds only what the toolchain puts there, and the
+    host-side handles of its kernels (one per __global__ function, demangled to
+    a function signature)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-C", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    own = []
+    for line in out.splitlines():
+        parts = line.split(" ", 2)
+        if len(parts) < 3 or parts[1] not in "bBdD":
+            continue
+        name = parts[2]
+        if _TOOLCHAIN_DATA.match(name):
+            continue
+        # a kernel's host-side launch handle: a function, demangled, or (where
+        # nm cannot demangle _Float16 template arguments) a mangled template
+        # function returning void, whose parameter types follow the name
+        plain = name.replace("(anonymous namespace)", "")
+        if plain.endswith(")") and "_kernel" in plain.split("(")[0]:
+            continue
+        if re.match(r"^_ZN\w*_kernelI\w*EEv\w+$", name):
+            continue
+        own.append(name)
+    assert not own, f"libpa.so holds writable state of its own: {own}"

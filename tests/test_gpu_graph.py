@@ -151,8 +151,9 @@ def test_large_batch_plan(pa):
 
 def test_mixed_step_graph_replays(pa):
     """A mixed step (KV write + pa_prefill_chunk, whose decode rows run on the
-    library's auxiliary stream beside the MFMA chunks) captured in a graph: the fork/join is captured
-    too, and replays with new q values match the oracle."""
+    caller's second stream, the binding's per-thread one, beside the MFMA
+    chunks) captured in a graph: the fork/join is captured too, and replays
+    with new q values match the oracle."""
     from workloads import mixed_prefill
     b = mixed_prefill(seed=73, chunks=2, chunk_len=48, prior_hi=120, n_decode=20,
                       dec_lo=20, dec_hi=400)
@@ -196,8 +197,8 @@ def test_mixed_step_graph_replays(pa):
 
 def test_shared_prefix_graph_replays(pa):
     """pa_decode_shared_prefix (decode kernel on the caller's stream, the
-    prefix tiles on the library's auxiliary stream, then the merge) captured
-    in a graph: replays with new q values match the oracle."""
+    prefix tiles on the caller's second stream, then the merge) captured in a
+    graph: replays with new q values match the oracle."""
     from workloads import long_context
     b = long_context(seed=74, batch=6, ctx=1200, shared_blocks=30)
     kp, vp = oracle.kv_write(b.k_pool, b.v_pool, b.new_k, b.new_v, b.slot_mapping)

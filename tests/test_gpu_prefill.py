@@ -71,12 +71,12 @@ def prepared(name):
     return _cache[name]
 
 
-def run(pa, d, b, part=0, write=True):
+def run(pa, d, b, part=0, write=True, aux=True):
     if write:
         pa.kv_write(d.new_k, d.new_v, d.slot_mapping, d.k_pool, d.v_pool)
     o = pa.prefill_chunk(d.q, d.query_start_loc, b.num_prefill_seqs, b.max_query_len, d.k_pool,
                          d.v_pool, d.block_tables, d.context_lens, b.max_context_len,
-                         scale=b.scale, partition_tokens=part)
+                         scale=b.scale, partition_tokens=part, aux=aux)
     torch.cuda.synchronize()
     return o
 
@@ -85,12 +85,13 @@ def run(pa, d, b, part=0, write=True):
 def test_prefill_matches_oracle(pa, name):
     b, ref = prepared(name)
     d = DeviceBatch(b)
-    for i, part in enumerate([0, -1, 64]):
+    # (partition, second stream): the library's choice also without a second
+    # stream (every kernel on the call's stream, the chunks first)
+    for i, (part, aux) in enumerate([(0, True), (0, False), (-1, True), (64, True)]):
         print(f"[prefill] {name} S={b.num_seqs} prefill={b.num_prefill_seqs} "
-              f"T={b.total_query_tokens} part={part}", flush=True)
-        out = run(pa, d, b, part, write=(i == 0))
-        max_abs, rel = assert_close(f64(out), ref, b.dtype, f"{name} part={part}")
-        print(f"    max-abs {max_abs:.3e} rel-L2 {rel:.3e}", flush=True)
+              f"T={b.total_query_tokens} part={part} aux={aux}", flush=True)
+        out = run(pa, d, b, part, write=(i == 0), aux=aux)
+        assert_close(f64(out), ref, b.dtype, f"{name} part={part} aux={aux}")
 
 
 def test_chunk_split_invariance(pa):

@@ -45,15 +45,18 @@ def run_case(pa, b, tables, group_start, prefixes, parts=(-1, 0, 64)):
     d_t, lens = dev(tables), dev(b.context_lens)
     gs, pl = dev(group_start), dev(np.asarray(prefixes, np.int32))
     sizes = np.diff(group_start)
-    for part in parts:
-        print(f"[shared prefix] {b.name} S={b.num_seqs} groups={len(prefixes)} prefixes={list(prefixes)[:6]} "
-              f"block={b.k_pool.shape[1]} part={part}", flush=True)
-        out = pa.decode_shared_prefix(q, d_k, d_v, d_t, lens, b.max_context_len, gs, pl, int(sizes.max()),
-                                      int(max(prefixes)), scale=b.scale, partition_tokens=part)
-        plain = pa.decode(q, d_k, d_v, d_t, lens, b.max_context_len, scale=b.scale, partition_tokens=part)
-        torch.cuda.synchronize()
-        assert_close(f64(out), ref, b.dtype, f"{b.name} part={part} vs oracle")
-        assert_close(f64(out), f64(plain), b.dtype, f"{b.name} part={part} vs pa_decode")
+    for i, part in enumerate(parts):
+        # the first partition choice also runs without a second stream (the
+        # prefix phase first, on the call's stream)
+        for aux in ((True, False) if i == 0 else (True,)):
+            print(f"[shared prefix] {b.name} S={b.num_seqs} groups={len(prefixes)} prefixes={list(prefixes)[:6]} "
+                  f"block={b.k_pool.shape[1]} part={part} aux={aux}", flush=True)
+            out = pa.decode_shared_prefix(q, d_k, d_v, d_t, lens, b.max_context_len, gs, pl, int(sizes.max()),
+                                          int(max(prefixes)), scale=b.scale, partition_tokens=part, aux=aux)
+            plain = pa.decode(q, d_k, d_v, d_t, lens, b.max_context_len, scale=b.scale, partition_tokens=part)
+            torch.cuda.synchronize()
+            assert_close(f64(out), ref, b.dtype, f"{b.name} part={part} aux={aux} vs oracle")
+            assert_close(f64(out), f64(plain), b.dtype, f"{b.name} part={part} aux={aux} vs pa_decode")
 
 
 def test_one_group_long_prefix(pa):
@@ -61,6 +64,35 @@ def test_one_group_long_prefix(pa):
     b = long_context(batch=5, ctx=1500, shared_blocks=40)
     S = b.num_seqs
     run_case(pa, b, b.block_tables, np.array([0, S], np.int32), [40 * 16], parts=(-1, 0, 64, 256))
+
+
+def test_long_context_full_size(pa):
+    """The full long-context shape the benchmark times: 64 sequences of
+    8,192 tokens, one group sharing a 4,096-token prefix, 28/4 heads (G = 7).
+    Its plan: 8 key parts of 512 for the prefix phase, four 128-row tiles per
+    kv head; checked for one pass, the library's choice and 64- and 512-token
+    partitions of the rest."""
+    b = long_context()
+    S = b.num_seqs
+    assert b.shared_prefix_tokens == 4096 and S == 64 and b.max_context_len == 8192
+    run_case(pa, b, b.block_tables, np.array([0, S], np.int32), [b.shared_prefix_tokens],
+             parts=(-1, 0, 64, 512))
+
+
+def test_empty_contexts_with_partitions(pa):
+    """Every context empty (max_context_len 0) with an explicit partition
+    size: zeros, not a launch error."""
+    b = make_batch(95, name="empty", dtype="bf16", num_q_heads=28, num_kv_heads=4, head_dim=128,
+                   draw_lens=lambda rng: np.zeros(3, np.int64), draw_query_lens=lambda rng, L: L,
+                   pool_blocks=4)
+    q = dev(np.ones((3, 28, 128), np.uint16) * np.uint16(0x3F80))
+    d_k, d_v, d_t, lens = dev(b.k_pool), dev(b.v_pool), dev(b.block_tables), dev(b.context_lens)
+    gs, pl = dev(np.array([0, 3], np.int32)), dev(np.array([0], np.int32))
+    for part in (16, 64, 0, -1):
+        out = torch.full_like(q, 5.0)
+        pa.decode_shared_prefix(q, d_k, d_v, d_t, lens, 0, gs, pl, 3, 0, out=out, partition_tokens=part)
+        torch.cuda.synchronize()
+        assert not out.float().abs().sum().item(), part
 
 
 @pytest.mark.parametrize("bs", [8, 16, 32])

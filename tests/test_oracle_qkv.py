@@ -137,6 +137,29 @@ def test_to_stored_rounds_to_nearest_even():
     assert got.tolist() == [0x3F80, 0x3F80, 0x3F81, 0x3F82, 0xC020, 0x0000]
 
 
+def test_to_stored_f16_rounds_to_nearest_even():
+    # fp16 keeps 10 fraction bits (one unit in the last place at 1.0 is 2^-10),
+    # 5 exponent bits (largest finite 65504, smallest normal 2^-14) and
+    # subnormals down to 2^-24; each expected pattern is worked out by hand.
+    x = np.array([
+        1.0 + 2 ** -11,             # half a unit: tie, to the even 1.0          -> 0x3C00
+        1.0 + 3 * 2 ** -11,         # tie between 1+2^-10 (odd) and 1+2^-9: up   -> 0x3C02
+        1.0 + 2 ** -11 + 2 ** -20,  # just past half a unit: up                  -> 0x3C01
+        65504.0,                    # largest finite                             -> 0x7BFF
+        65519.0,                    # below the midpoint 65520: down             -> 0x7BFF
+        65520.0,                    # midpoint, 65504's last bit odd: to inf     -> 0x7C00
+        2.0 ** -14,                 # smallest normal                            -> 0x0400
+        2.0 ** -24,                 # smallest subnormal                         -> 0x0001
+        2.0 ** -25,                 # half of it: tie, to the even 0             -> 0x0000
+        3 * 2.0 ** -25,             # 1.5 subnormal units: tie, to the even 2    -> 0x0002
+        -2.5,                       # sign, exponent 1, fraction 0.25            -> 0xC100
+        0.0,
+    ], np.float64)
+    got = oracle.to_stored(x, "f16").view(np.uint16)
+    assert got.tolist() == [0x3C00, 0x3C02, 0x3C01, 0x7BFF, 0x7BFF, 0x7C00, 0x0400, 0x0001, 0x0000,
+                            0x0002, 0xC100, 0x0000]
+
+
 # --- planted mistakes --------------------------------------------------------
 
 def rope_interleaved(x, positions, theta):
