@@ -74,8 +74,10 @@ typedef enum {
     PA_ERR_LAUNCH = 6,      /* the HIP runtime rejected a launch */
     PA_ERR_ALIGN = 7,       /* a pointer or stride breaks 16-byte alignment */
     PA_ERR_CAPACITY = 8,    /* block manager: not enough free blocks (nothing changed) */
-    PA_ERR_STREAM = 9       /* pa_aux_stream incomplete, equal to the call's stream,
+    PA_ERR_STREAM = 9,      /* pa_aux_stream incomplete, equal to the call's stream,
                                or on another device */
+    PA_ERR_SCRATCH = 10     /* pa_decode_noalloc: the call needs more scratch than the
+                               library's fixed per-device array holds */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
@@ -230,6 +232,31 @@ int32_t pa_decode(const void* q, const void* k_pool, const void* v_pool,
                   int32_t max_context_len, int32_t num_q_heads, float scale,
                   void* out, int32_t partition_tokens,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Arguments, results and errors as pa_decode (same
+ * kernels, bit-identical output), without the workspace: what pa_decode keeps
+ * in its workspace (the longest-first order of batches over 2048 sequences,
+ * split-context partials) goes to a fixed 32 MiB array in device memory that
+ * the library holds for each device it runs on until the process ends.
+ * PA_ERR_SCRATCH, with nothing enqueued, when the call needs more than that
+ * (pa_decode_workspace_bytes > 32 MiB for the same arguments).  Nothing in the
+ * array needs clearing between calls (every byte a call reads, it first
+ * writes).  All calls on one device share its array: calls that overlap on one
+ * device (two host threads, two streams without an ordering between them)
+ * race and give unspecified values; calls ordered on one stream are safe.  The
+ * first call on a device that needs scratch looks the array's address up
+ * (hipGetSymbolAddress, with that device current): make that first call
+ * outside graph capture.
+ */
+int32_t pa_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                          pa_pool_desc pool,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t num_seqs,
+                          int32_t max_context_len, int32_t num_q_heads, float scale,
+                          void* out, int32_t partition_tokens, void* stream);
 
 /*
  * pa_decode_append -- a decode step with the step's KV-cache write fused into

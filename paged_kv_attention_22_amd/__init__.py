@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 BLOCK_SIZE = 16
 
 PA_OK, PA_F32, PA_BF16, PA_F16 = 0, 0, 1, 2
-PA_ERR_SHAPE, PA_ERR_WORKSPACE, PA_ERR_CAPACITY, PA_ERR_STREAM = 2, 5, 8, 9
+PA_ERR_SHAPE, PA_ERR_WORKSPACE, PA_ERR_CAPACITY, PA_ERR_STREAM, PA_ERR_SCRATCH = 2, 5, 8, 9, 10
 
 c_i32, c_i64, c_size, c_vp, c_f = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
                                   ctypes.c_void_p, ctypes.c_float)
@@ -53,6 +53,8 @@ _SIGNATURES = {
     "pa_decode_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (c_i32, [c_vp, c_vp, c_vp, PoolDesc, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
                           c_f, c_vp, c_i32, c_vp, c_size, c_vp]),
+    "pa_decode_noalloc": (c_i32, [c_vp, c_vp, c_vp, PoolDesc, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
+                                  c_f, c_vp, c_i32, c_vp]),
     "pa_decode_append": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, PoolDesc, c_vp, c_i32, c_vp,
                                  c_i32, c_i32, c_i32, c_f, c_vp, c_i32, c_vp, c_size, c_vp]),
     "pa_decode_shared_prefix_workspace_bytes": (c_size, [c_i32] * 9),
@@ -288,6 +290,25 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale
                          int(max_context_len), Hq, float(scale), _contig(out, "out"),
                          int(partition_tokens), wp, wb, _stream(stream))
     _check(st, "pa_decode")
+    return out
+
+
+def decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale=None,
+                   out=None, partition_tokens=0, stream=None):
+    """decode() through pa_decode_noalloc: the library's per-device scratch
+    array instead of a workspace; `out` must be given by a caller that
+    cannot allocate."""
+    S, Hq, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        with _on(stream):
+            out = torch.empty_like(q)
+    st = lib().pa_decode_noalloc(_contig(q, "q"), _contig(k_pool, "k_pool"), _contig(v_pool, "v_pool"),
+                                 pool_desc(k_pool), _i32(block_tables, "block_tables"), block_tables.shape[1],
+                                 _i32(context_lens, "context_lens"), S, int(max_context_len), Hq, float(scale),
+                                 _contig(out, "out"), int(partition_tokens), _stream(stream))
+    _check(st, "pa_decode_noalloc")
     return out
 
 

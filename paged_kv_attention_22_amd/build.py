@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build", "libpa")
 LIB = os.path.join(PKG, "libpa.so")
 
 SOURCES = ["kv_write.hip", "qkv_write.hip", "attn_rows.hip", "attn_chunks.hip", "pa_api.cpp",
-           "block_manager.cpp"]
+           "noalloc.hip", "block_manager.cpp"]
 ARCH = "gfx950"
 
 

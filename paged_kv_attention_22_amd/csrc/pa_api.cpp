@@ -198,12 +198,12 @@ int32_t run_rows(const RowsArgs& a, hipStream_t s) {
     return launch_rows(a, s);
 }
 
-// pa_decode, and pa_decode_append when k_new is set (validated by the caller).
-int32_t decode_impl(const void* q, const void* k_new, const void* v_new, int64_t k_new_stride,
-                    int64_t v_new_stride, const void* k_pool, const void* v_pool, pa_pool_desc pool,
-                    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-                    int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads, float scale, void* out,
-                    int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+}  // namespace
+
+int32_t pa::check_decode(const void* q, const void* k_pool, const void* v_pool, pa_pool_desc pool,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                         int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads, const void* out,
+                         int32_t partition_tokens) {
     if (int32_t st = check_pool(pool)) return st;
     if (int32_t st = check_heads(num_q_heads, pool.num_kv_heads)) return st;
     if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
@@ -214,6 +214,19 @@ int32_t decode_impl(const void* q, const void* k_new, const void* v_new, int64_t
     if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return PA_ERR_NULL;
     if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool))
         return PA_ERR_ALIGN;
+    return PA_OK;
+}
+
+// pa_decode, and pa_decode_append when k_new is set (validated by the caller).
+int32_t pa::decode_impl(const void* q, const void* k_new, const void* v_new, int64_t k_new_stride,
+                    int64_t v_new_stride, const void* k_pool, const void* v_pool, pa_pool_desc pool,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads, float scale, void* out,
+                    int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+    if (int32_t st = check_decode(q, k_pool, v_pool, pool, block_tables, max_blocks_per_seq, context_lens,
+                                  num_seqs, max_context_len, num_q_heads, out, partition_tokens))
+        return st;
+    if (num_seqs == 0) return PA_OK;
 
     RowsArgs a = {};
     a.q = q;
@@ -245,8 +258,6 @@ int32_t decode_impl(const void* q, const void* k_new, const void* v_new, int64_t
     return run_rows(a, static_cast<hipStream_t>(stream));
 }
 
-}  // namespace
-
 extern "C" {
 
 const char* pa_status_str(int32_t status) {
@@ -260,6 +271,7 @@ const char* pa_status_str(int32_t status) {
         case PA_ERR_LAUNCH: return "kernel launch failed";
         case PA_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
         case PA_ERR_CAPACITY: return "not enough free blocks";
+        case PA_ERR_SCRATCH: return "needs more scratch than the library's per-device array holds (32 MiB)";
         case PA_ERR_STREAM: return "auxiliary stream or its events missing, equal to the call's stream, or on another device";
         default: return "unknown status";
     }

@@ -198,4 +198,19 @@ struct ChunkArgs {
 int32_t launch_chunks(const ChunkArgs& a, hipStream_t stream);
 bool chunks_supported(int32_t dtype, int32_t head_dim, int32_t group);
 
+// pa_decode's host-side argument checks (PA_OK for a valid call, including an
+// empty batch).
+int32_t check_decode(const void* q, const void* k_pool, const void* v_pool, pa_pool_desc pool,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads, const void* out,
+                     int32_t partition_tokens);
+
+// pa_decode (k_new == NULL) and pa_decode_append: validation, path choice and
+// launch, with the workspace the caller provides.
+int32_t decode_impl(const void* q, const void* k_new, const void* v_new, int64_t k_new_stride,
+                    int64_t v_new_stride, const void* k_pool, const void* v_pool, pa_pool_desc pool,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads, float scale, void* out,
+                    int32_t partition_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
 }  // namespace pa

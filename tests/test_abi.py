@@ -262,11 +262,18 @@ _TOOLCHAIN_DATA = re.compile(r"^(__hip_|__do_|__dso_handle$|_DYNAMIC$|_GLOBAL_OF
                              r"|__bss_start$|_edata$|_end$|__TMC_END__$)")
 
 
+# pa_decode_noalloc's state, the one exception, kept for callers that cannot
+# allocate: the host-side stand-in of its per-device scratch array, the array's
+# device address per device, and the once-flags of that lookup.
+_NOALLOC_STATE = {"scratch", "(anonymous namespace)::scratch_addr", "(anonymous namespace)::scratch_once"}
+
+
 def test_library_keeps_no_mutable_state(pa):
     """The library keeps no handle, stream, event, lock or other state between
-    calls: its writable data holds only what the toolchain puts there, and the
+    calls: its writable data holds only what the toolchain puts there, the
     host-side handles of its kernels (one per __global__ function, demangled to
-    a function signature)."""
+    a function signature), and pa_decode_noalloc's scratch array with its
+    per-device address table."""
     import shutil
     import subprocess
     nm = shutil.which("nm")
@@ -279,7 +286,7 @@ def test_library_keeps_no_mutable_state(pa):
         if len(parts) < 3 or parts[1] not in "bBdD":
             continue
         name = parts[2]
-        if _TOOLCHAIN_DATA.match(name):
+        if _TOOLCHAIN_DATA.match(name) or name in _NOALLOC_STATE:
             continue
         # a kernel's host-side launch handle: a function, demangled, or (where
         # nm cannot demangle _Float16 template arguments) a mangled template
@@ -291,3 +298,24 @@ def test_library_keeps_no_mutable_state(pa):
             continue
         own.append(name)
     assert not own, f"libpa.so holds writable state of its own: {own}"
+
+
+def test_decode_noalloc_validation(pa):
+    """pa_decode_noalloc: pa_decode's checks, and PA_ERR_SCRATCH (nothing
+    enqueued) when the call needs more scratch than the fixed per-device array
+    holds; none of these calls reaches the GPU."""
+    L = pa.lib()
+
+    def call(**kw):
+        a = dict(q=FAKE, pool=pool(nb=40000, hkv=4, d=128), maxb=512, S=64, maxL=8192, Hq=28, part=16)
+        a.update(kw)
+        return L.pa_decode_noalloc(a["q"], FAKE, FAKE, a["pool"], FAKE, a["maxb"], FAKE, a["S"], a["maxL"],
+                                   a["Hq"], 0.0884, FAKE, a["part"], 0)
+    # 64 rows x 28 heads x 512 partitions x (128 + 2) fp32 = 477 MB > 32 MiB
+    assert call() == 10
+    assert pa.decode_workspace_bytes(64, 28, 4, 128, 8192, 16) > 32 << 20
+    assert call(q=0, part=-1) == 1          # pa_decode's own checks
+    assert call(part=24) == 2
+    assert call(pool=pool(nb=40000, bs=12, hkv=4, d=128)) == 4
+    assert call(S=0, q=0) == 0              # empty batch: no-op
+    assert pa.status_str(10) != "unknown status"
