@@ -401,12 +401,49 @@ def copy_reference(steps: int) -> dict:
             "gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def cpu_baseline(b, min_seconds: float = 10.0) -> dict:
-    """The fp64 oracle on the same step (KV write + decode), one thread,
-    repeated over the whole batch until at least min_seconds have passed."""
+# What the oracle workers read: the batch and the pools after the step's KV
+# write (set before the pool forks, so each worker sees them without a copy).
+_ORACLE_INPUT = None
+
+
+def _oracle_part(seqs):
+    """Worker of the all-cores oracle leg: decode of the given sequences over
+    the written pools (the oracle as it stands, one BLAS thread per worker)."""
     from threadpoolctl import threadpool_limits
 
     import oracle
+    b, kp, vp = _ORACLE_INPUT
+    with threadpool_limits(1):
+        oracle.decode(b.q[seqs], kp, vp, b.block_tables[seqs], b.context_lens[seqs], b.scale, b.dtype)
+    return len(seqs)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(b, min_seconds: float = 8.0) -> dict:
+    """The fp64 oracle on the same step (KV write + decode of every sequence),
+    timed on the host in two legs: one core (one BLAS thread), and every core
+    this process may run on (the KV write in this process, then the decode on
+    a pool of that many worker processes with the sequences dealt round-robin
+    to them).  Each leg repeats whole passes over the batch until at least
+    min_seconds have passed.  Runs before the GPU is touched, so the pool forks
+    a process with no GPU state."""
+    import multiprocessing
+
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    global _ORACLE_INPUT
+    nbytes = decode_bytes(b) + kv_write_bytes(b)
     passes, t0 = 0, time.perf_counter()
     with threadpool_limits(1):
         while True:
@@ -415,12 +452,59 @@ def cpu_baseline(b, min_seconds: float = 10.0) -> dict:
             passes += 1
             if time.perf_counter() - t0 >= min_seconds:
                 break
-    dt = (time.perf_counter() - t0) / passes
-    gbs = (decode_bytes(b) + kv_write_bytes(b)) / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seq_steps_per_s": round(b.num_seqs / dt, 2),
-            "sample": f"whole batch ({b.num_seqs} seqs), KV write + decode, {passes} pass(es), "
-                      f"{dt:.2f} s per pass, numpy fp64, BLAS limited to 1 thread"}
+    dt1 = (time.perf_counter() - t0) / passes
+    ncores = len(os.sched_getaffinity(0))
+    parts = [list(range(w, b.num_seqs, ncores)) for w in range(ncores)]
+    parts = [p for p in parts if p]
+    kp, vp = oracle.kv_write(b.k_pool, b.v_pool, b.new_k, b.new_v, b.slot_mapping)
+    _ORACLE_INPUT = (b, kp, vp)
+    ctx = multiprocessing.get_context("fork")
+    with ctx.Pool(len(parts)) as pool:
+        passes_n, t0 = 0, time.perf_counter()
+        while True:
+            # the write again (the workers read the copy made before they
+            # forked, which holds the same values), then the parallel decode
+            oracle.kv_write(b.k_pool, b.v_pool, b.new_k, b.new_v, b.slot_mapping)
+            assert sum(pool.map(_oracle_part, parts, chunksize=1)) == b.num_seqs
+            passes_n += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+        dtn = (time.perf_counter() - t0) / passes_n
+    _ORACLE_INPUT = None
+    del kp, vp
+    model = cpu_model()
+    return {"value": round(nbytes / dtn / 1e9, 4), "unit": "GB/s", "cores": len(parts), "kind": "oracle",
+            "seq_steps_per_s": round(b.num_seqs / dtn, 2), "seconds_per_pass": round(dtn, 3),
+            "cpu_model": model, "affinity_cores": ncores,
+            "one_core": {"value": round(nbytes / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                         "seq_steps_per_s": round(b.num_seqs / dt1, 2), "seconds_per_pass": round(dt1, 3),
+                         "passes": passes},
+            "sample": f"whole batch ({b.num_seqs} seqs), KV write + decode, numpy fp64: {passes_n} pass(es) "
+                      f"with the decode on {len(parts)} worker processes (sequences dealt round-robin, one BLAS "
+                      f"thread each) after the write, and {passes} pass(es) on one core; CPU: {model}"}
+
+
+# hipDeviceAttribute_t values (HIP 7 runtime): global memory bus width in
+# bits, peak memory clock in kHz, peak core clock in kHz.
+_HIP_ATTR_MEMORY_BUS_WIDTH, _HIP_ATTR_MEMORY_CLOCK_RATE, _HIP_ATTR_CLOCK_RATE = 59, 60, 5
+
+
+def device_memory_props(dev_index: int) -> dict:
+    """The device's reported memory bus width and clock (from the HIP runtime
+    torch has loaded) and the peak they imply (bus bytes x clock x 2 for
+    double data rate), beside the published 8 TB/s the roofline uses."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    out = {}
+    for name, attr in (("memory_bus_width_bits", _HIP_ATTR_MEMORY_BUS_WIDTH),
+                       ("memory_clock_khz", _HIP_ATTR_MEMORY_CLOCK_RATE), ("core_clock_khz", _HIP_ATTR_CLOCK_RATE)):
+        v = ctypes.c_int(0)
+        rc = hip.hipDeviceGetAttribute(ctypes.byref(v), ctypes.c_int(attr), ctypes.c_int(dev_index))
+        out[name] = v.value if rc == 0 else None
+    if out["memory_bus_width_bits"] and out["memory_clock_khz"]:
+        out["implied_peak_gbs"] = round(out["memory_bus_width_bits"] / 8 * out["memory_clock_khz"] * 1e3 * 2 / 1e9, 1)
+    out["published_peak_gbs"] = HBM_PEAK_GBS
+    return out
 
 
 def main() -> int:
@@ -479,6 +563,11 @@ def main() -> int:
 
     log(f"[bench] generating {args.workload}")
     b = PRESETS[args.workload](**({} if args.block_size == 16 else {"block_size": args.block_size}))
+    baseline = None
+    if args.op == "step" and not b.num_prefill_seqs and not args.no_cpu_baseline and not args.copy_first:
+        # before anything touches the GPU: the oracle's worker pool forks
+        log("[bench] timing the fp64 oracle on the host (one core, then every core)")
+        baseline = cpu_baseline(b)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
@@ -606,9 +695,8 @@ def main() -> int:
         "cpu_baseline": None,
     }
     result["copy_reference"] = copy_reference(args.steps)
-    if not args.no_cpu_baseline:
-        log("[bench] timing the fp64 oracle on the host")
-        result["cpu_baseline"] = cpu_baseline(b)
+    result["device_memory"] = device_memory_props(dev.index or 0)
+    result["cpu_baseline"] = baseline
     print(json.dumps(result), flush=True)
     return 0
 

@@ -59,11 +59,6 @@ void launch_typed(const ChunkArgs& a, Shape shape, int tiles, dim3 grid, dim3 bl
 
 }  // namespace
 
-bool chunks_supported(int32_t dtype, int32_t head_dim, int32_t group) {
-    return (dtype == PA_BF16 || dtype == PA_F16) && (head_dim == 64 || head_dim == 128) && group >= 1 &&
-           group <= kMaxGroup;
-}
-
 int32_t launch_chunks(const ChunkArgs& a, hipStream_t stream) {
     const int group = a.num_q_heads / a.num_kv_heads;
     if (!chunks_supported(a.dtype, a.head_dim, group)) return PA_ERR_UNSUPPORTED;

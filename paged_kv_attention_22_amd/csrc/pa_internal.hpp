@@ -196,7 +196,11 @@ struct ChunkArgs {
 // Returns PA_ERR_UNSUPPORTED when no matrix-core kernel exists for the shape
 // (the caller then sends every row down the vector path).
 int32_t launch_chunks(const ChunkArgs& a, hipStream_t stream);
-bool chunks_supported(int32_t dtype, int32_t head_dim, int32_t group);
+// Shapes the matrix-core chunk kernel is built for.
+inline bool chunks_supported(int32_t dtype, int32_t head_dim, int32_t group) {
+    return (dtype == PA_BF16 || dtype == PA_F16) && (head_dim == 64 || head_dim == 128) && group >= 1 &&
+           group <= kMaxGroup;
+}
 
 // pa_decode's host-side argument checks (PA_OK for a valid call, including an
 // empty batch).

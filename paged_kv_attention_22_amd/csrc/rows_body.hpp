@@ -440,15 +440,38 @@ __device__ __forceinline__ void rows_block(const RowsArgs& a, int bid, unsigned 
         rows_of(k, lo, hi);
         // element offsets of the chunk's rows 0 and 8 (wave-uniform)
         const int64_t o_lo = lo * tok_stride, o_hi = (hi - 8) * tok_stride;
+        // rows of the chunk inside the visible context (wave-uniform): 16 or
+        // more except in the sequence's last, partial block
+        const int lim = len - (first + k * kWaves) * kBlock;
+        if (lim >= kBlock) {
 #pragma unroll
-        for (int i = 0; i < NT; ++i)
+            for (int i = 0; i < NT; ++i)
 #pragma unroll
-            for (int u = 0; u < V; ++u) {
-                // this lane's row rg + i*TPW of the chunk is in its first half iff i*TPW < 8
-                const int64_t o = (i * TPW < 8 ? o_lo : o_hi) + (i * TPW) * tok_stride + u * R * E;
-                kk[i][u] = ld16_stream(kbase + o);
-                vv[i][u] = ld16_stream(vbase + o);
-            }
+                for (int u = 0; u < V; ++u) {
+                    // this lane's row rg + i*TPW of the chunk is in its first half iff i*TPW < 8
+                    const int64_t o = (i * TPW < 8 ? o_lo : o_hi) + (i * TPW) * tok_stride + u * R * E;
+                    kk[i][u] = ld16_stream(kbase + o);
+                    vv[i][u] = ld16_stream(vbase + o);
+                }
+        } else {
+            // The partial last block: rows at or past the end of the context
+            // are not loaded (they take no part in the result: compute()
+            // masks their scores and zeroes their V rows), which saves their
+            // bytes of memory traffic.
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int u = 0; u < V; ++u) {
+                    const int64_t o = (i * TPW < 8 ? o_lo : o_hi) + (i * TPW) * tok_stride + u * R * E;
+                    uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+                    if (rg + i * TPW < lim) {
+                        kx = ld16_stream(kbase + o);
+                        vx = ld16_stream(vbase + o);
+                    }
+                    kk[i][u] = kx;
+                    vv[i][u] = vx;
+                }
+        }
     };
     auto compute = [&](const uint4 (&kk)[NT][V], const uint4 (&vv)[NT][V], int k, bool masked) {
         bool valid[NT];

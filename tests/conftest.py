@@ -8,3 +8,11 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+# A stand-in build of the library (the host code under sanitizers, built by
+# tests/test_host_sanitizers.py) replaces libpa.so when this is set.
+if os.environ.get("PA_TEST_LIB"):
+    import paged_kv_attention_22_amd as _pa
+
+    _pa.LIB_PATH = os.environ["PA_TEST_LIB"]
