@@ -25,6 +25,9 @@ constexpr int kWaves = 4;      // waves of a vector-path workgroup
 constexpr int kMaxWaves = 8;   // the most waves any decode workgroup has
 // Smallest GQA group that takes the matrix-core decode path (bf16).
 constexpr int kMfmaMinGroup = 4;
+// Fewest full steps (of two 16-token chunks) per wave for which the
+// matrix-core decode may run its steps backwards.
+constexpr int kRevMinSteps = 8;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -699,8 +702,14 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
     const int bsh = a.block_shift;
     const ChunkMap cm = chunk_map(bsh);
     int ids = 0, ids_hi = 0;
+    // Step k of the loop attends step step_of(k) of this wave: the full steps
+    // run backwards (last to first) in a long context whose table ends on an
+    // odd physical block, forwards otherwise; the tail step always comes last.
+    bool rev = false;
+    int nkf_rev = 0;
+    auto step_of = [&](int k) { return rev && k < nkf_rev ? nkf_rev - 1 - k : k; };
     auto fetch_ids = [&](int kbase) {
-        const int jj = b0 + 2 * (wave + (kbase + (lane >> 1)) * W) + (lane & 1);
+        const int jj = b0 + 2 * (wave + step_of(kbase + (lane >> 1)) * W) + (lane & 1);
         ids = bt[min((jj << cm.mul) >> cm.shr, a.max_blocks - 1)];
         ids_hi = bt[min(((jj << cm.mul) + cm.mul) >> cm.shr, a.max_blocks - 1)];
     };
@@ -724,12 +733,28 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
     // takes the tail step, which puts the new token in)
     const int full_end = min(b1, (append ? max(len - 1, 0) : len) / kBlock);
     const int nkf = full_end >= first + 2 ? min(nk, (full_end - first - 2) / (2 * W) + 1) : 0;
+    // Direction of the full steps.  In a batch whose sequences share a long
+    // prefix, a unit reads the prefix (shared: from the caches, after the
+    // first reader) and then its own blocks (from HBM); if every unit went in
+    // the same direction, the whole chip would first read from the caches
+    // and then stream from HBM.  Running about half of the long units
+    // backwards (by the parity of the last table entry of the context, a
+    // property of the sequence, so its result does not depend on the rest of
+    // the batch) overlaps the two (measured: the long-context batch's
+    // pa_decode 130 -> 127 us).  Short contexts keep the forward order, whose
+    // first ids are already on their way.
+    if (nkf >= kRevMinSteps) {
+        const int last_id = bt[min(((nblk - 1) << cm.mul) >> cm.shr, a.max_blocks - 1)];
+        rev = (__builtin_amdgcn_readfirstlane(last_id) & 1) != 0;
+        nkf_rev = nkf;
+        if (rev) fetch_ids(0);
+    }
     // First pool rows of the step's chunk `half`, tokens 0-7 (lo) and 8-15 (hi).
     auto chunk_rows = [&](int k, int half, int64_t& lo, int64_t& hi) {  // ids already fetched
         const int ln = ((k & 31) << 1) | half;
         const int bl = min(max(__builtin_amdgcn_readlane(ids, ln), 0), a.num_blocks - 1);
         const int bh = min(max(__builtin_amdgcn_readlane(ids_hi, ln), 0), a.num_blocks - 1);
-        const int off = ((first + 2 * W * k + half) << 4) & cm.in_block;
+        const int off = ((first + 2 * W * step_of(k) + half) << 4) & cm.in_block;
         lo = ((int64_t)bl << bsh) + off;
         hi = ((int64_t)bh << bsh) + off + cm.hi_off;
     };
@@ -754,7 +779,7 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
     for (int i = 0; i < MT; ++i) acc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
     auto load = [&](uint4 (&kf)[2][KS], uint4 (&vr)[VL], int k) {
-        const int jb = first + 2 * W * k;
+        const int jb = first + 2 * W * step_of(k);
         int64_t lo0, hi0, lo1, hi1;
         rows_of(k, 0, lo0, hi0);
         if (jb + 1 < b1) {
@@ -789,7 +814,7 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
         }
     };
     auto compute = [&](const uint4 (&kf)[2][KS], const uint4 (&vr)[VL], int k, bool masked) {
-        const int pos0 = (first + 2 * W * k) * kBlock;  // first token of the step
+        const int pos0 = (first + 2 * W * step_of(k)) * kBlock;  // first token of the step
         const int pend = min(len, b1 * kBlock);              // tokens at or past this are excluded
 #pragma unroll
         for (int u = 0; u < VL; ++u) {
@@ -848,10 +873,11 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
     };
 
     // Two register buffers, as in rows_block: the load at the end of the loop
-    // is clamped to this wave's last step, so with an even number of full
-    // steps the tail step is in flight when the loop ends.  (With an odd
-    // number it is loaded after the last full step: a second live buffer for
-    // it would push this kernel past 256 registers.)
+    // fetches step k + 2 when this wave has one, so with an even number of
+    // full steps the tail step is in flight when the loop ends, and a wave
+    // with nothing left loads nothing.  (With an odd number the tail is
+    // loaded after the last full step: a second live buffer for it would push
+    // this kernel past 256 registers.)
     uint4 ka[2][KS], va[VL], kb[2][KS], vb[VL];
     const int last = nk - 1;
     int k = 0;
@@ -859,7 +885,7 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
     for (; k + 1 < nkf; k += 2) {
         load(kb, vb, k + 1);
         compute(ka, va, k, false);
-        load(ka, va, min(k + 2, last));
+        if (k + 2 <= last) load(ka, va, k + 2);
         compute(kb, vb, k + 1, false);
     }
     const bool tail_loaded = nkf > 0 && k == nkf;  // the loop's last load was step nkf
