@@ -9,18 +9,28 @@ using namespace chunk_impl;
 
 // The chip hands workgroups to its XCDs (each with its own L2) round-robin by
 // linear index.  Every row tile and key part of one (sequence, kv head) reads
-// the same keys, so the launch is numbered to put all of them on one XCD:
-// (sequence, kv head) pair c runs on XCD c % kXcds, its `tiles` workgroups
-// spread over that XCD's compute units.  The grid holds tiles * (pairs
-// rounded up to a multiple of kXcds) workgroups; the padding ones exit.
+// the same keys, so a launch of at least kXcds such pairs is numbered to put
+// all of them on one XCD: pair c runs on XCD c % kXcds, its `tiles`
+// workgroups spread over that XCD's compute units (the grid holds tiles *
+// (pairs rounded up to a multiple of kXcds) workgroups; the padding ones
+// exit).  With fewer pairs that numbering would leave XCDs idle, so the
+// workgroups are numbered plainly, pair-major.
 constexpr int kXcds = 8;
 
 template <typename T, int D, int NT, int DEPTH, int KSPLIT>
 __global__ __launch_bounds__(kRowWaves * KSPLIT * 64) void chunk_kernel(const ChunkArgs a, int tiles) {
     const int id = blockIdx.x;
-    const int x = id % kXcds, k = id / kXcds;
-    const int pair = k / tiles * kXcds + x;
-    if (pair >= a.num_kv_heads * a.num_seqs) return;
+    const int npairs = a.num_kv_heads * a.num_seqs;
+    int pair, k;
+    if (npairs >= kXcds) {
+        const int x = id % kXcds;
+        k = id / kXcds;
+        pair = k / tiles * kXcds + x;
+    } else {
+        pair = id / tiles;
+        k = id;  // k % tiles below is the tile
+    }
+    if (pair >= npairs) return;
     if constexpr (KSPLIT == 1) {
         // the tile stages, one LDS array each (the loads into them go
         // straight from memory to LDS)
@@ -70,7 +80,7 @@ int32_t launch_chunks(const ChunkArgs& a, hipStream_t stream) {
     const int64_t tiles = small ? small_tiles : (rows + kRowsLarge - 1) / kRowsLarge * kparts;
     const Shape shape = small ? kSmallHalves : (a.alone ? kLargeHalves : kLargeRange);
     const int64_t pairs = (int64_t)a.num_kv_heads * a.num_seqs;
-    const int64_t blocks = tiles * ((pairs + kXcds - 1) / kXcds * kXcds);
+    const int64_t blocks = tiles * (pairs >= kXcds ? (pairs + kXcds - 1) / kXcds * kXcds : pairs);
     if (blocks > INT32_MAX) return PA_ERR_SHAPE;
     const dim3 grid((unsigned)blocks);
     const dim3 block(kRowWaves * (shape == kLargeRange ? 1 : 2) * 64);

@@ -196,7 +196,7 @@ int32_t launch_typed(const RowsArgs& a, hipStream_t stream) {
         // Eight waves per workgroup (two per SIMD) keep twice the loads in
         // flight of four; a decode beside the shared-prefix tiles keeps four,
         // which leave room on each compute unit for a prefix workgroup.
-        if (a.group_start != nullptr)
+        if (a.group_start != nullptr && !a.fold_prefix)
             hipLaunchKernelGGL((mfma_rows_kernel<T, D, G, kWaves>), dim3((unsigned)units), dim3(kWaves * 64), 0,
                                stream, a);
         else

@@ -408,33 +408,49 @@ namespace {
 struct CascadePlan {
     int32_t prefix_part;   // keys per part of the prefix phase (multiple of 64), 0: no prefix phase
     int32_t prefix_slots;  // key parts of the longest prefix
-    int32_t part;          // partition of the keys after the prefix (multiple of 16)
+    int32_t part;          // partition of the keys after the prefix (multiple of 16); <= 0 with fold
+    bool fold;             // one pass after the prefix phase, folding its partial states (no merge)
     size_t bytes;          // workspace
 };
 
-// The prefix phase (matrix cores) runs beside the decode kernel, which keeps
-// about one workgroup per compute unit streaming from memory: its key range is
-// split into parts of at least 256 keys until it has about 128 workgroups of
-// 128 rows (row tiles x kv heads x groups x parts), few enough parts to keep
-// the merge short.  The keys after the prefix are split as pa_decode would
-// split the whole context (one partition when it would not split), always
-// into partial states that the merge combines with the prefix's.
+// Two plans, chosen by how pa_decode would split the whole context.
+//
+// When it would run one pass (enough (sequence, kv head) units to fill the
+// chip), the prefix phase runs first, alone, on the call's stream, its key
+// range split into parts until it has about 256 workgroups of 128 rows (row
+// tiles x kv heads x groups x parts; at least two 64-key tiles per part, one
+// for each key half); then the decode kernel reads each sequence's keys after
+// the prefix in one pass and folds the prefix's partial states into its own
+// before writing the output.  No second stream, no merge launch.
+//
+// Otherwise the keys after the prefix are split as pa_decode would split the
+// whole context, always into partial states, and the prefix phase runs beside
+// the decode kernel (on the caller's second stream when given): its key range
+// is split into parts of at least 256 keys until it has about 128 workgroups,
+// few enough parts to keep the merge short; the merge combines both.
 CascadePlan cascade_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                          int32_t max_context_len, int32_t num_groups, int32_t max_group_size,
                          int32_t prefix_cap, int32_t partition_tokens) {
     CascadePlan p = {};
     const int32_t group = num_q_heads / num_kv_heads;
     const int32_t plen = prefix_cap & ~15;
+    int32_t part = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_tokens);
+    p.fold = part <= 0 && plen > 0;
     if (plen > 0) {
         const int64_t row_tiles = ceil_div((int64_t)max_group_size * group, 128);
         const int64_t tiles = ceil_div(plen, 64);
         const int64_t base = row_tiles * num_kv_heads * num_groups;
-        int64_t parts = ceil_div(128, base);
-        parts = std::max<int64_t>(1, std::min<int64_t>(parts, tiles / 4));
+        int64_t parts = p.fold ? ceil_div(256, base) : ceil_div(128, base);
+        parts = std::max<int64_t>(1, std::min<int64_t>(parts, p.fold ? tiles / 2 : tiles / 4));
         p.prefix_part = (int32_t)(64 * ceil_div(tiles, parts));
         p.prefix_slots = ceil_div(plen, p.prefix_part);
     }
-    int32_t part = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_tokens);
+    if (p.fold) {
+        p.part = -1;
+        p.bytes = rows_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, -1, true) +
+                  (size_t)num_seqs * num_q_heads * p.prefix_slots * (size_t)(head_dim + 2) * 4;
+        return p;
+    }
     if (part <= 0) part = std::max(16, (max_context_len + 15) / 16 * 16);
     p.part = part;
     p.bytes = rows_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, part, true,
@@ -509,8 +525,21 @@ int32_t pa_decode_shared_prefix(const void* q, const void* k_pool, const void* v
     a.num_groups = num_groups;
     a.prefix_cap = prefix_cap;
     a.prefix_part_tokens = cp.prefix_part > 0 ? cp.prefix_part : 64;
-    if (int32_t st = prepare_rows(a, num_seqs, cp.part, workspace, workspace_bytes, cp.prefix_slots)) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (cp.fold) {
+        // one pass; the prefix's partial states follow the order array (if any)
+        if (workspace == nullptr || workspace_bytes < cp.bytes) return PA_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return PA_ERR_ALIGN;
+        if (int32_t st = prepare_rows(a, num_seqs, -1, workspace, workspace_bytes)) return st;
+        const size_t order_bytes = rows_bytes(num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim,
+                                              max_context_len, -1, true);
+        a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + order_bytes);
+        a.nparts = cp.prefix_slots;
+        a.prefix_slots = cp.prefix_slots;
+        a.fold_prefix = 1;
+    } else if (int32_t st = prepare_rows(a, num_seqs, cp.part, workspace, workspace_bytes, cp.prefix_slots)) {
+        return st;
+    }
     if (cp.prefix_slots == 0) return run_rows(a, s);
     {
         // Prefix phase: each group's members are the rows of one "chunk" that
@@ -543,6 +572,12 @@ int32_t pa_decode_shared_prefix(const void* q, const void* k_pool, const void* v
         c.partials = a.ws;
         c.part_slots = a.nparts;
         c.num_items = num_seqs;
+        if (cp.fold) {
+            // the prefix phase alone, then the decode kernel, which folds it in
+            c.alone = 1;
+            if (int32_t st = launch_chunks(c, s)) return st;
+            return run_rows(a, s);
+        }
         c.prefer_large = 1;
         // The prefix phase (matrix cores, LDS, cache-resident keys) runs on the
         // caller's auxiliary stream beside the decode kernel (HBM); they write

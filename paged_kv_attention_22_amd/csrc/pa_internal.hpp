@@ -83,6 +83,11 @@ struct RowsArgs {
     int32_t prefix_slots;
     // Split launches: 1 leaves the merge to a later launch_merge call.
     int32_t defer_merge;
+    // Shared-prefix mode in one pass (part_tokens <= 0): 1 = the prefix's
+    // partial states (slots 0 .. of each (item, q head), nparts slots per
+    // (item, q head)) are already in ws, and the attention kernel folds them
+    // into its own state before writing the output (no merge launch).
+    int32_t fold_prefix;
     // Append mode (decode items only, k_new != NULL): sequence s's new token
     // is the one at position len-1 (len = its clamped context length); its K
     // and V rows are at k_new + s*k_new_stride and v_new + s*v_new_stride

@@ -286,11 +286,21 @@ __device__ __forceinline__ void combine_waves(const RowsArgs& a, const Item& it,
     constexpr int E = Elem<T>::kPerChunk;
     constexpr int CPR = D / E;  // 16-byte chunks per output row
     const int Hq = a.num_q_heads;
+    // With a folded prefix: the prefix's key parts of this (row, q head), in
+    // the first slots of its partial states (as the merge would read them).
+    int npre = 0;
+    if (a.fold_prefix && final_out) {
+        const int pch = prefix_chunks(a, it.seq);
+        npre = min((pch * kBlock + a.prefix_part_tokens - 1) / a.prefix_part_tokens, a.nparts);
+    }
+    const int64_t nslots = (int64_t)a.num_items * a.num_q_heads * a.nparts;
     for (int t = threadIdx.x; t < G * CPR; t += W * 64) {
         const int h = t / CPR, cc = t % CPR;
         float M = s_m[0][h];
 #pragma unroll
         for (int w = 1; w < W; ++w) M = fmaxf(M, s_m[w][h]);
+        const int64_t slot0 = ((int64_t)it.item * a.num_q_heads + g * G + h) * a.nparts;
+        for (int p = 0; p < npre; ++p) M = fmaxf(M, a.ws[nslots * D + slot0 + p]);
         const float mref = (M == kNegInf) ? 0.0f : M;
         float den = 0.0f, o[E];
 #pragma unroll
@@ -301,6 +311,14 @@ __device__ __forceinline__ void combine_waves(const RowsArgs& a, const Item& it,
             den = fmaf(s_l[w][h], wt, den);
 #pragma unroll
             for (int e = 0; e < E; ++e) o[e] = fmaf(s_acc[w][h][cc * E + e], wt, o[e]);
+        }
+        for (int p = 0; p < npre; ++p) {  // the prefix's partial states, folded in
+            const float mp = a.ws[nslots * D + slot0 + p];
+            const float wt = mp == kNegInf ? 0.0f : fast_exp2(mp - mref);
+            den = fmaf(a.ws[nslots * D + nslots + slot0 + p], wt, den);
+            const float* ap = a.ws + (slot0 + p) * D + cc * E;
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = fmaf(ap[e], wt, o[e]);
         }
         const int hq = g * G + h;
         if (final_out) {
@@ -315,7 +333,6 @@ __device__ __forceinline__ void combine_waves(const RowsArgs& a, const Item& it,
             for (int e = 0; e < E; e += 4) st16(wa + e, make_uint4(__float_as_uint(o[e]), __float_as_uint(o[e + 1]),
                                                                    __float_as_uint(o[e + 2]), __float_as_uint(o[e + 3])));
             if (cc == 0) {
-                const int64_t nslots = (int64_t)a.num_items * Hq * a.nparts;
                 a.ws[nslots * D + slot] = M;
                 a.ws[nslots * D + nslots + slot] = den;
             }
