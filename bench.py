@@ -61,6 +61,61 @@ def measured_traffic(partition: int, block_size: int, workload: str):
     return t.get("hbm_bytes_per_decode")
 
 
+def traffic_record(fetch_csv: str, write_csv: str) -> dict:
+    """The traffic record of the headline decode kernel, from the counter CSVs
+    of two rocprofv3 runs of `bench.py --no-cpu-baseline --copy-first --steps 5
+    --warmup 1`, one with --pmc FETCH_SIZE and one with --pmc WRITE_SIZE (KiB
+    per dispatch).  Each counter is scaled to bytes by what it reads for the
+    1 GiB elementwise kernel the same process runs first (1 GiB read and
+    1 GiB written per launch).  The decode dispatches are those of the
+    two-call steps: each directly follows a kv_write dispatch."""
+    import csv
+    import statistics
+
+    def pick(path):
+        with open(path) as f:
+            rs = list(csv.DictReader(f))
+        copy = [float(r["Counter_Value"]) for r in rs if "MulFunctor" in r["Kernel_Name"]]
+        dec = [float(r["Counter_Value"]) for i, r in enumerate(rs)
+               if "rows_kernel" in r["Kernel_Name"] and i > 0 and "kv_write_kernel" in rs[i - 1]["Kernel_Name"]]
+        if not copy or not dec:
+            raise SystemExit(f"{path}: no calibration or decode dispatches found")
+        return statistics.mean(copy), statistics.mean(dec), len(dec)
+
+    copy_f, dec_f, n = pick(fetch_csv)
+    copy_w, dec_w, _ = pick(write_csv)
+    fs, ws = (1 << 30) / 1024 / copy_f, (1 << 30) / 1024 / copy_w
+    rd, wr = dec_f * fs * 1024, dec_w * ws * 1024
+    from workloads import qwen3_06b_decode
+    alg = decode_bytes(qwen3_06b_decode())
+    cmd = ("cd /tmp && timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d <out> -o run -- "
+           "python3 /root/repo/bench.py --no-cpu-baseline --copy-first --steps 5 --warmup 1")
+    return {
+        "kernel": "rows_kernel<bf16, 128, 2> (pa_decode, one pass, longest first ranked in-kernel)",
+        "workload": "qwen3_06b_decode (seed 3): 256 seqs, 16/8 heads, head_dim 128, bf16, block size 16",
+        "block_size": 16,
+        "kernel_source_hash": kernel_source_hash(),
+        "partition_tokens": -1,
+        "fetch_size_kib_per_dispatch": round(dec_f, 1),
+        "write_size_kib_per_dispatch": round(dec_w, 1),
+        "dispatches": n,
+        "calibration": {
+            "kernel": "torch.mul int32 over 1 GiB, three launches in the same process before the decode steps "
+                      "(bench.py --copy-first): 1 GiB read + 1 GiB written per launch",
+            "fetch_size_kib": round(copy_f, 1), "write_size_kib": round(copy_w, 1),
+            "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)},
+        "hbm_bytes_per_decode": int(rd + wr),
+        "hbm_read_bytes": int(rd),
+        "hbm_write_bytes": int(wr),
+        "algorithmic_bytes": alg,
+        "traffic_over_algorithmic": round((rd + wr) / alg, 4),
+        "commands": [cmd.format(c="FETCH_SIZE"), cmd.format(c="WRITE_SIZE"),
+                     "python3 bench.py --traffic-record <out>/fetch/run_counter_collection.csv "
+                     "<out>/write/run_counter_collection.csv > profiles/decode_qwen3_06b_b256_traffic.json"],
+        "dispatch_selection": "pa_decode dispatches of the two-call steps (each directly after a kv_write dispatch)",
+    }
+
+
 def unique_context_tokens(b) -> int:
     """Distinct pool slots the batch reads: a physical block shared by several
     tables (a common prefix) counts once."""
@@ -377,7 +432,8 @@ def bench_shared_prefix(args, b, up) -> dict:
                              "p10": round(float(np.percentile(s_us, 10)), 2),
                              "p90": round(float(np.percentile(s_us, 90)), 2)},
         "pa_decode_us": {"mean": round(float(np.mean(p_us)), 2), "median": round(float(np.median(p_us)), 2)},
-        "roofline": {"kernel": "pa_decode_shared_prefix call: prefix chunk kernel + decode kernel + merge",
+        "roofline": {"kernel": "pa_decode_shared_prefix call: prefix chunk kernel, then the decode kernel folding its "
+                                 "partial states in (with a split context: both side by side, then the merge)",
                      "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "algorithmic_bytes": dbytes},
@@ -490,9 +546,10 @@ _HIP_ATTR_MEMORY_BUS_WIDTH, _HIP_ATTR_MEMORY_CLOCK_RATE, _HIP_ATTR_CLOCK_RATE = 
 
 
 def device_memory_props(dev_index: int) -> dict:
-    """The device's reported memory bus width and clock (from the HIP runtime
-    torch has loaded) and the peak they imply (bus bytes x clock x 2 for
-    double data rate), beside the published 8 TB/s the roofline uses."""
+    """The device's reported memory bus width and clocks (from the HIP runtime
+    torch has loaded), as context beside the published 8 TB/s the roofline
+    uses.  No peak is derived from them: the runtime does not state how many
+    transfers per pin it counts in one reported memory clock."""
     import ctypes
     hip = ctypes.CDLL("libamdhip64.so.7")
     out = {}
@@ -501,8 +558,6 @@ def device_memory_props(dev_index: int) -> dict:
         v = ctypes.c_int(0)
         rc = hip.hipDeviceGetAttribute(ctypes.byref(v), ctypes.c_int(attr), ctypes.c_int(dev_index))
         out[name] = v.value if rc == 0 else None
-    if out["memory_bus_width_bits"] and out["memory_clock_khz"]:
-        out["implied_peak_gbs"] = round(out["memory_bus_width_bits"] / 8 * out["memory_clock_khz"] * 1e3 * 2 / 1e9, 1)
     out["published_peak_gbs"] = HBM_PEAK_GBS
     return out
 
@@ -528,10 +583,16 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--traffic-record", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the headline decode's traffic record from two rocprofv3 --pmc counter CSVs "
+                         "(FETCH_SIZE, WRITE_SIZE) and exit; uses no GPU")
     ap.add_argument("--copy-first", action="store_true",
                     help="run the plain 1 GiB copy three times before the benchmark, in the same process, "
                          "so one counter run reads both (the copy's bytes are known)")
     args = ap.parse_args()
+    if args.traffic_record:
+        print(json.dumps(traffic_record(*args.traffic_record), indent=1))
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               "(no multi-GPU path is built)", file=sys.stderr)
