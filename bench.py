@@ -61,7 +61,7 @@ def measured_traffic(partition: int, block_size: int, workload: str):
     return t.get("hbm_bytes_per_decode")
 
 
-def traffic_record(fetch_csv: str, write_csv: str) -> dict:
+def traffic_record(fetch_csv: str, write_csv: str, alg: int | None = None) -> dict:
     """The traffic record of the headline decode kernel, from the counter CSVs
     of two rocprofv3 runs of `bench.py --no-cpu-baseline --copy-first --steps 5
     --warmup 1`, one with --pmc FETCH_SIZE and one with --pmc WRITE_SIZE (KiB
@@ -86,8 +86,9 @@ def traffic_record(fetch_csv: str, write_csv: str) -> dict:
     copy_w, dec_w, _ = pick(write_csv)
     fs, ws = (1 << 30) / 1024 / copy_f, (1 << 30) / 1024 / copy_w
     rd, wr = dec_f * fs * 1024, dec_w * ws * 1024
-    from workloads import qwen3_06b_decode
-    alg = decode_bytes(qwen3_06b_decode())
+    if alg is None:  # the headline batch's algorithmic bytes
+        from workloads import qwen3_06b_decode
+        alg = decode_bytes(qwen3_06b_decode())
     cmd = ("cd /tmp && timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d <out> -o run -- "
            "python3 /root/repo/bench.py --no-cpu-baseline --copy-first --steps 5 --warmup 1")
     return {
@@ -462,15 +463,31 @@ def copy_reference(steps: int) -> dict:
 _ORACLE_INPUT = None
 
 
-def _oracle_part(seqs):
-    """Worker of the all-cores oracle leg: decode of the given sequences over
-    the written pools (the oracle as it stands, one BLAS thread per worker)."""
-    from threadpoolctl import threadpool_limits
+def _oracle_rows(b, kp, vp, seqs=None):
+    """The oracle's attention over the written pools for the given sequences
+    (all of them by default): their query rows (one per decode sequence, a
+    chunk's rows for a prefill sequence), their tables and lengths."""
+    import numpy as np
 
     import oracle
+    qsl = np.asarray(b.query_start_loc)
+    if seqs is None:
+        return oracle.attention(b.q, qsl, kp, vp, b.block_tables, b.context_lens, b.scale, b.dtype)
+    rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in seqs])
+    sub_qsl = np.concatenate([[0], np.cumsum([qsl[s + 1] - qsl[s] for s in seqs])])
+    return oracle.attention(b.q[rows], sub_qsl, kp, vp, b.block_tables[seqs], b.context_lens[seqs],
+                            b.scale, b.dtype)
+
+
+def _oracle_part(seqs):
+    """Worker of the all-cores oracle leg: attention of the given sequences
+    over the written pools (the oracle as it stands, one BLAS thread per
+    worker)."""
+    from threadpoolctl import threadpool_limits
+
     b, kp, vp = _ORACLE_INPUT
     with threadpool_limits(1):
-        oracle.decode(b.q[seqs], kp, vp, b.block_tables[seqs], b.context_lens[seqs], b.scale, b.dtype)
+        _oracle_rows(b, kp, vp, seqs)
     return len(seqs)
 
 
@@ -486,7 +503,9 @@ def cpu_model() -> str:
 
 
 def cpu_baseline(b, min_seconds: float = 8.0) -> dict:
-    """The fp64 oracle on the same step (KV write + decode of every sequence),
+    """The fp64 oracle on the same step (KV write + attention of every
+    sequence's query rows: one per decode sequence, a chunk's rows for a
+    prefill sequence),
     timed on the host in two legs: one core (one BLAS thread), and every core
     this process may run on (the KV write in this process, then the decode on
     a pool of that many worker processes with the sequences dealt round-robin
@@ -504,7 +523,7 @@ def cpu_baseline(b, min_seconds: float = 8.0) -> dict:
     with threadpool_limits(1):
         while True:
             kp, vp = oracle.kv_write(b.k_pool, b.v_pool, b.new_k, b.new_v, b.slot_mapping)
-            oracle.decode(b.q, kp, vp, b.block_tables, b.context_lens, b.scale, b.dtype)
+            _oracle_rows(b, kp, vp)
             passes += 1
             if time.perf_counter() - t0 >= min_seconds:
                 break
@@ -519,7 +538,7 @@ def cpu_baseline(b, min_seconds: float = 8.0) -> dict:
         passes_n, t0 = 0, time.perf_counter()
         while True:
             # the write again (the workers read the copy made before they
-            # forked, which holds the same values), then the parallel decode
+            # forked, which holds the same values), then the parallel attention
             oracle.kv_write(b.k_pool, b.v_pool, b.new_k, b.new_v, b.slot_mapping)
             assert sum(pool.map(_oracle_part, parts, chunksize=1)) == b.num_seqs
             passes_n += 1
@@ -530,13 +549,13 @@ def cpu_baseline(b, min_seconds: float = 8.0) -> dict:
     del kp, vp
     model = cpu_model()
     return {"value": round(nbytes / dtn / 1e9, 4), "unit": "GB/s", "cores": len(parts), "kind": "oracle",
-            "seq_steps_per_s": round(b.num_seqs / dtn, 2), "seconds_per_pass": round(dtn, 3),
+            "seq_steps_per_s": round(b.num_seqs / dtn, 2), "seconds_per_pass": round(dtn, 6),
             "cpu_model": model, "affinity_cores": ncores,
             "one_core": {"value": round(nbytes / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
-                         "seq_steps_per_s": round(b.num_seqs / dt1, 2), "seconds_per_pass": round(dt1, 3),
+                         "seq_steps_per_s": round(b.num_seqs / dt1, 2), "seconds_per_pass": round(dt1, 6),
                          "passes": passes},
-            "sample": f"whole batch ({b.num_seqs} seqs), KV write + decode, numpy fp64: {passes_n} pass(es) "
-                      f"with the decode on {len(parts)} worker processes (sequences dealt round-robin, one BLAS "
+            "sample": f"whole batch ({b.num_seqs} seqs), KV write + attention, numpy fp64: {passes_n} pass(es) "
+                      f"with the attention on {len(parts)} worker processes (sequences dealt round-robin, one BLAS "
                       f"thread each) after the write, and {passes} pass(es) on one core; CPU: {model}"}
 
 
@@ -625,7 +644,7 @@ def main() -> int:
     log(f"[bench] generating {args.workload}")
     b = PRESETS[args.workload](**({} if args.block_size == 16 else {"block_size": args.block_size}))
     baseline = None
-    if args.op == "step" and not b.num_prefill_seqs and not args.no_cpu_baseline and not args.copy_first:
+    if args.op == "step" and not args.no_cpu_baseline and not args.copy_first:
         # before anything touches the GPU: the oracle's worker pool forks
         log("[bench] timing the fp64 oracle on the host (one core, then every core)")
         baseline = cpu_baseline(b)
@@ -647,7 +666,16 @@ def main() -> int:
         print(json.dumps(bench_shared_prefix(args, b, up)), flush=True)
         return 0
     if b.num_prefill_seqs:
-        print(json.dumps(bench_mixed(args, b, up, dev)), flush=True)
+        res = bench_mixed(args, b, up, dev)
+        if baseline is not None:
+            # the mixed step's metric is a time: the oracle's, per whole pass
+            baseline = dict(baseline, value=round(baseline["seconds_per_pass"] * 1e6, 1), unit="us",
+                            higher_is_better=False,
+                            one_core=dict(baseline["one_core"],
+                                          value=round(baseline["one_core"]["seconds_per_pass"] * 1e6, 1),
+                                          unit="us"))
+        res["cpu_baseline"] = baseline
+        print(json.dumps(res), flush=True)
         return 0
 
     pools = [(up(b.k_pool), up(b.v_pool)) for _ in range(2)]
@@ -712,7 +740,7 @@ def main() -> int:
     achieved = dbytes / dec_mean_s / 1e9
     traffic = measured_traffic(part, int(b.k_pool.shape[1]), b.name)
     result = {
-        "metric": METRIC,
+        "metric": METRIC if b.name == "qwen3_06b_decode" else f"pa_decode HBM GB/s (% of peak) + seq-steps/s, {b.name}",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,

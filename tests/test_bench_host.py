@@ -80,3 +80,50 @@ def test_traffic_reported_only_for_matching_sources(tmp_path, monkeypatch):
     p.write_text(json.dumps(stale))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(p))
     assert bench.measured_traffic(-1, 16, "qwen3_06b_decode") is None
+
+
+def test_oracle_rows_of_a_subset_are_the_whole_batch_rows():
+    """The all-cores baseline leg splits the batch by sequence: the oracle's
+    rows for a subset of sequences (prefill chunks and decode rows) equal
+    those rows of the whole batch's result."""
+    import oracle
+    b = mixed_prefill(seed=9, chunks=2, chunk_len=20, prior_hi=50, n_decode=3, dec_lo=5, dec_hi=30)
+    kp, vp = oracle.kv_write(b.k_pool, b.v_pool, b.new_k, b.new_v, b.slot_mapping)
+    whole = bench._oracle_rows(b, kp, vp)
+    qsl = b.query_start_loc
+    for seqs in ([0], [1, 3], [4, 0, 2]):
+        rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in seqs])
+        assert np.array_equal(bench._oracle_rows(b, kp, vp, seqs), whole[rows])
+
+
+def test_cpu_baseline_legs_on_a_mixed_batch():
+    b = mixed_prefill(seed=9, chunks=2, chunk_len=20, prior_hi=50, n_decode=3, dec_lo=5, dec_hi=30)
+    r = bench.cpu_baseline(b, min_seconds=0.0)
+    assert r["kind"] == "oracle" and r["cores"] >= 1 and r["one_core"]["cores"] == 1
+    assert r["seconds_per_pass"] > 0 and r["one_core"]["seconds_per_pass"] > 0
+    assert r["affinity_cores"] == len(os.sched_getaffinity(0))
+
+
+def test_traffic_record_scales_counters_by_the_copy(tmp_path):
+    """FETCH_SIZE/WRITE_SIZE in KiB per dispatch, scaled by what each reads
+    for the 1 GiB copy; only decode dispatches right after a KV write count."""
+    cols = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
+
+    def write(path, name, copy_kib, dec_kib, other_kib):
+        rows = [f"1,vectorized_elementwise_kernel<MulFunctor>,{name},{copy_kib}",
+                f"2,kv_write_kernel,{name},10",
+                f"3,rows_kernel<bf16>,{name},{dec_kib}",
+                f"4,rows_kernel<bf16>,{name},{other_kib}",   # not after a KV write: ignored
+                f"5,kv_write_kernel,{name},10",
+                f"6,rows_kernel<bf16>,{name},{dec_kib}"]
+        path.write_text(cols + "\n".join(rows) + "\n")
+
+    f, w = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    write(f, "FETCH_SIZE", 524288, 500000, 1)     # reads half the copy's bytes: scale 2
+    write(w, "WRITE_SIZE", 1048576, 1000, 1)      # reads them exactly: scale 1
+    r = bench.traffic_record(str(f), str(w), alg=2 * 500000 * 1024)
+    assert r["dispatches"] == 2
+    assert r["calibration"]["fetch_scale"] == 2.0 and r["calibration"]["write_scale"] == 1.0
+    assert r["hbm_read_bytes"] == 2 * 500000 * 1024 and r["hbm_write_bytes"] == 1000 * 1024
+    assert r["traffic_over_algorithmic"] == round((2 * 500000 + 1000) / (2 * 500000), 4)
+    assert r["kernel_source_hash"] == bench.kernel_source_hash()
