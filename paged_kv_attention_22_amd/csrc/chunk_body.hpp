@@ -92,8 +92,9 @@ constexpr int kDepth = 1;
 // rows (two row tiles per wave, so each K/V fragment read from LDS feeds two
 // MFMAs) and one key range, which leaves a compute unit's LDS and wave slots
 // for the other kernel.
-constexpr int kSplitBelow = 256;
+constexpr int kSplitBelow = kChunkSplitBelow;
 constexpr int kRowsSmall = 16 * 1 * kRowWaves;
+static_assert(kRowsSmall == kChunkRowsSmall, "the planner's view of the small shape");
 constexpr int kRowsLarge = 16 * 2 * kRowWaves;
 
 

@@ -26,6 +26,11 @@ __host__ __device__ inline ChunkMap chunk_map(int shift) {
     return shift == 3 ? ChunkMap{1, 0, 0, 0} : ChunkMap{0, shift - 4, (1 << shift) - 1, 8};
 }
 constexpr int kMaxGroup = 8; // largest GQA group built
+// Chunk-kernel launch shapes (chosen in launch_chunks): a launch with fewer
+// than kChunkSplitBelow workgroups of kChunkRowsSmall rows runs them with key
+// halves; larger launches take 128-row tiles.
+constexpr int kChunkSplitBelow = 256;
+constexpr int kChunkRowsSmall = 64;
 
 // One launch of the vector-path attention over a set of query rows ("items").
 struct RowsArgs {

@@ -70,10 +70,11 @@ def test_long_context_full_size(pa):
     """The full long-context shape the benchmark times: 64 sequences of
     8,192 tokens, one group sharing a 4,096-token prefix, 28/4 heads (G = 7).
     The library's plan (one pass: 256 (sequence, kv head) units fill the
-    chip) runs the prefix phase first in 16 key parts of 256 (four 128-row
-    tiles per kv head) and folds its partial states into the decode kernel's
-    output; the explicit partitions (64, 512 tokens) run the prefix phase in
-    8 parts of 512 beside the split decode and merge the two."""
+    chip) runs the prefix phase first in 8 key parts of 512 (seven 64-row
+    tiles per kv head, key halves) and folds its partial states into the
+    decode kernel's output; the explicit partitions (64, 512 tokens) run the
+    prefix phase in 8 parts of 512 (128-row tiles) beside the split decode and
+    merge the two."""
     b = long_context()
     S = b.num_seqs
     assert b.shared_prefix_tokens == 4096 and S == 64 and b.max_context_len == 8192
