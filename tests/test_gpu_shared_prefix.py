@@ -126,12 +126,14 @@ def test_large_group_g7_d64_and_fp16(pa):
     run_case(pa, b, tables, gs, [256, 290])
 
 
-def test_many_small_groups(pa):
-    """Thirty groups of two (the prefix phase as many small launches' worth of
-    rows), prefixes from 16 to 464 tokens."""
-    S = 60
-    b = make_batch(94, name="pairs", dtype="bf16", num_q_heads=16, num_kv_heads=8, head_dim=128,
-                   draw_lens=lambda rng: rng.integers(480, 1200, size=S))
+@pytest.mark.parametrize("S", [60, 72])
+def test_many_small_groups(pa, S):
+    """Thirty (or thirty-six) groups of two, prefixes from 16 to 576 tokens:
+    the prefix phase has a 64-row tile per (group, kv head), 240 (or 288)
+    of them, so the one-pass plan keeps the prefix in one key part (with
+    288 even one part exceeds the small launch)."""
+    b = make_batch(94, name=f"pairs{S}", dtype="bf16", num_q_heads=16, num_kv_heads=8, head_dim=128,
+                   draw_lens=lambda rng: rng.integers(600, 1200, size=S))
     groups = [[2 * i, 2 * i + 1] for i in range(S // 2)]
     prefixes = [16 * (1 + i) for i in range(S // 2)]
     tables, gs = share(b, groups, prefixes)
