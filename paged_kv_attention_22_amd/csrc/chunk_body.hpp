@@ -456,116 +456,136 @@ __device__ __forceinline__ void chunk_block(const ChunkArgs& a, int bx, int by, 
             vro[mt] = vr * VRB + (kDma ? ((b >> 4) ^ swz_v<D>(vr)) * 16 + (b & 15) : b);
         }
     }
-    // One tile of math on the K and V tiles at kt, vt (keys j0 .. j0+63).
-    auto compute_tile = [&](int j0, const unsigned char* kt, const unsigned char* vt) {
-        if (j0 < wkend) {
-            // S^T for keys j0 .. j0+63.  Every K fragment is read first and
-            // the products follow, so the LDS reads overlap one another
-            // instead of each waiting in front of its product; each fragment
-            // feeds the kNT row tiles.
-            uint4 kf[4][KS];
+    // The math of one tile (keys j0 .. j0+63), in four parts: the scores
+    // (first product), the V^T fragments read from LDS, the online softmax,
+    // and the second product.
+    using Scores = floatx4[kNT][4];
+    using VFrags = uint4[2][MT];  // (keys 32kk..+15, keys 32kk+16..+31) halves, as the A operand
+    using Probs = uint32_t[kNT][8];
+    // S^T from the K tile at kt.  Every K fragment is read first and the
+    // products follow, so the LDS reads overlap one another instead of each
+    // waiting in front of its product; each fragment feeds the kNT row tiles.
+    auto s_part = [&](const unsigned char* kt, Scores& st) __attribute__((always_inline)) {
+        uint4 kf[4][KS];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kf[mt][ks] = ld16(kt + mt * 16 * KRB + kro[ks]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) st[nt][mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    kf[mt][ks] = ld16(kt + mt * 16 * KRB + kro[ks]);
-            __builtin_amdgcn_sched_barrier(0);
-            floatx4 st[kNT][4];
+                for (int nt = 0; nt < kNT; ++nt) st[nt][mt] = Mma<T>::mfma(as_v8(kf[mt][ks]), qf[nt][ks], st[nt][mt]);
+    };
+    // The V^T fragments of the V tile at vt (they do not depend on the
+    // probabilities, so they are read before the softmax that overlaps them).
+    auto v_read = [&](const unsigned char* vt, VFrags& vf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const uint2 lo = ld_tr(vt + 32 * kk * VRB + vro[mt]);
+                const uint2 hi = ld_tr(vt + (32 * kk + 16) * VRB + vro[mt]);
+                vf[kk][mt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+        }
+    };
+    // Online softmax of the scores: the running max and sum, the lazy
+    // rescaling of the accumulators, and the probabilities packed for the
+    // second product.
+    auto sm_part = [&](int j0, const Scores& st, Probs& pk) __attribute__((always_inline)) {
+        // Only a tile that crosses some row's last visible key (a
+        // wave-uniform test) needs the causal mask.
+        const bool masked = j0 + kKeys - 1 > wlim_min;
+        float sc[kNT][16], mx[kNT];
+        bool need_any = false;
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sc[nt][mt * 4 + r] = st[nt][mt][r];
+            if (masked) {
+                const int rel = lim[nt] - j0 - kg * 4;  // last visible key, tile-relative
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (mt * 16 + r > rel) sc[nt][mt * 4 + r] = kNegInf;
+            }
+            float x = kNegInf;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x = fmaxf(x, sc[nt][i]);
+            x = max_across_row_lanes(x);
+            mx[nt] = x * sl2;  // sl2 > 0: the max of the scaled scores
+            need_any |= mx[nt] > m[nt] + 8.0f;
+        }
+        // Lazy rescaling: the reference max moves only when a score exceeds
+        // it by more than 2^8, so the accumulators are rescaled rarely and
+        // the exponentials stay below 256.  The test is made wave-uniform
+        // so it stays a real branch.
+        if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+                const float mn = mx[nt] > m[nt] + 8.0f ? mx[nt] : m[nt];
+                // A row that has seen no key yet (possible in the second key
+                // half, whose first tile can lie wholly past a row's last
+                // visible key) has nothing to rescale: -inf - -inf is NaN.
+                const float alpha = m[nt] == kNegInf ? 0.0f : fast_exp2(m[nt] - mn);
+                lsum[nt] *= alpha;
+#pragma unroll
+                for (int i = 0; i < MT; ++i) acc[nt][i] *= alpha;
+                m[nt] = mn;
+            }
+        }
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+            const float nmref = (m[nt] == kNegInf) ? 0.0f : -m[nt];
+            float psum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float p0 = fast_exp2(fmaf(sc[nt][2 * i], sl2, nmref));
+                const float p1 = fast_exp2(fmaf(sc[nt][2 * i + 1], sl2, nmref));
+                psum += p0 + p1;
+                pk[nt][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){p0, p1}, V2));
+            }
+            lsum[nt] += psum;
+        }
+    };
+    // O^T += V^T P^T; each V^T fragment feeds the kNT row tiles.
+    auto pv_part = [&](const Probs& pk, const VFrags& vf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            // keys 32*kk .. 32*kk+31: slots 0-3 from st[.][2kk], 4-7 from st[.][2kk+1]
+            V8 pb[kNT];
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt)
+                pb[nt] = as_v8(make_uint4(pk[nt][4 * kk], pk[nt][4 * kk + 1], pk[nt][4 * kk + 2], pk[nt][4 * kk + 3]));
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) st[nt][mt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int mt = 0; mt < MT; ++mt) {
+                const V8 va = as_v8(vf[kk][mt]);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < kNT; ++nt) st[nt][mt] = Mma<T>::mfma(as_v8(kf[mt][ks]), qf[nt][ks], st[nt][mt]);
-            // The V^T fragments of the second product do not depend on the
-            // probabilities: reading them now overlaps the reads with the
-            // softmax.
-            uint2 vlo[2][MT], vhi[2][MT];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    vlo[kk][mt] = ld_tr(vt + 32 * kk * VRB + vro[mt]);
-                    vhi[kk][mt] = ld_tr(vt + (32 * kk + 16) * VRB + vro[mt]);
-                }
+                for (int nt = 0; nt < kNT; ++nt) acc[nt][mt] = Mma<T>::mfma(va, pb[nt], acc[nt][mt]);
             }
-            // Only a tile that crosses some row's last visible key (a
-            // wave-uniform test) needs the causal mask.
-            const bool masked = j0 + kKeys - 1 > wlim_min;
-            float sc[kNT][16], mx[kNT];
-            bool need_any = false;
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sc[nt][mt * 4 + r] = st[nt][mt][r];
-                if (masked) {
-                    const int rel = lim[nt] - j0 - kg * 4;  // last visible key, tile-relative
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (mt * 16 + r > rel) sc[nt][mt * 4 + r] = kNegInf;
-                }
-                float x = kNegInf;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) x = fmaxf(x, sc[nt][i]);
-                x = max_across_row_lanes(x);
-                mx[nt] = x * sl2;  // sl2 > 0: the max of the scaled scores
-                need_any |= mx[nt] > m[nt] + 8.0f;
-            }
-            // Lazy rescaling: the reference max moves only when a score exceeds
-            // it by more than 2^8, so the accumulators are rescaled rarely and
-            // the exponentials stay below 256.  The test is made wave-uniform
-            // so it stays a real branch.
-            if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
-#pragma unroll
-                for (int nt = 0; nt < kNT; ++nt) {
-                    const float mn = mx[nt] > m[nt] + 8.0f ? mx[nt] : m[nt];
-                    // A row that has seen no key yet (possible in the second key
-                    // half, whose first tile can lie wholly past a row's last
-                    // visible key) has nothing to rescale: -inf - -inf is NaN.
-                    const float alpha = m[nt] == kNegInf ? 0.0f : fast_exp2(m[nt] - mn);
-                    lsum[nt] *= alpha;
-#pragma unroll
-                    for (int i = 0; i < MT; ++i) acc[nt][i] *= alpha;
-                    m[nt] = mn;
-                }
-            }
-            uint32_t pk[kNT][8];
-#pragma unroll
-            for (int nt = 0; nt < kNT; ++nt) {
-                const float nmref = (m[nt] == kNegInf) ? 0.0f : -m[nt];
-                float psum = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float p0 = fast_exp2(fmaf(sc[nt][2 * i], sl2, nmref));
-                    const float p1 = fast_exp2(fmaf(sc[nt][2 * i + 1], sl2, nmref));
-                    psum += p0 + p1;
-                    pk[nt][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2){p0, p1}, V2));
-                }
-                lsum[nt] += psum;
-            }
-            // O^T += V^T P^T; each V^T fragment feeds the kNT row tiles.
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                // keys 32*kk .. 32*kk+31: slots 0-3 from st[.][2kk], 4-7 from st[.][2kk+1]
-                V8 pb[kNT];
-#pragma unroll
-                for (int nt = 0; nt < kNT; ++nt)
-                    pb[nt] = as_v8(make_uint4(pk[nt][4 * kk], pk[nt][4 * kk + 1], pk[nt][4 * kk + 2], pk[nt][4 * kk + 3]));
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const V8 va = as_v8(make_uint4(vlo[kk][mt].x, vlo[kk][mt].y, vhi[kk][mt].x, vhi[kk][mt].y));
-#pragma unroll
-                    for (int nt = 0; nt < kNT; ++nt) acc[nt][mt] = Mma<T>::mfma(va, pb[nt], acc[nt][mt]);
-                }
-            }
+        }
+    };
+    // One whole tile on the K and V tiles at kt, vt.
+    auto compute_tile = [&](int j0, const unsigned char* kt, const unsigned char* vt) __attribute__((always_inline)) {
+        if (j0 < wkend) {
+            Scores st;
+            s_part(kt, st);
+            VFrags vf;
+            v_read(vt, vf);
+            Probs pk;
+            sm_part(j0, st, pk);
+            pv_part(pk, vf);
         }
     };
 
@@ -633,15 +653,20 @@ __device__ __forceinline__ void chunk_block(const ChunkArgs& a, int bx, int by, 
         __syncthreads();
         const int hsteps = (ntiles + KSPLIT - 1) / KSPLIT;
         const int nsteps = (hsteps + DEPTH - 1) / DEPTH * DEPTH;
+        // End of step i: tile i+1 into the other LDS buffer, the tile after
+        // the register buffers' ones requested, and the barrier.
+        auto advance = [&](int i, int r) __attribute__((always_inline)) {
+            const int tile = half + KSPLIT * i;
+            store_tile((i + 1) & 1, (tbase + tile + KSPLIT) * kKeys, kreg[r], vreg[r]);
+            load_tile(tile + KSPLIT * (1 + DEPTH), kreg[r], vreg[r]);
+            __syncthreads();
+        };
         for (int i0 = 0; i0 < nsteps; i0 += DEPTH) {
 #pragma unroll
             for (int r = 0; r < DEPTH; ++r) {  // unrolled: static register buffers
                 const int i = i0 + r;
-                const int tile = half + KSPLIT * i;
-                compute_tile((tbase + tile) * kKeys, hk + (i & 1) * KTILE, hv + (i & 1) * VTILE);
-                store_tile((i + 1) & 1, (tbase + tile + KSPLIT) * kKeys, kreg[r], vreg[r]);
-                load_tile(tile + KSPLIT * (1 + DEPTH), kreg[r], vreg[r]);
-                __syncthreads();
+                compute_tile((tbase + half + KSPLIT * i) * kKeys, hk + (i & 1) * KTILE, hv + (i & 1) * VTILE);
+                advance(i, r);
             }
         }
     }
