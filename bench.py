@@ -682,7 +682,7 @@ def main() -> int:
     q, new_k, new_v = up(b.q), up(b.new_k), up(b.new_v)
     slots, tables, lens = up(b.slot_mapping), up(b.block_tables), up(b.context_lens)
     out = torch.empty_like(q)
-    part = pa.decode_partition_tokens(b.num_seqs, b.num_kv_heads, b.max_context_len, args.partition)
+    part = pa.decode_partition_tokens(b.num_seqs, b.num_kv_heads, b.head_dim, b.max_context_len, args.partition)
     ws_bytes = pa.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
                                          b.max_context_len, args.partition)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)

@@ -200,13 +200,16 @@ int32_t pa_qkv_rope_write(const void* qkv, int64_t qkv_token_stride,
  *
  * pa_decode_partition_tokens returns the partition size the library uses for
  * these arguments (-1 = one pass): one pass with at least 256 (sequence, kv
- * head) units, else partitions that bring the launch to about 256 workgroups.
+ * head) units, or when one unit's K and V at the longest context
+ * (max_context_len x 2 x head_dim x 2 bytes) are at most 384 KiB (a split
+ * then costs more than it saves); else partitions that bring the launch to
+ * about 256 workgroups.
  * pa_decode_workspace_bytes returns the workspace pa_decode needs for the same
  * arguments: the longest-first processing order (num_seqs int32, 256-byte
  * aligned) when the batch has more than 2048 sequences and uses one, then the
  * split partials; 0 when neither is used.
  */
-int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
                                    int32_t max_context_len, int32_t partition_tokens);
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim,

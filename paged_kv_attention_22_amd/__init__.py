@@ -49,7 +49,7 @@ class PAError(RuntimeError):
 _SIGNATURES = {
     "pa_status_str": (ctypes.c_char_p, [c_i32]),
     "pa_kv_write": (c_i32, [c_vp, c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_vp, PoolDesc, c_vp]),
-    "pa_decode_partition_tokens": (c_i32, [c_i32, c_i32, c_i32, c_i32]),
+    "pa_decode_partition_tokens": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode_workspace_bytes": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (c_i32, [c_vp, c_vp, c_vp, PoolDesc, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32,
                           c_f, c_vp, c_i32, c_vp, c_size, c_vp]),
@@ -237,8 +237,8 @@ def qkv_rope_write(qkv, num_q_heads, context_lens, block_tables, k_pool, v_pool,
     return q_out
 
 
-def decode_partition_tokens(num_seqs, num_kv_heads, max_context_len, partition_tokens=0) -> int:
-    return lib().pa_decode_partition_tokens(num_seqs, num_kv_heads, max_context_len,
+def decode_partition_tokens(num_seqs, num_kv_heads, head_dim, max_context_len, partition_tokens=0) -> int:
+    return lib().pa_decode_partition_tokens(num_seqs, num_kv_heads, head_dim, max_context_len,
                                             partition_tokens)
 
 

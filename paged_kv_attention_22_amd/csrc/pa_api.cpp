@@ -96,14 +96,23 @@ int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 // contexts) are split into as many partitions as bring the launch to about 256
 // workgroups; more partitions only add per-workgroup start-up, partial-state
 // traffic and merge work (measured at 32-128 units: the best split always gave
-// about 256 workgroups).
+// about 256 workgroups).  A split call costs about 15 us whatever its size (two
+// launches and the partial states), while one pass costs about 5 us plus the
+// longest unit's K/V at 35-50 GB/s per compute unit, so short units run in one
+// pass too: those whose K/V (at two bytes an element) is at most
+// kOnePassBytes.  (Measured, one pass against the split: head_dim 64, G = 7,
+// 32 sequences up to 1,024 tokens 11.6 against 15.7 us, up to 2,048 14.6
+// against 15.5; head_dim 128 up to 1,024 tokens at G = 2 20.5 against 16.6
+// and at G = 4 16.3 against 15.5.)
 constexpr int64_t kSplitTarget = 256;
-int32_t choose_partition(int64_t items, int32_t num_kv_heads, int32_t max_context_len,
+constexpr int64_t kOnePassBytes = 384 << 10;
+int32_t choose_partition(int64_t items, int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len,
                          int32_t requested) {
     if (requested < 0) return -1;
     if (requested > 0) return requested;
     const int64_t units = items * num_kv_heads;
-    if (units <= 0 || units >= kSplitTarget || max_context_len <= 128) return -1;
+    if (units <= 0 || units >= kSplitTarget || (int64_t)max_context_len * head_dim * 4 <= kOnePassBytes)
+        return -1;
     const int64_t parts = ceil_div(kSplitTarget, units);
     const int32_t part = std::max<int32_t>(64, (ceil_div(max_context_len, parts) + 15) / 16 * 16);
     return ceil_div(max_context_len, part) > 1 ? part : -1;
@@ -253,7 +262,8 @@ int32_t pa::decode_impl(const void* q, const void* k_new, const void* v_new, int
     a.v_new = v_new;
     a.k_new_stride = k_new_stride;
     a.v_new_stride = v_new_stride;
-    const int32_t part = choose_partition(num_seqs, pool.num_kv_heads, max_context_len, partition_tokens);
+    const int32_t part = choose_partition(num_seqs, pool.num_kv_heads, pool.head_dim, max_context_len,
+                                          partition_tokens);
     if (int32_t st = prepare_rows(a, num_seqs, part, workspace, workspace_bytes)) return st;
     return run_rows(a, static_cast<hipStream_t>(stream));
 }
@@ -306,10 +316,10 @@ int32_t pa_kv_write(const void* k, const void* v, int64_t k_token_stride, int64_
     return launch_kv_write(a, static_cast<hipStream_t>(stream));
 }
 
-int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
-                                   int32_t partition_tokens) {
-    return choose_partition(num_seqs, num_kv_heads > 0 ? num_kv_heads : 1, max_context_len,
-                            partition_tokens);
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_context_len, int32_t partition_tokens) {
+    return choose_partition(num_seqs, num_kv_heads > 0 ? num_kv_heads : 1, head_dim > 0 ? head_dim : 0,
+                            max_context_len, partition_tokens);
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -318,7 +328,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         max_context_len < 0 || check_partition(partition_tokens))
         return 0;
-    const int32_t part = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_tokens);
+    const int32_t part = choose_partition(num_seqs, num_kv_heads, head_dim, max_context_len, partition_tokens);
     return rows_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, part, true);
 }
 
@@ -437,7 +447,7 @@ CascadePlan cascade_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_h
     CascadePlan p = {};
     const int32_t group = num_q_heads / num_kv_heads;
     const int32_t plen = prefix_cap & ~15;
-    int32_t part = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_tokens);
+    int32_t part = choose_partition(num_seqs, num_kv_heads, head_dim, max_context_len, partition_tokens);
     p.fold = part <= 0 && plen > 0;
     if (plen > 0) {
         const int64_t row_tiles = ceil_div((int64_t)max_group_size * group, 128);
@@ -627,13 +637,13 @@ size_t pa_prefill_workspace_bytes(int32_t num_seqs, int32_t num_prefill_seqs,
         // the element type decides which, so size for both.
         const int64_t slots = (int64_t)num_prefill_seqs * small_rows_for(num_q_heads / num_kv_heads);
         for (const int64_t items : {prefill_rows, slots}) {
-            const int32_t part = choose_partition(items, num_kv_heads, max_context_len, partition_tokens);
+            const int32_t part = choose_partition(items, num_kv_heads, head_dim, max_context_len, partition_tokens);
             const size_t p = rows_bytes(items, num_q_heads, num_kv_heads, head_dim, max_context_len, part, false);
             if (p > pre) pre = p;
         }
     }
     if (num_decode > 0) {
-        const int32_t part = choose_partition(num_decode, num_kv_heads, max_context_len, partition_tokens);
+        const int32_t part = choose_partition(num_decode, num_kv_heads, head_dim, max_context_len, partition_tokens);
         dec = rows_bytes(num_decode, num_q_heads, num_kv_heads, head_dim, max_context_len, part, true);
     }
     return pre > 0 ? align256(dec) + pre : dec;
@@ -707,11 +717,13 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
     dec.seq_end = num_seqs;
     dec.row_begin = (int32_t)prefill_rows;
     dec.mfma_min_pairs = 0;
-    const int32_t dpart = choose_partition(num_decode, pool.num_kv_heads, max_context_len, partition_tokens);
+    const int32_t dpart = choose_partition(num_decode, pool.num_kv_heads, pool.head_dim, max_context_len,
+                                           partition_tokens);
     if (int32_t st = prepare_rows(dec, num_decode, dpart, workspace, workspace_bytes)) return st;
     const size_t dec_bytes = align256(rows_bytes(num_decode, num_q_heads, pool.num_kv_heads,
                                                  pool.head_dim, max_context_len, dpart, true));
-    const int32_t ppart = choose_partition(pre_items, pool.num_kv_heads, max_context_len, partition_tokens);
+    const int32_t ppart = choose_partition(pre_items, pool.num_kv_heads, pool.head_dim, max_context_len,
+                                           partition_tokens);
     const bool pre_ws = rows_bytes(pre_items, num_q_heads, pool.num_kv_heads, pool.head_dim,
                                    max_context_len, ppart, false) > 0;
     if (pre_ws && workspace_bytes < dec_bytes) return PA_ERR_WORKSPACE;

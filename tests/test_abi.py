@@ -149,20 +149,26 @@ def test_prefill_validation(pa):
 
 def test_partition_choice_and_workspace(pa):
     # explicit requests are honoured; -1 means one pass
-    assert pa.decode_partition_tokens(256, 8, 2048, -1) == -1
-    assert pa.decode_partition_tokens(256, 8, 2048, 128) == 128
-    # the library's own choice: one pass for short contexts and for at least
-    # 256 (row, kv head) units; otherwise partitions bringing the launch to
-    # about 256 workgroups (multiples of 16, at least 64 tokens)
-    assert pa.decode_partition_tokens(4, 1, 64, 0) == -1
-    assert pa.decode_partition_tokens(0, 4, 8192, 0) == -1      # no rows (a prefill-only batch's decode part)
-    assert pa.decode_partition_tokens(64, 4, 8192, 0) == -1
-    assert pa.decode_partition_tokens(256, 8, 2048, 0) == -1
-    assert pa.decode_partition_tokens(32, 4, 8192, 0) == 4096
-    assert pa.decode_partition_tokens(16, 4, 8192, 0) == 2048
-    assert pa.decode_partition_tokens(8, 4, 8192, 0) == 1024
-    assert pa.decode_partition_tokens(3, 1, 1000, 0) == 64     # 86 parts wanted: 64-token floor
-    assert pa.decode_partition_tokens(5, 4, 1500, 0) == 128    # ceil(1500 / 13) = 116 -> 128
+    assert pa.decode_partition_tokens(256, 8, 128, 2048, -1) == -1
+    assert pa.decode_partition_tokens(256, 8, 128, 2048, 128) == 128
+    # the library's own choice: one pass for at least 256 (row, kv head)
+    # units and for units whose K/V at the longest context is at most 384 KiB
+    # (L x 2 x head_dim x 2 bytes); otherwise partitions bringing the launch
+    # to about 256 workgroups (multiples of 16, at least 64 tokens)
+    assert pa.decode_partition_tokens(4, 1, 128, 64, 0) == -1
+    assert pa.decode_partition_tokens(0, 4, 128, 8192, 0) == -1      # no rows (a prefill-only batch's decode part)
+    assert pa.decode_partition_tokens(64, 4, 128, 8192, 0) == -1
+    assert pa.decode_partition_tokens(256, 8, 128, 2048, 0) == -1
+    assert pa.decode_partition_tokens(32, 4, 128, 8192, 0) == 4096
+    assert pa.decode_partition_tokens(16, 4, 128, 8192, 0) == 2048
+    assert pa.decode_partition_tokens(8, 4, 128, 8192, 0) == 1024
+    assert pa.decode_partition_tokens(3, 1, 128, 1000, 0) == 64     # 86 parts wanted: 64-token floor
+    assert pa.decode_partition_tokens(5, 4, 128, 1500, 0) == 128    # ceil(1500 / 13) = 116 -> 128
+    # the unit-size rule: 384 KiB is 1,536 tokens at head_dim 64, 768 at 128
+    assert pa.decode_partition_tokens(32, 2, 64, 1536, 0) == -1
+    assert pa.decode_partition_tokens(32, 2, 64, 1552, 0) == 400     # ceil(1552 / 4) = 388 -> 400
+    assert pa.decode_partition_tokens(16, 8, 128, 768, 0) == -1
+    assert pa.decode_partition_tokens(16, 8, 128, 784, 0) == 400     # two parts
     # workspace = the longest-first order (items int32, 256-byte aligned) when
     # the batch is larger than the kernels rank themselves (2048 rows), then
     # items * Hq * nparts * (D + 2) fp32 partials
