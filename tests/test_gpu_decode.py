@@ -52,6 +52,19 @@ WORKLOADS = {
     "qwen25_f16": lambda: qwen25_05b_decode(batch=17, lo=1, hi=900, dtype="f16"),
     "g4_d128_f16": lambda: make_batch(64, name="g4_d128_f16", dtype="f16", num_q_heads=16, num_kv_heads=4,
                                       head_dim=128, draw_lens=lambda rng: rng.integers(1, 700, size=21)),
+    # the group sizes no other case takes: 1 (plain multi-head attention) and
+    # 3 on the vector path, 6 on the matrix-core path (fp16)
+    "g1_d128": lambda: make_batch(66, name="g1_d128", dtype="bf16", num_q_heads=8, num_kv_heads=8,
+                                  head_dim=128, draw_lens=lambda rng: rng.integers(1, 800, size=12)),
+    "g3_d64": lambda: make_batch(67, name="g3_d64", dtype="bf16", num_q_heads=12, num_kv_heads=4,
+                                 head_dim=64, draw_lens=lambda rng: rng.integers(1, 900, size=15)),
+    "g6_d128_f16": lambda: make_batch(68, name="g6_d128_f16", dtype="f16", num_q_heads=24, num_kv_heads=4,
+                                      head_dim=128, draw_lens=lambda rng: rng.integers(1, 1200, size=9)),
+    # one sequence of 65,536 tokens: the library splits it into 1,024-token
+    # partitions, and 16-token partitions give 4,096 partial states per row
+    # for the merge
+    "one_64k": lambda: make_batch(69, name="one_64k", dtype="bf16", num_q_heads=28, num_kv_heads=4,
+                                  head_dim=128, draw_lens=lambda rng: np.array([65536]), pool_factor=1.05),
 }
 
 _cache = {}

@@ -56,6 +56,10 @@ WORKLOADS = {
     # a group of 7 (decode rows on the matrix-core decode path, chunks on MFMA)
     "mixed_g7": lambda: mixed_prefill(seed=7, chunks=2, chunk_len=33, prior_hi=200, n_decode=9,
                                       dec_lo=1, dec_hi=500, num_q_heads=28, num_kv_heads=4),
+    # one long chunk at G = 7: 1,024 new rows after up to 3,000 cached tokens
+    # (56 row tiles of 128 per kv head), beside a few decode rows
+    "long_chunk_g7": lambda: mixed_prefill(seed=20, chunks=1, chunk_len=1024, prior_hi=3000, n_decode=4,
+                                           num_q_heads=28, num_kv_heads=4),
 }
 
 _cache = {}
