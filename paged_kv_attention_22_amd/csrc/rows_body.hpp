@@ -285,6 +285,8 @@ __device__ __forceinline__ void combine_waves(const RowsArgs& a, const Item& it,
                                               const float (&s_m)[W][G], const float (&s_l)[W][G]) {
     constexpr int E = Elem<T>::kPerChunk;
     constexpr int CPR = D / E;  // 16-byte chunks per output row
+    constexpr int kFold = 8;    // prefix slots read together
+    static_assert(E % 4 == 0, "whole 16-byte accumulator chunks");
     const int Hq = a.num_q_heads;
     // With a folded prefix: the prefix's key parts of this (row, q head), in
     // the first slots of its partial states (as the merge would read them).
@@ -300,7 +302,19 @@ __device__ __forceinline__ void combine_waves(const RowsArgs& a, const Item& it,
 #pragma unroll
         for (int w = 1; w < W; ++w) M = fmaxf(M, s_m[w][h]);
         const int64_t slot0 = ((int64_t)it.item * a.num_q_heads + g * G + h) * a.nparts;
-        for (int p = 0; p < npre; ++p) M = fmaxf(M, a.ws[nslots * D + slot0 + p]);
+        // The prefix's slots are read kFold at a time, the loads of a group
+        // issued together (one memory round trip per group, not per slot);
+        // past the last slot the index is clamped to it, which leaves the
+        // maximum unchanged and is given no weight below.
+        const float* const pm = a.ws + nslots * D + slot0;
+        const float* const pl = pm + nslots;
+        for (int p0 = 0; p0 < npre; p0 += kFold) {
+            float mg[kFold];
+#pragma unroll
+            for (int j = 0; j < kFold; ++j) mg[j] = pm[min(p0 + j, npre - 1)];
+#pragma unroll
+            for (int j = 0; j < kFold; ++j) M = fmaxf(M, mg[j]);
+        }
         const float mref = (M == kNegInf) ? 0.0f : M;
         float den = 0.0f, o[E];
 #pragma unroll
@@ -312,13 +326,30 @@ __device__ __forceinline__ void combine_waves(const RowsArgs& a, const Item& it,
 #pragma unroll
             for (int e = 0; e < E; ++e) o[e] = fmaf(s_acc[w][h][cc * E + e], wt, o[e]);
         }
-        for (int p = 0; p < npre; ++p) {  // the prefix's partial states, folded in
-            const float mp = a.ws[nslots * D + slot0 + p];
-            const float wt = mp == kNegInf ? 0.0f : fast_exp2(mp - mref);
-            den = fmaf(a.ws[nslots * D + nslots + slot0 + p], wt, den);
-            const float* ap = a.ws + (slot0 + p) * D + cc * E;
+        for (int p0 = 0; p0 < npre; p0 += kFold) {  // the prefix's partial states, folded in
+            float mg[kFold], lg[kFold];
+            uint4 ag[kFold][E / 4];
 #pragma unroll
-            for (int e = 0; e < E; ++e) o[e] = fmaf(ap[e], wt, o[e]);
+            for (int j = 0; j < kFold; ++j) {
+                const int p = min(p0 + j, npre - 1);
+                mg[j] = pm[p];
+                lg[j] = pl[p];
+                const float* ap = a.ws + (slot0 + p) * D + cc * E;
+#pragma unroll
+                for (int k = 0; k < E / 4; ++k) ag[j][k] = ld16(ap + 4 * k);
+            }
+#pragma unroll
+            for (int j = 0; j < kFold; ++j) {
+                const float wt = (p0 + j >= npre || mg[j] == kNegInf) ? 0.0f : fast_exp2(mg[j] - mref);
+                den = fmaf(lg[j], wt, den);
+#pragma unroll
+                for (int k = 0; k < E / 4; ++k) {
+                    o[4 * k] = fmaf(__uint_as_float(ag[j][k].x), wt, o[4 * k]);
+                    o[4 * k + 1] = fmaf(__uint_as_float(ag[j][k].y), wt, o[4 * k + 1]);
+                    o[4 * k + 2] = fmaf(__uint_as_float(ag[j][k].z), wt, o[4 * k + 2]);
+                    o[4 * k + 3] = fmaf(__uint_as_float(ag[j][k].w), wt, o[4 * k + 3]);
+                }
+            }
         }
         const int hq = g * G + h;
         if (final_out) {
