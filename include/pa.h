@@ -320,20 +320,27 @@ int32_t pa_decode_append(const void* q, const void* k_new, const void* v_new,
  *                 the prefix (0 = no shared prefix)
  * max_group_size  host upper bound of the group sizes (1..num_seqs)
  * max_prefix_len  host upper bound of prefix_lens (0..max_context_len)
- * partition_tokens as pa_decode, for the keys after the prefix (which are
- *                 always stored as partial states: -1 means one partition)
+ * partition_tokens as pa_decode, for the keys after the prefix
  * workspace       pa_decode_shared_prefix_workspace_bytes(...) bytes,
  *                 16-byte aligned (never zero)
  *
- * aux             NULL, or the caller's second stream (pa_aux_stream): the
- *                 prefix phase then runs on it beside the decode kernel
+ * aux             NULL, or the caller's second stream (pa_aux_stream), used
+ *                 only when the keys after the prefix are split (below)
  *
  * Work: the prefix of each group is attended on the matrix cores, the group's
  * members as rows of one block that sees all of the prefix (split into key
- * parts over workgroups): on aux->stream (forked from and joined back into
- * `stream`) when aux is given, else first on `stream`; the rest of each
- * context runs on the decode path on `stream`; a log-sum-exp merge on
- * `stream` combines the partial states.
+ * parts over workgroups, each leaving partial softmax states in the
+ * workspace).  Then one of two plans, by what pa_decode would do with these
+ * arguments (partition_tokens, or the library's choice):
+ *   one pass   the prefix phase first on `stream`, then the decode kernel
+ *              reads each context after its prefix in one pass and folds the
+ *              prefix's partial states into its output (no merge launch; aux
+ *              is not used);
+ *   split      the keys after the prefix in partitions on the decode path on
+ *              `stream`, the prefix phase beside it on aux->stream (forked
+ *              from and joined back into `stream`) when aux is given, else
+ *              first on `stream`; a log-sum-exp merge on `stream` combines
+ *              the partial states.
  * Supported: bf16 or fp16 pools (the matrix cores), group size 1..8.
  * Preconditions on the group arrays are not checked beyond memory safety:
  * rows of groups larger than max_group_size, or groups that overlap, give

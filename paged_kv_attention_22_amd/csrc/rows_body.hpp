@@ -409,7 +409,8 @@ __device__ __forceinline__ void rows_block(const RowsArgs& a, int bid, unsigned 
     if (it.skip) return;
     const bool split = a.part_tokens > 0;
     const int pb = split ? a.part_tokens / kBlock : 0;
-    // shared-prefix mode: the chunks after the group's prefix, always split
+    // shared-prefix mode: the chunks after the group's prefix (split, or one pass
+    // that folds the prefix's partial states into its output)
     const bool cascade = a.group_start != nullptr;
     const int b0 = (cascade ? prefix_chunks(a, it.seq) : 0) + (split ? part * pb : 0);
     const int first = b0 + wave;  // this wave's blocks: first + k*kWaves
@@ -728,7 +729,8 @@ __device__ __forceinline__ void mfma_rows_block(const RowsArgs& a, int bid, unsi
     if (it.skip) return;
     const bool split = a.part_tokens > 0;
     const int pb = split ? a.part_tokens / kBlock : 0;
-    // shared-prefix mode: the chunks after the group's prefix, always split
+    // shared-prefix mode: the chunks after the group's prefix (split, or one pass
+    // that folds the prefix's partial states into its output)
     const bool cascade = a.group_start != nullptr;
     const int b0 = (cascade ? prefix_chunks(a, it.seq) : 0) + (split ? part * pb : 0);
 
