@@ -788,6 +788,8 @@ int32_t pa_prefill_chunk(const void* q, const int32_t* query_start_loc, int32_t 
         if (int32_t st = run_rows(dec, x)) return st;
         return join_from(*aux, s);
     }
+    // One stream: the chunk kernel runs before the vector path, alone.
+    c.alone = 1;
     if (mfma)
         if (int32_t st = launch_chunks(c, s)) return st;
     if (int32_t st = run_rows(pre, s)) return st;
