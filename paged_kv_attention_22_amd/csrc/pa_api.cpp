@@ -604,6 +604,7 @@ int32_t pa_decode_shared_prefix(const void* q, const void* k_pool, const void* v
         // disjoint partial slots, and the merge waits for both.  Without an
         // auxiliary stream the two run one after the other on `stream`.
         if (aux == nullptr) {
+            c.alone = 1;  // nothing beside it: the key-halves shape
             if (int32_t st = launch_chunks(c, s)) return st;
             return run_rows(a, s);
         }
