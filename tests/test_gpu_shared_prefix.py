@@ -138,3 +138,17 @@ def test_many_small_groups(pa, S):
     prefixes = [16 * (1 + i) for i in range(S // 2)]
     tables, gs = share(b, groups, prefixes)
     run_case(pa, b, tables, gs, prefixes, parts=(0,))
+
+
+def test_large_batch_with_order_array(pa):
+    """2,100 sequences in 30 groups of 70: more rows than the decode kernels
+    rank themselves, so a sorting launch writes the longest-first order to
+    the front of the workspace and the one-pass plan keeps the prefix's
+    partial states after it.  G = 2 (the vector decode path)."""
+    S, n = 2100, 70
+    b = make_batch(96, name="order2100", dtype="bf16", num_q_heads=4, num_kv_heads=2, head_dim=64,
+                   draw_lens=lambda rng: rng.integers(130, 400, size=S))
+    groups = [list(range(n * i, n * (i + 1))) for i in range(S // n)]
+    prefixes = [32 + 3 * i for i in range(S // n)]   # not all multiples of 16
+    tables, gs = share(b, groups, prefixes)
+    run_case(pa, b, tables, gs, prefixes, parts=(-1, 0))
