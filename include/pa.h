@@ -322,7 +322,8 @@ int32_t pa_decode_append(const void* q, const void* k_new, const void* v_new,
  * max_prefix_len  host upper bound of prefix_lens (0..max_context_len)
  * partition_tokens as pa_decode, for the keys after the prefix
  * workspace       pa_decode_shared_prefix_workspace_bytes(...) bytes,
- *                 16-byte aligned (never zero)
+ *                 16-byte aligned; when that is 0 (no group has a prefix and
+ *                 the keys run in one pass) it may be NULL
  *
  * aux             NULL, or the caller's second stream (pa_aux_stream), used
  *                 only when the keys after the prefix are split (below)

@@ -426,7 +426,9 @@ struct CascadePlan {
 // Two plans, chosen by how pa_decode would split the whole context.
 //
 // When it would run one pass (enough (sequence, kv head) units to fill the
-// chip), the prefix phase runs first, alone, on the call's stream, its key
+// chip, or units short enough that a split costs more than it saves), the
+// prefix phase (if any group has a prefix) runs first, alone, on the call's
+// stream, its key
 // range split into as many parts as keep it a launch of 64-row tiles with key
 // halves (row tiles x kv heads x groups x parts below kChunkSplitBelow; at
 // least two 64-key tiles per part, one for each key half); then the decode
@@ -448,7 +450,7 @@ CascadePlan cascade_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_h
     const int32_t group = num_q_heads / num_kv_heads;
     const int32_t plen = prefix_cap & ~15;
     int32_t part = choose_partition(num_seqs, num_kv_heads, head_dim, max_context_len, partition_tokens);
-    p.fold = part <= 0 && plen > 0;
+    p.fold = part <= 0;
     if (plen > 0) {
         const int64_t row_tiles = ceil_div((int64_t)max_group_size * group, 128);
         const int64_t tiles = ceil_div(plen, 64);
@@ -547,13 +549,15 @@ int32_t pa_decode_shared_prefix(const void* q, const void* k_pool, const void* v
     a.prefix_part_tokens = cp.prefix_part > 0 ? cp.prefix_part : 64;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (cp.fold) {
-        // one pass; the prefix's partial states follow the order array (if any)
-        if (workspace == nullptr || workspace_bytes < cp.bytes) return PA_ERR_WORKSPACE;
-        if (!aligned16(workspace)) return PA_ERR_ALIGN;
+        // one pass; the prefix's partial states follow the order array (if
+        // any); with no prefix and no order array nothing is needed
+        if (cp.bytes > 0 && (workspace == nullptr || workspace_bytes < cp.bytes)) return PA_ERR_WORKSPACE;
+        if (workspace != nullptr && !aligned16(workspace)) return PA_ERR_ALIGN;
         if (int32_t st = prepare_rows(a, num_seqs, -1, workspace, workspace_bytes)) return st;
         const size_t order_bytes = rows_bytes(num_seqs, num_q_heads, pool.num_kv_heads, pool.head_dim,
                                               max_context_len, -1, true);
-        a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + order_bytes);
+        a.ws = cp.prefix_slots > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + order_bytes)
+                                   : nullptr;
         a.nparts = cp.prefix_slots;
         a.prefix_slots = cp.prefix_slots;
         a.fold_prefix = 1;

@@ -152,3 +152,15 @@ def test_large_batch_with_order_array(pa):
     prefixes = [32 + 3 * i for i in range(S // n)]   # not all multiples of 16
     tables, gs = share(b, groups, prefixes)
     run_case(pa, b, tables, gs, prefixes, parts=(-1, 0))
+
+
+def test_no_group_has_a_prefix(pa):
+    """max_prefix_len 0 (a batch with no prefix-cache hit): the one-pass plan
+    is plain pa_decode (no prefix phase, no partial states, no workspace), the
+    split plan keeps its partitions and merge."""
+    b = make_batch(97, name="noprefix", dtype="bf16", num_q_heads=28, num_kv_heads=4, head_dim=128,
+                   draw_lens=lambda rng: rng.integers(1, 1500, size=40))
+    groups = [list(range(10 * i, 10 * (i + 1))) for i in range(4)]
+    tables, gs = share(b, groups, [0, 0, 0, 0])
+    assert pa.decode_shared_prefix_workspace_bytes(40, 28, 4, 128, b.max_context_len, 4, 10, 0, -1) == 0
+    run_case(pa, b, tables, gs, [0, 0, 0, 0], parts=(-1, 0, 64))
