@@ -234,6 +234,26 @@ def test_shared_prefix_validation(pa):
     assert pa.decode_shared_prefix_workspace_bytes(4, 2, 1, 64, 64, 0, 3, 32, 0) == 0
 
 
+def test_shared_prefix_plans(pa):
+    """The planner's choices, seen through the workspace it asks for.
+    64 sequences of 8,192 tokens sharing 4,096, G = 7 (28/4 heads, D 128):
+    one pass (256 units fill the chip), so the prefix phase takes 64-row tiles
+    with key halves in 255 // (7 row tiles x 4 kv heads) = 9 parts wanted,
+    64 tiles / 9 -> 8 tiles of 64 keys a part, 8 parts: 8 partial states per
+    (sequence, q head) of D + 2 fp32."""
+    ws = pa.decode_shared_prefix_workspace_bytes
+    assert ws(64, 28, 4, 128, 8192, 1, 64, 4096, 0) == 64 * 28 * 8 * 130 * 4
+    # no group has a prefix and the keys run in one pass: plain decode, nothing
+    assert ws(64, 28, 4, 128, 8192, 1, 64, 0, -1) == 0
+    # 64-token partitions: the split plan, 8192 / 64 = 128 partitions after 8
+    # prefix parts of 512 keys (about 128 workgroups of 128 rows: 4 row tiles
+    # x 4 kv heads x 8 parts)
+    assert ws(64, 28, 4, 128, 8192, 1, 64, 4096, 64) == 64 * 28 * (128 + 8) * 130 * 4
+    # 36 groups of two at G = 2: a 64-row tile per (group, kv head), 288 of
+    # them, so one part even exceeds the small launch: one part, one slot
+    assert ws(72, 16, 8, 128, 1200, 36, 2, 576, 0) == 72 * 16 * 1 * 130 * 4
+
+
 def test_qkv_rope_write_validation(pa):
     L = pa.lib()
     p = pool(hkv=2, d=64)               # width (Hq + 2*Hkv) * D = (4 + 4) * 64 = 512
